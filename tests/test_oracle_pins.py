@@ -1,0 +1,506 @@
+"""Pins for the CPU oracle.
+
+Each test ties the oracle to something other than itself: values worked by
+hand (tests/golden/*.json, each citing its page), exact rational arithmetic
+(fractions.Fraction), closed forms, invariants, and library routines (numpy's
+float16 conversion, numpy integer matmul and stable argsort, math.erf,
+scipy's softmax).  A plausible slip in the oracle -- a swapped nibble, a
+wrong group index, a transposed operand, a dropped bias, half-away rounding
+instead of half-even, a divide instead of a multiply, double rounding --
+fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import qgemm_inputs as qi
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bits16(a):
+    return np.asarray(a, np.float16).view(np.uint16)
+
+
+def unpack_numpy(Wb, K, N):
+    """Natural int4 decode by numpy arithmetic shifts (independent of the oracle):
+    even column = low nibble, odd column = high nibble, two's complement."""
+    b = Wb.reshape(K, N // 2)
+    lo = (b.astype(np.uint8) << 4).view(np.int8) >> 4
+    hi = b.view(np.int8) >> 4
+    q = np.empty((K, N), np.int8)
+    q[:, 0::2] = lo
+    q[:, 1::2] = hi
+    return q
+
+
+def pack_numpy(q):
+    """Pack int8 values in [-8, 7] [K][N] into natural bytes (test-side helper)."""
+    u = (q.astype(np.int16) & 15).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+# ------------------------------------------------------------------ binary16
+
+def test_f16_to_f64_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float64)
+    got = oracle.f16_to_f64(h.view(np.float16))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f64_to_f16_against_numpy():
+    r = qi.rng(1)
+    finite = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite = finite[np.isfinite(finite)].astype(np.float64)
+    finite = np.unique(finite)
+    mids = (finite[:-1] + finite[1:]) / 2  # exact ties between neighbours
+    quarter = finite[:-1] + (finite[1:] - finite[:-1]) / 4
+    rand = np.concatenate([
+        r.standard_normal(200000),
+        r.standard_normal(20000) * 1e-6,   # subnormal range
+        r.standard_normal(20000) * 3e4,    # near overflow
+        np.array([65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -25, 2.0 ** -26, 0.0, -0.0]),
+    ])
+    x = np.concatenate([finite, mids, quarter, rand])
+    got = bits16(oracle.f64_to_f16(x))
+    ref = bits16(x.astype(np.float16))
+    assert np.array_equal(got, ref)
+
+
+def test_f64_to_f16_rounds_once():
+    # Just above the midpoint between 1 and 1 + 2^-10: one rounding goes up;
+    # rounding to fp32 first would land on the midpoint and then go down.
+    x = 1.0 + 2.0 ** -11 + 2.0 ** -40
+    assert float(oracle.f64_to_f16([x])[0]) == 1.0 + 2.0 ** -10
+    assert float(oracle.f64_to_f16([1.0 + 2.0 ** -11])[0]) == 1.0  # tie -> even
+
+
+# ------------------------------------------------------------------ int4
+
+def test_int4_decode_exhaustive():
+    b = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    for i in range(256):
+        got = oracle.int4_unpack(b[i], 1, 2)[0]
+        assert list(got) == list(unpack_numpy(b[i], 1, 2)[0])
+
+
+def test_int4_hand_bytes():
+    g = golden("w4a16_hand_4x4.json")
+    packed = np.array([int(h, 16) for h in g["packed_hex"].split()], np.uint8)
+    assert oracle.int4_unpack(packed, 4, 4).tolist() == g["Q"]
+    assert pack_numpy(np.array(g["Q"], np.int8)).ravel().tolist() == packed.tolist()
+
+
+# ------------------------------------------------------------------ W4A16
+
+def test_w4a16_hand_4x4():
+    g = golden("w4a16_hand_4x4.json")
+    packed = np.array([int(h, 16) for h in g["packed_hex"].split()], np.uint8).reshape(4, 2)
+    A = np.array(g["A"], np.float16)
+    S = np.array(g["S"], np.float16)
+    Y = oracle.w4a16(A, packed, S, g["G"])
+    assert Y.astype(np.float64).tolist() == g["Y"]
+
+
+def exact_w4a16(A, q, S, G):
+    M, K = A.shape
+    N = q.shape[1]
+    out = np.empty((M, N), object)
+    for m in range(M):
+        for n in range(N):
+            out[m, n] = sum(Fraction(float(A[m, k])) * int(q[k, n]) * Fraction(float(S[k // G, n]))
+                            for k in range(K))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_w4a16_brute_force_tiny(seed):
+    r = qi.rng(50 + seed)
+    M = int(r.integers(1, 5))
+    N = 2 * int(r.integers(1, 3))
+    G = int(r.choice([1, 2, 4]))
+    K = G * int(r.integers(1, 9 // G + 1))
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 60 + seed)
+    q = unpack_numpy(Wb, K, N)
+    ex = exact_w4a16(A, q, S, G)
+    Y, Y64 = oracle.w4a16(A, Wb, S, G, want_f64=True)
+    ref64 = np.array([[float(v) for v in row] for row in ex])
+    assert np.allclose(Y64, ref64, rtol=1e-14, atol=0)
+    assert np.array_equal(bits16(Y), bits16(ref64.astype(np.float16)))
+
+
+def test_w4a16_all_16_nibbles_brute_force():
+    # every nibble value in every column parity, K spanning two groups
+    K, N, G, M = 32, 4, 16, 3
+    q = np.array([[((k * 5 + n * 3) % 16) - 8 for n in range(N)] for k in range(K)], np.int8)
+    assert set(np.unique(q)) == set(range(-8, 8))
+    A = qi.activations(M, K, 71)
+    S = qi.w4a16_weights(K, N, G, 72)[1]
+    Y, Y64 = oracle.w4a16(A, pack_numpy(q), S, G, want_f64=True)
+    ex = exact_w4a16(A, q, S, G)
+    ref64 = np.array([[float(v) for v in row] for row in ex])
+    assert np.allclose(Y64, ref64, rtol=1e-14, atol=0)
+    assert np.array_equal(bits16(Y), bits16(ref64.astype(np.float16)))
+
+
+def test_w4a16_equal_scales_is_integer_matmul():
+    M, K, N, G = 8, 256, 64, 64
+    A, Wb, _ = qi.w4a16_problem(M, K, N, G, 80)
+    s = np.float16(0.0137)
+    S = np.full((K // G, N), s, np.float16)
+    Y = oracle.w4a16(A, Wb, S, G)
+    # A is a multiple of 2^-24, so A * 2^24 is integral: an exact int64 matmul
+    Ai = (A.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    P = Ai @ unpack_numpy(Wb, K, N).astype(np.int64)
+    ref = np.array([[float(Fraction(int(v), 2 ** 24) * Fraction(float(s))) for v in row] for row in P])
+    assert np.array_equal(bits16(Y), bits16(ref.astype(np.float16)))
+
+
+def test_w4a16_group_isolation():
+    M, K, N, G = 4, 512, 32, 128
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 81)
+    A2 = np.zeros_like(A)
+    A2[:, 256:384] = A[:, 256:384]  # only group 2 active
+    S2 = S.copy()
+    S2[[0, 1, 3]] = np.float16(0.5)  # change every other group's scales
+    Y1 = oracle.w4a16(A2, Wb, S, G)
+    Y2 = oracle.w4a16(A2, Wb, S2, G)
+    assert np.array_equal(bits16(Y1), bits16(Y2))
+    S3 = S.copy()
+    S3[2] = np.float16(0.5)
+    assert not np.array_equal(bits16(oracle.w4a16(A2, Wb, S3, G)), bits16(Y1))
+
+
+def test_w4a16_k_split_additivity_and_linearity():
+    M, K, N, G = 3, 512, 64, 128
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 82)
+    _, Y = oracle.w4a16(A, Wb, S, G, want_f64=True)
+    _, Y1 = oracle.w4a16(A[:, :256], Wb[:256], S[:2], G, want_f64=True)
+    _, Y2 = oracle.w4a16(A[:, 256:], Wb[256:], S[2:], G, want_f64=True)
+    assert np.allclose(Y, Y1 + Y2, rtol=1e-12, atol=1e-12)
+    _, Yd = oracle.w4a16((A.astype(np.float32) * 2).astype(np.float16), Wb, S, G, want_f64=True)
+    assert np.array_equal(Yd, 2 * Y)
+    # transposing the roles of rows and columns changes the answer (orientation check)
+    A4 = qi.activations(4, 4, 83)
+    g = golden("w4a16_hand_4x4.json")
+    packed = np.array([int(h, 16) for h in g["packed_hex"].split()], np.uint8).reshape(4, 2)
+    qT = np.array(g["Q"], np.int8).T.copy()
+    S = np.array(g["S"], np.float16)
+    assert not np.array_equal(bits16(oracle.w4a16(A4, packed, S, 2)),
+                              bits16(oracle.w4a16(A4, pack_numpy(qT), S, 2)))
+
+
+def test_w4a16_zero_weights():
+    A, _, S = qi.w4a16_problem(2, 256, 32, 128, 84)
+    Y = oracle.w4a16(A, np.zeros((256, 16), np.uint8), S, 128)
+    assert not np.any(Y.astype(np.float32))
+
+
+def test_w4a16_sampled_matches_full():
+    M, K, N, G = 16, 512, 512, 128
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 100)
+    Y = oracle.w4a16(A, Wb, S, G)
+    ms, ns = qi.sample_positions(M, N, 300, 5)
+    y = oracle.w4a16_at(A, Wb, S, G, ms, ns)
+    assert np.array_equal(bits16(y), bits16(Y[ms, ns]))
+
+
+def test_w4a16_output_scale_statistics():
+    # y = sum_k a_k w_k with a ~ N(0,1), w = q s: std(y) = sqrt(K E[q^2] E[s^2])
+    M, K, N, G = 8, 4096, 1024, 128
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 85)
+    Y = oracle.w4a16(A, Wb, S, G).astype(np.float64)
+    eq2 = sum(v * v for v in range(-8, 8)) / 16
+    es2 = (0.005 ** 2 + 0.005 * 0.02 + 0.02 ** 2) / 3
+    assert abs(Y.std() / math.sqrt(K * eq2 * es2) - 1) < 0.05
+
+
+# ------------------------------------------------------------------ fragment layout
+
+def test_prepack_layout_is_a_bijection():
+    K, N = 256, 256
+    idx = np.array([[oracle.frag_nibble_index(K, k, n) for n in range(N)] for k in range(K)])
+    assert np.array_equal(np.sort(idx.ravel()), np.arange(K * N))
+
+
+def test_prepack_layout_hand_positions():
+    K = 256
+    cases = {  # (k, n) -> nibble index, worked from the layout definition
+        (0, 0): 0, (2, 0): 1, (4, 0): 2, (6, 0): 3, (1, 0): 4, (7, 0): 7,
+        (32, 0): 8, (8, 0): 512, (0, 1): 32, (0, 16): 2048,
+        (128, 0): 16384, (0, 128): 32768, (255, 255): 32768 + 8192 * 2 + 7 * 2048 + 2 * ((15 + 48) * 16 + 12) + 7,
+    }
+    for (k, n), want in cases.items():
+        assert oracle.frag_nibble_index(K, k, n) == want, (k, n)
+
+
+def test_prepack_offset_binary_values():
+    K, N = 128, 128
+    assert not oracle.w4a16_prepack(np.full((K, N // 2), 0x88, np.uint8), K, N).any()
+    assert (oracle.w4a16_prepack(np.full((K, N // 2), 0x77, np.uint8), K, N) == 0xFF).all()
+    assert (oracle.w4a16_prepack(np.zeros((K, N // 2), np.uint8), K, N) == 0x88).all()
+
+
+def test_prepack_moves_every_nibble():
+    K, N = 256, 384
+    Wb = qi.w4a16_weights(K, N, 128, 86)[0]
+    F = oracle.w4a16_prepack(Wb, K, N)
+    q = unpack_numpy(Wb, K, N)
+    nib = np.empty(K * N, np.int64)
+    nib[0::2] = F & 15
+    nib[1::2] = F >> 4
+    for k in range(0, K, 7):
+        for n in range(0, N, 5):
+            assert nib[oracle.frag_nibble_index(K, k, n)] == q[k, n] + 8
+
+
+# ------------------------------------------------------------------ int8 quant / dequant
+
+def test_quant_hand_rows():
+    g = golden("quant_hand.json")
+    for row in g["rows"]:
+        x = np.array([row["x"]], np.float16)
+        Q, S = oracle.quant_sym_int8(x)
+        assert Q[0].tolist() == row["q"]
+        if "s" in row:
+            assert float(S[0]) == row["s"]
+    assert float(S[0]) == float(np.float32(3) / np.float32(127))
+
+
+def test_dequant_hand():
+    g = golden("quant_hand.json")["dequant"]
+    X = oracle.dequant_sym_int8(np.array([g["q"]], np.int8), np.array([g["s"]], np.float32))
+    assert X[0].astype(np.float64).tolist() == g["x"]
+
+
+def round_half_even(fr):
+    fl = math.floor(fr)
+    d = fr - fl
+    if d > Fraction(1, 2) or (d == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def test_quant_against_exact_rationals():
+    X = qi.kv_problem(1, 64, 128, 90).reshape(64, 128)
+    X[3, 5] = np.float16(0.0)
+    Q, S = oracle.quant_sym_int8(X)
+    mism = 0
+    for r in range(X.shape[0]):
+        amax = max(abs(Fraction(float(v))) for v in X[r])
+        for c in range(X.shape[1]):
+            t = Fraction(float(X[r, c])) * 127 / amax
+            qe = round_half_even(t)
+            if qe != Q[r, c]:
+                mism += 1
+                assert abs(qe - int(Q[r, c])) == 1
+                assert abs((t - math.floor(t)) - Fraction(1, 2)) < Fraction(1, 10 ** 4)
+        assert S[r] == np.float32(float(amax / 127))  # correctly rounded amax/127
+    assert mism <= 4
+
+
+def test_quant_error_bounds_and_statistics():
+    X = qi.kv_problem(4, 2048, 128, 91).reshape(-1, 128)
+    Q, S = oracle.quant_sym_int8(X)
+    x = X.astype(np.float64)
+    s = S.astype(np.float64)[:, None]
+    err = np.abs(x - Q.astype(np.float64) * s)
+    assert np.all(err <= s * (0.5 + 2.0 ** -14))
+    mse_ratio = np.mean(err ** 2) / np.mean(s ** 2 / 12)
+    assert 0.95 < mse_ratio < 1.05
+    # the KV demo's own acceptance bar: round-trip MSE below 1e-4
+    Xh = oracle.dequant_sym_int8(Q, S).astype(np.float64)
+    assert np.mean((x - Xh) ** 2) < 1e-4
+    ulp = np.spacing(np.abs(Xh).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(x - Xh) <= s * (0.5 + 2.0 ** -14) + ulp / 2)
+    # extremes map to +-127 exactly, never -128
+    amax_idx = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(Q[np.arange(len(Q)), amax_idx]) == 127)
+    assert Q.min() >= -127
+
+
+def test_dequant_unit_scale_identity():
+    q = np.arange(-127, 128, dtype=np.int8).reshape(1, -1)
+    X = oracle.dequant_sym_int8(q, np.ones(1, np.float32))
+    assert X.astype(np.int32).tolist() == q.astype(np.int32).tolist()
+
+
+# ------------------------------------------------------------------ W8A8
+
+def test_w8a8_acc_hand():
+    g = golden("w8a8_hand_4x4.json")
+    acc = oracle.w8a8_acc(np.array(g["qa"], np.int8), np.array(g["qw"], np.int8))
+    assert acc.tolist() == g["acc"]
+
+
+def test_w8a8_acc_closed_forms_and_numpy():
+    K = 4096
+    a = np.full((2, K), 127, np.int8)
+    w = np.stack([np.full(K, 127, np.int8), np.full(K, -127, np.int8)])
+    assert oracle.w8a8_acc(a, w).tolist() == [[K * 16129, -K * 16129]] * 2
+    r = qi.rng(92)
+    A = r.integers(-127, 128, size=(33, 300), dtype=np.int8)
+    W = r.integers(-127, 128, size=(17, 300), dtype=np.int8)
+    assert np.array_equal(oracle.w8a8_acc(A, W), A.astype(np.int64) @ W.astype(np.int64).T)
+
+
+def test_w8a8_epilogue_hand():
+    g = golden("w8a8_hand_4x4.json")
+    qa = np.array(g["qa"], np.int8)
+    qw = np.array(g["qw"], np.int8)
+    sa = np.array(g["sa"], np.float32)
+    sw = np.array(g["sw"], np.float32)
+    bias = np.array(g["bias"], np.float16)
+    Y = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 1.0, oracle.EPI_BIAS)
+    assert Y.tolist() == g["bias_only_mult1"]
+    Y4 = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 4.0, oracle.EPI_BIAS)
+    for r, row in g["bias_only_mult4_rows"].items():
+        assert Y4[int(r)].tolist() == row
+    Yg = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 1.0, oracle.EPI_BIAS | oracle.EPI_GELU)
+    assert Yg.tolist() == g["bias_gelu_mult1"]
+    # without the bias flag the bias is ignored: row 3 (acc = 0) is all zero
+    Yn = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 1.0, 0)
+    assert Yn[3].tolist() == [0, 0, 0, 0] and Yn[0].tolist() == [10, 2, -6, 48]
+
+
+def gelu_exact(y):
+    return 0.5 * y * (1.0 + math.erf(y / math.sqrt(2.0)))
+
+
+def test_gelu28_against_erf():
+    ys = np.concatenate([np.linspace(-10, 10, 40001), [-300.0, -60.0, 60.0, 300.0, 1e-30, -1e-30]])
+    ys = ys.astype(np.float32)
+    g = oracle.gelu28(ys).astype(np.float64)
+    ref = np.array([gelu_exact(float(y)) for y in ys])
+    # A&S 7.1.28 bounds |erf error| by 3e-7; evaluating it in fp32 adds rounding
+    # that the 16th power amplifies (about 16 x 1.5e-7).  |g error| = |y|/2 * |erf error|.
+    assert np.all(np.abs(g - ref) <= 0.5 * (3e-7 + 2.7e-6) * np.abs(ys.astype(np.float64)) + 1e-37)
+    mid = np.abs(ys) > 2.0  # p^16 is large there: A&S error plus the rounding of g itself
+    assert np.all(np.abs(g - ref)[mid] <= 0.5 * 6e-7 * np.abs(ys[mid].astype(np.float64)) + 1e-37)
+    assert oracle.gelu28(np.float32(0.0)) == 0.0
+    assert oracle.gelu28(np.float32(6.0)) == 6.0
+    big = np.float32(64.5)
+    assert oracle.gelu28(big) == big
+    assert oracle.gelu28(np.float32(-6.0)) == 0.0
+
+
+def test_w8a8_epilogue_matches_acc_path():
+    M, N, K = 16, 24, 64
+    X, Wf, bias, om = qi.w8a8_problem(M, N, K, 93)
+    qa, sa = oracle.quant_sym_int8(X)
+    qw, sw = oracle.quant_sym_int8(Wf)
+    Y, acc = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, om, 3, want_acc=True)
+    assert np.array_equal(acc, qa.astype(np.int64) @ qw.astype(np.int64).T)
+    ms, ns = qi.sample_positions(M, N, 50, 6)
+    y, a2 = oracle.w8a8_epilogue_at(qa, qw, sa, sw, bias, om, 3, ms, ns)
+    assert np.array_equal(y, Y[ms, ns]) and np.array_equal(a2, acc[ms, ns])
+    # dequantized int8 GEMM approximates the fp GEMM (rescale step is right)
+    yq = acc * sa[:, None].astype(np.float64) * sw[None, :].astype(np.float64)
+    yf = X.astype(np.float64) @ Wf.astype(np.float64).T
+    assert np.abs(yq - yf).max() < 0.05 * np.abs(yf).max()
+
+
+# ------------------------------------------------------------------ MoE
+
+def test_moe_route_hand():
+    g = golden("moe_route_hand.json")
+    ids, w = oracle.moe_route(np.array(g["logits"], np.float16), g["topK"])
+    assert ids.tolist() == g["ids"]
+    assert np.allclose(w, np.array(g["w"]), rtol=1e-12, atol=0)
+    off, pairs = oracle.moe_permute(ids, g["E"])
+    assert off.tolist() == g["offsets"] and pairs.tolist() == g["pairs"]
+
+
+def test_moe_route_against_numpy():
+    logits = qi.moe_problem(256, 8, 8, 8, 8, 94)[1]
+    logits[5] = logits[5, 0]  # an all-tie row
+    ids, w = oracle.moe_route(logits, 2)
+    l = logits.astype(np.float64)
+    ref = np.argsort(-l, axis=1, kind="stable")[:, :2]
+    assert np.array_equal(ids, ref)
+    sel = np.take_along_axis(l, ref, axis=1)
+    assert np.allclose(w, scipy.special.softmax(sel, axis=1), rtol=1e-13, atol=0)
+    assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+    off, pairs = oracle.moe_permute(ids, 8)
+    flat = ids.ravel()
+    assert np.array_equal(pairs, np.argsort(flat, kind="stable"))
+    assert np.array_equal(np.diff(off), np.bincount(flat, minlength=8))
+
+
+SMALL_MOE = dict(T=6, H=256, I=256, E=4, topK=2, G=128)
+
+
+def small_moe(seed):
+    c = SMALL_MOE
+    return qi.moe_problem(c["T"], c["H"], c["I"], c["E"], c["G"], seed)
+
+
+def test_moe_identical_experts_is_dense_swiglu():
+    c = SMALL_MOE
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = small_moe(95)
+    for arr in (Wg, Wu, Wd, Sg, Su, Sd):
+        arr[1:] = arr[0]
+    Y, ids, w = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"])
+    _, g = oracle.w4a16(X, Wg[0], Sg[0], c["G"], want_f64=True)
+    _, u = oracle.w4a16(X, Wu[0], Su[0], c["G"], want_f64=True)
+    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float16)
+    _, o = oracle.w4a16(h, Wd[0], Sd[0], c["G"], want_f64=True)
+    ref = o.astype(np.float16)
+    diff = np.abs(Y.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(diff <= np.spacing(np.abs(ref)).astype(np.float64))
+
+
+def test_moe_token_permutation_and_expert_removal():
+    c = SMALL_MOE
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = small_moe(96)
+    Y, ids, w = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"])
+    perm = qi.rng(97).permutation(c["T"])
+    Yp, idsp, _ = oracle.moe(X[perm], logits[perm], Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"])
+    assert np.array_equal(bits16(Yp), bits16(Y[perm])) and np.array_equal(idsp, ids[perm])
+    # relabelling experts relabels ids and leaves the output unchanged
+    rel = np.array([2, 0, 3, 1])
+    inv = np.argsort(rel)
+    Yr, idsr, _ = oracle.moe(X, logits[:, rel], Wg[rel], Wu[rel], Wd[rel], Sg[rel], Su[rel], Sd[rel],
+                             c["topK"], c["G"])
+    assert np.array_equal(bits16(Yr), bits16(Y)) and np.array_equal(rel[idsr], ids)
+    assert np.array_equal(idsr, inv[ids])
+    # zero the down projection of the top-1 expert of token 0: only the other remains
+    e0 = ids[0, 0]
+    Sd0 = Sd.copy()
+    Sd0[e0] = np.float16(0.0)
+    _, _, _, Y64 = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd0, c["topK"], c["G"], tokens=[0],
+                              want_f64=True)
+    _, _, _, Yfull = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"], tokens=[0],
+                                want_f64=True)
+    e1 = ids[0, 1]
+    keep = np.ones(c["E"], bool)
+    keep[e1] = False
+    Sd1 = Sd.copy()
+    Sd1[keep] = np.float16(0.0)
+    _, _, _, Yonly1 = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd1, c["topK"], c["G"], tokens=[0],
+                                 want_f64=True)
+    assert np.allclose(Y64[0], Yonly1[0], rtol=0, atol=0)
+    assert not np.allclose(Yfull[0], Y64[0])
+
+
+def test_moe_sampled_tokens_match_full():
+    c = SMALL_MOE
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = small_moe(98)
+    Y, _, _ = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"])
+    Ys, _, _ = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"], tokens=[4, 1])
+    assert np.array_equal(bits16(Ys[[4, 1]]), bits16(Y[[4, 1]]))
