@@ -1,0 +1,247 @@
+"""Python binding for libqgemm (HIP, gfx950) -- argument marshalling only.
+
+Every function has the name of the C entry point it calls (include/libqgemm.h)
+and takes torch tensors that live on the GPU; the work itself runs in the
+library's kernels on ``torch.cuda.current_stream()``.  Outputs may be passed
+in (no allocation then) or are allocated here with ``torch.empty``.  A non-zero
+status raises ``QGemmError``.  There is no fallback: without the built
+library (``python -m bit_quantized_gemm_qgemm_amd.build`` or
+``__graft_entry__.build()``) every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+OK = 0
+NULL_PTR = 1
+BAD_SHAPE = 2
+MISALIGNED = 3
+WORKSPACE_TOO_SMALL = 4
+UNSUPPORTED = 5
+HIP_ERROR = 6
+
+EPI_BIAS = 1
+EPI_GELU = 2
+
+_lib = None
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({qgemm_status_str(status)})")
+
+
+def _hip_runtimes_loaded():
+    with open("/proc/self/maps") as f:
+        return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+
+
+def lib():
+    """Load libqgemm.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run bit_quantized_gemm_qgemm_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    rts = _hip_runtimes_loaded()
+    if len(rts) > 1:
+        raise RuntimeError(f"two HIP runtimes in one process: {rts}")
+    _declare(L)
+    _lib = L
+    return L
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def _declare(L):
+    sig = {
+        "qgemm_abi_version": (_I32, []),
+        "qgemm_status_str": (ctypes.c_char_p, [_I32]),
+        "qgemm_w4a16_packed_bytes": (_SZ, [_I32, _I32]),
+        "qgemm_w4a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
+        "qgemm_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+        "qgemm_w4a16": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+        "quant_sym_int8": (_I32, [_P, _P, _P, _I32, _I32, _P]),
+        "dequant_sym_int8": (_I32, [_P, _P, _P, _I32, _I32, _P]),
+        "qgemm_w8a8_epilogue": (_I32, [_P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_uint32, _P, _P,
+                                       _I32, _I32, _I32, _P]),
+        "moe_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+        "moe_w4a16": (_I32, [_P] * 11 + [_I32] * 7 + [_P, _SZ, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
+           "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
+           "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn, status):
+    if status != OK:
+        raise QGemmError(fn, status)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name}: expected a contiguous CUDA tensor of {dtype}")
+    return t
+
+
+# ---------------------------------------------------------------- ABI
+
+def qgemm_abi_version():
+    return lib().qgemm_abi_version()
+
+
+def qgemm_status_str(status):
+    return lib().qgemm_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------- W4A16
+
+def qgemm_w4a16_packed_bytes(K, N):
+    return lib().qgemm_w4a16_packed_bytes(K, N)
+
+
+def qgemm_w4a16_prepack(w_natural, K, N, w_frag=None):
+    """Natural int4 bytes uint8 [K, N/2] -> fragment-layout bytes uint8 [K*N/2]."""
+    _need(w_natural, torch.uint8, "w_natural")
+    if w_frag is None:
+        w_frag = torch.empty(max(qgemm_w4a16_packed_bytes(K, N), 1), dtype=torch.uint8,
+                             device=w_natural.device)
+    _need(w_frag, torch.uint8, "w_frag")
+    _check("qgemm_w4a16_prepack",
+           lib().qgemm_w4a16_prepack(_ptr(w_natural), _ptr(w_frag), K, N, _stream()))
+    return w_frag
+
+
+def qgemm_w4a16_workspace_bytes(M, N, K, G):
+    return lib().qgemm_w4a16_workspace_bytes(M, N, K, G)
+
+
+def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
+    """Y[M, N] = A[M, K] (fp16) x dequant(w_frag, scales [K/G, N] fp16)."""
+    _need(A, torch.float16, "A")
+    _need(w_frag, torch.uint8, "w_frag")
+    _need(scales, torch.float16, "scales")
+    M, K = A.shape
+    N = scales.shape[1] if N is None else N
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    _need(Y, torch.float16, "Y")
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("qgemm_w4a16", lib().qgemm_w4a16(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
+                                             _ptr(workspace), ws, _stream()))
+    return Y
+
+
+# ---------------------------------------------------------------- int8 quant
+
+def quant_sym_int8(X, Q=None, scales=None):
+    """Per-row symmetric int8 codes and fp32 dequant scales of fp16 X [..., cols]."""
+    _need(X, torch.float16, "X")
+    cols = X.shape[-1]
+    rows = X.numel() // cols if cols else 0
+    if Q is None:
+        Q = torch.empty(X.shape, dtype=torch.int8, device=X.device)
+    if scales is None:
+        scales = torch.empty(max(rows, 1), dtype=torch.float32, device=X.device)[:rows]
+    _need(Q, torch.int8, "Q")
+    _need(scales, torch.float32, "scales")
+    _check("quant_sym_int8",
+           lib().quant_sym_int8(_ptr(X), _ptr(Q), _ptr(scales), rows, cols, _stream()))
+    return Q, scales
+
+
+def dequant_sym_int8(Q, scales, X=None):
+    _need(Q, torch.int8, "Q")
+    _need(scales, torch.float32, "scales")
+    cols = Q.shape[-1]
+    rows = Q.numel() // cols if cols else 0
+    if X is None:
+        X = torch.empty(Q.shape, dtype=torch.float16, device=Q.device)
+    _need(X, torch.float16, "X")
+    _check("dequant_sym_int8",
+           lib().dequant_sym_int8(_ptr(Q), _ptr(scales), _ptr(X), rows, cols, _stream()))
+    return X
+
+
+# ---------------------------------------------------------------- W8A8
+
+def qgemm_w8a8_epilogue(A, W, a_scale, w_scale, bias, out_mult, flags, Y=None, acc_out=None):
+    """int8 Y[M, N] from int8 A [M, K], W [N, K] with the fused requantizing epilogue."""
+    _need(A, torch.int8, "A")
+    _need(W, torch.int8, "W")
+    _need(a_scale, torch.float32, "a_scale")
+    _need(w_scale, torch.float32, "w_scale")
+    if bias is not None:
+        _need(bias, torch.float16, "bias")
+    M, K = A.shape
+    N = W.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.int8, device=A.device)
+    _need(Y, torch.int8, "Y")
+    if acc_out is not None:
+        _need(acc_out, torch.int32, "acc_out")
+    _check("qgemm_w8a8_epilogue",
+           lib().qgemm_w8a8_epilogue(_ptr(A), _ptr(W), _ptr(a_scale), _ptr(w_scale), _ptr(bias),
+                                     float(out_mult), int(flags), _ptr(Y), _ptr(acc_out), M, N, K,
+                                     _stream()))
+    return Y
+
+
+# ---------------------------------------------------------------- MoE
+
+def moe_w4a16_workspace_bytes(T, H, I, E, topK):
+    return lib().moe_w4a16_workspace_bytes(T, H, I, E, topK)
+
+
+def moe_w4a16(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down, topK, G,
+              I=None, activation=0, Y=None, topk_ids=None, topk_w=None, workspace=None):
+    """SiLU-gated INT4 MoE layer.  Returns (Y, topk_ids, topk_w, workspace)."""
+    _need(X, torch.float16, "X")
+    _need(logits, torch.float16, "logits")
+    for name, t in (("w_gate_frag", w_gate_frag), ("w_up_frag", w_up_frag),
+                    ("w_down_frag", w_down_frag)):
+        _need(t, torch.uint8, name)
+    for name, t in (("s_gate", s_gate), ("s_up", s_up), ("s_down", s_down)):
+        _need(t, torch.float16, name)
+    T, H = X.shape
+    E = logits.shape[1]
+    I = s_gate.shape[-1] if I is None else I
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((T, H), dtype=torch.float16, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topK), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, topK), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(moe_w4a16_workspace_bytes(T, H, I, E, topK), 1),
+                                dtype=torch.uint8, device=dev)
+    _check("moe_w4a16",
+           lib().moe_w4a16(_ptr(X), _ptr(logits), _ptr(w_gate_frag), _ptr(w_up_frag),
+                           _ptr(w_down_frag), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(Y),
+                           _ptr(topk_ids), _ptr(topk_w), T, H, I, E, topK, G, activation,
+                           _ptr(workspace), workspace.numel(), _stream()))
+    return Y, topk_ids, topk_w, workspace

@@ -1,0 +1,167 @@
+// W8A8 int8 GEMM with a fused requantizing epilogue.
+//
+// INT8 cross-modal MHA TensorRT plugin interview page: knowledge point 1
+// (int8 operands, integer accumulation, then fp32 and requantization to
+// int8), knowledge point 2 (per-channel weight / per-token activation scales;
+// after the int8 GEMM: rescale + bias + GELU, then requantize), answer step 3
+// (a per-tensor output scale and an fp16 bias applied after the GEMM).
+//
+// A [M][K] and W [N][K] are both K-contiguous.  128x128 output tiles, four
+// waves of 64x64, each a 2x2 grid of v_mfma_i32_32x32x32_i8; A and W tiles
+// (128 k deep) double-buffered through LDS.  The epilogue runs on the int32
+// accumulators in registers and is the bit-exact fp32 sequence of the header
+// (no contraction; division correctly rounded).
+#include "common.hpp"
+
+namespace {
+
+using namespace qg;
+
+constexpr int BM = 128, BN = 128, BK = 128, LDK = 144;  // LDS row: 128 bytes + 16 pad
+
+__device__ __forceinline__ intx16 mfma_i8(intx4 a, intx4 b, intx16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// Abramowitz & Stegun 7.1.28 erf inside GELU, fixed fp32 sequence.
+__device__ __forceinline__ float gelu28(float y) {
+    const float a1 = 0.0705230784f, a2 = 0.0422820123f, a3 = 0.0092705272f;
+    const float a4 = 0.0001520143f, a5 = 0.0002765672f, a6 = 0.0000430638f;
+    const float u = y * 0.70710678f;
+    const float a = fabsf(u);
+    float p = __builtin_fmaf(a, a6, a5);
+    p = __builtin_fmaf(a, p, a4);
+    p = __builtin_fmaf(a, p, a3);
+    p = __builtin_fmaf(a, p, a2);
+    p = __builtin_fmaf(a, p, a1);
+    p = __builtin_fmaf(a, p, 1.0f);
+    p = p * p;
+    p = p * p;
+    p = p * p;
+    p = p * p;
+    float e = 1.0f - 1.0f / p;
+    e = __builtin_copysignf(e, u);
+    return (0.5f * y) * (1.0f + e);
+}
+
+__device__ __forceinline__ int8_t requant(int32_t acc, float sa, float sw, float bias,
+                                          float out_mult, uint32_t flags) {
+    float t = (float)acc;
+    t = t * sa;
+    t = t * sw;
+    if (flags & QGEMM_EPI_BIAS) t = t + bias;
+    const float g = (flags & QGEMM_EPI_GELU) ? gelu28(t) : t;
+    float v = __builtin_rintf(g * out_mult);
+    v = fminf(fmaxf(v, -127.0f), 127.0f);
+    return (int8_t)(int32_t)v;
+}
+
+__global__ __launch_bounds__(256, 2) void w8a8_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ W, const float* __restrict__ sa,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, float out_mult, uint32_t flags,
+    int8_t* __restrict__ Y, int32_t* __restrict__ acc_out, int M, int N, int K) {
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * LDK];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int h = lane >> 5, c32 = lane & 31;
+    const int kchunks = K / BK;
+
+    intx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0;
+
+    // each tile: 128 rows x 128 bytes = 1024 pieces of 16 bytes, 4 per thread
+    uintx4 ra[4], rw[4];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, col = idx & 7;
+            const int gm = m0 + row;
+            ra[i] = gm < M ? *reinterpret_cast<const uintx4*>(A + (size_t)gm * K + c * BK + col * 16)
+                           : uintx4{0, 0, 0, 0};
+            rw[i] = *reinterpret_cast<const uintx4*>(W + (size_t)(n0 + row) * K + c * BK + col * 16);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, col = idx & 7;
+            *reinterpret_cast<uintx4*>(&sA[buf][row * LDK + col * 16]) = ra[i];
+            *reinterpret_cast<uintx4*>(&sW[buf][row * LDK + col * 16]) = rw[i];
+        }
+    };
+
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < kchunks; ++c) {
+        const int buf = c & 1;
+        const bool more = c + 1 < kchunks;
+        if (more) load(c + 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // step s covers k = 32 s .. 32 s + 31; lane half h holds 16 of them
+            const int koff = 32 * s + 16 * h;
+            intx4 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const intx4*>(&sA[buf][(wm * 64 + i * 32 + c32) * LDK + koff]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                b[t] = *reinterpret_cast<const intx4*>(&sW[buf][(wn * 64 + t * 32 + c32) * LDK + koff]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma_i8(a[i], b[t], acc[i][t]);
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int col = n0 + wn * 64 + t * 32 + c32;
+        const float swv = sw[col];
+        const float bv = (flags & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+                if (row < M) {
+                    const int32_t a = acc[i][t][j];
+                    if (acc_out) acc_out[(size_t)row * N + col] = a;
+                    Y[(size_t)row * N + col] = requant(a, sa[row], swv, bv, out_mult, flags);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const float* a_scale,
+                                       const float* w_scale, const uint16_t* bias, float out_mult,
+                                       uint32_t flags, int8_t* Y, int32_t* acc_out, int32_t M,
+                                       int32_t N, int32_t K, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return QGEMM_BAD_SHAPE;
+    if (M == 0) return QGEMM_OK;
+    if (!A || !W || !a_scale || !w_scale || !Y) return QGEMM_NULL_PTR;
+    if ((flags & QGEMM_EPI_BIAS) && !bias) return QGEMM_NULL_PTR;
+    if (flags & ~(QGEMM_EPI_BIAS | QGEMM_EPI_GELU)) return QGEMM_UNSUPPORTED;
+    if (N == 0 || K == 0 || N % BN != 0 || K % BK != 0 || K > 133120) return QGEMM_UNSUPPORTED;
+    if (!qgh::aligned(A, 16) || !qgh::aligned(W, 16) || !qgh::aligned(Y, 16) ||
+        !qgh::aligned(a_scale, 4) || !qgh::aligned(w_scale, 4) || (bias && !qgh::aligned(bias, 2)) ||
+        (acc_out && !qgh::aligned(acc_out, 16)))
+        return QGEMM_MISALIGNED;
+    dim3 grid(N / BN, (M + BM - 1) / BM);
+    hipLaunchKernelGGL(w8a8_kernel, grid, dim3(256), 0, (hipStream_t)stream, A, W, a_scale, w_scale,
+                       bias, out_mult, flags, Y, acc_out, (int)M, (int)N, (int)K);
+    return qgh::launch_status();
+}

@@ -1,0 +1,214 @@
+/*
+ * libqgemm -- quantized GEMM kernels for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * C ABI.  Every entry point is asynchronous on the caller's HIP stream and
+ * returns an int32 status (0 = success), in the manner of the plugin
+ * `enqueue` calls of the TensorRT-Edge-LLM "Int4 Groupwise GEMM Plugin V2"
+ * and "Int4 Moe Plugin" pages (Public Functions: enqueue returns 0 on success,
+ * non-zero on error).  No C++ exception crosses this boundary and the library
+ * never prints or exits.
+ *
+ * Conventions for every function below:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory, caches nothing and keeps no state between
+ *     calls, so calls are re-entrant and thread-safe.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - All matrices are row-major and densely packed.
+ *   - `stream` is a hipStream_t (NULL = the null stream).
+ *   - Shapes, pointers, alignment and workspace are validated before any
+ *     launch; on a validation error nothing is launched and no output is
+ *     touched.  A launch failure returns QGEMM_HIP_ERROR.  Faults that happen
+ *     while a kernel runs surface at the caller's next synchronization.
+ *   - Every pointer must be 16-byte aligned (128-bit vector loads), except
+ *     the per-row/per-column vectors (scales, bias, routing outputs), which
+ *     need 4-byte alignment.
+ *   - Results are deterministic: fixed reduction orders, no floating-point
+ *     atomics; two calls with the same inputs give identical bits.
+ */
+#ifndef LIBQGEMM_H
+#define LIBQGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QGEMM_API __attribute__((visibility("default")))
+#else
+#define QGEMM_API
+#endif
+
+#define QGEMM_ABI_VERSION 1
+
+/* Status codes. */
+#define QGEMM_OK 0
+#define QGEMM_NULL_PTR 1            /* a required pointer is NULL */
+#define QGEMM_BAD_SHAPE 2           /* negative size, topK > E, G not dividing K, ... */
+#define QGEMM_MISALIGNED 3          /* a pointer violates the alignment rule above */
+#define QGEMM_WORKSPACE_TOO_SMALL 4 /* workspace_bytes below the *_workspace_bytes() query */
+#define QGEMM_UNSUPPORTED 5         /* valid request outside what this version implements */
+#define QGEMM_HIP_ERROR 6           /* a HIP launch or API call failed */
+
+/* Returns QGEMM_ABI_VERSION. */
+QGEMM_API int32_t qgemm_abi_version(void);
+
+/* Static string naming a status code ("unknown status" for other values). */
+QGEMM_API const char* qgemm_status_str(int32_t status);
+
+/* ------------------------------------------------------------------------
+ * W4A16 group-wise GEMM  (Int4 Groupwise GEMM Plugin V2 page, class summary
+ * and constructor: fp16 activations [b,seq,K] x int4 weights with fp16
+ * scales [ceil(K/G), N] -> fp16 [b,seq,N]; K = weight rows, N = weight
+ * columns, G = quantization group size; weights are repacked offline into a
+ * fragment layout, with no repack or cached weight buffer at run time).
+ *
+ *   Y[m][n] = fp16( sum_k A[m][k] * q(k,n) * S[k/G][n] )
+ *
+ * Natural weight format: uint8 [K][N/2]; column n of row k is the low nibble
+ * (bits 0-3) of byte [k][n/2] for even n and the high nibble for odd n; each
+ * nibble is a two's-complement int4 in [-8, 7].
+ *
+ * Supported in this version: K % 128 == 0, N % 128 == 0, G in {32, 64, 128}
+ * (K % G == 0 then holds); other shapes return QGEMM_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the fragment-layout weight buffer for a K x N int4 matrix
+   (= K*N/2); 0 if the shape is unsupported. */
+QGEMM_API size_t qgemm_w4a16_packed_bytes(int32_t K, int32_t N);
+
+/* Repack natural int4 weights into the library's gfx950 fragment layout.
+   w_natural: uint8 [K][N/2] (input, not modified).
+   w_frag:    uint8 [qgemm_w4a16_packed_bytes(K, N)] (output); must not
+              overlap w_natural.
+   Run once per weight matrix, offline; the layout is the library's own and
+   is only consumed by qgemm_w4a16 and moe_w4a16. */
+QGEMM_API int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag, int32_t K, int32_t N,
+                            void* stream);
+
+/* Workspace bytes qgemm_w4a16 needs for this shape (currently always 0). */
+QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
+
+/* Y = A x dequant(w_frag, scales).
+   A:      fp16 [M][K] activations (M = batch * sequence length).
+   w_frag: prepacked weights from qgemm_w4a16_prepack(K, N).
+   scales: fp16 [K/G][N].
+   Y:      fp16 [M][N] output; must not overlap the inputs.
+   M == 0 is a successful no-op.  M <= 16 runs the memory-bound decode
+   kernel, larger M the MFMA prefill kernel; both compute the same function
+   (fp32 accumulation, one rounding to fp16 at the end). */
+QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales, uint16_t* Y,
+                    int32_t M, int32_t N, int32_t K, int32_t G, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Symmetric int8 quantization, one scale per row  (INT8 cross-modal MHA
+ * TensorRT plugin interview page, answer step 1: scale = 127 / max|x| per
+ * output channel of the weights and per token of the activations, and
+ * knowledge point 5: codes limited to [-127, 127]; KV Cache INT8量化 page,
+ * quantize_symmetric / dequantize_symmetric).
+ *
+ * Per row r of `cols` contiguous values:
+ *   amax = max |x|;  amax == 0 -> scale 0 and all codes 0; otherwise
+ *   mult = fl32(127 / amax);  scale = fl32(amax / 127);
+ *   q = clamp(round_half_even(fl32(x * mult)), -127, 127)
+ * (each fl32 is one IEEE single-precision operation).
+ * Used for per-token activations, per-output-channel weights (rows of W
+ * [N][K]) and KV-cache rows (one row per (head, token)).
+ * ---------------------------------------------------------------------- */
+
+/* X: fp16 [rows][cols] (input); Q: int8 [rows][cols] (output);
+   scales: fp32 [rows] (output, the dequantization scale amax/127).
+   cols must be a multiple of 8 and at most 65536; rows == 0 is a no-op.
+   Codes and scales are bit-exact functions of X. */
+QGEMM_API int32_t quant_sym_int8(const uint16_t* X, int8_t* Q, float* scales, int32_t rows, int32_t cols,
+                       void* stream);
+
+/* X[r][c] = fp16( fl32( float(Q[r][c]) * scales[r] ) ), round to nearest even.
+   Q: int8 [rows][cols]; scales: fp32 [rows]; X: fp16 [rows][cols] (output).
+   cols must be a multiple of 8. */
+QGEMM_API int32_t dequant_sym_int8(const int8_t* Q, const float* scales, uint16_t* X, int32_t rows,
+                         int32_t cols, void* stream);
+
+/* ------------------------------------------------------------------------
+ * W8A8 int8 GEMM with fused epilogue  (INT8 cross-modal MHA TensorRT plugin
+ * interview page, knowledge points 1-2: int8 operands with integer
+ * accumulation, then rescale + bias + GELU and requantization to int8;
+ * answer step 3: per-tensor output scale and fp16 bias).
+ *
+ *   acc[m][n] = sum_k A[m][k] * W[n][k]                       (exact int32)
+ *   t = fl32(acc); t = t * a_scale[m]; t = t * w_scale[n];
+ *   if (flags & QGEMM_EPI_BIAS) t = t + float(bias[n]);
+ *   g = (flags & QGEMM_EPI_GELU) ? gelu(t) : t;
+ *   Y[m][n] = clamp(round_half_even(g * out_mult), -127, 127)
+ *
+ * gelu(t) = t/2 * (1 + erf(t / sqrt 2)) with erf from Abramowitz & Stegun
+ * formula 7.1.28, evaluated in a fixed fp32 sequence:
+ *   u = t * 0.70710678f; a = |u|;
+ *   p = fma(a, fma(a, fma(a, fma(a, fma(a, fma(a, a6, a5), a4), a3), a2), a1), 1);
+ *   p = p^16 by four squarings; e = copysign(1 - 1/p, u);  g = (0.5f * t) * (1 + e)
+ *   a1..a6 = 0.0705230784, 0.0422820123, 0.0092705272, 0.0001520143,
+ *            0.0002765672, 0.0000430638.
+ * ---------------------------------------------------------------------- */
+#define QGEMM_EPI_BIAS 1u
+#define QGEMM_EPI_GELU 2u
+
+/* A: int8 [M][K] activation codes; W: int8 [N][K] weight codes (one row per
+   output channel); a_scale: fp32 [M]; w_scale: fp32 [N]; bias: fp16 [N]
+   (may be NULL when QGEMM_EPI_BIAS is clear); Y: int8 [M][N] (output);
+   acc_out: int32 [M][N] raw accumulators (optional, NULL to skip).
+   Supported: any M >= 0, N % 128 == 0, K % 128 == 0 and K <= 133120 (so
+   |acc| <= K * 127^2 < 2^31).  Other shapes return QGEMM_UNSUPPORTED.
+   M == 0 is a successful no-op. */
+QGEMM_API int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const float* a_scale,
+                            const float* w_scale, const uint16_t* bias, float out_mult,
+                            uint32_t flags, int8_t* Y, int32_t* acc_out, int32_t M, int32_t N,
+                            int32_t K, void* stream);
+
+/* ------------------------------------------------------------------------
+ * INT4 mixture-of-experts layer  (Int4 Moe Plugin page, constructor:
+ * numExperts, topK, hiddenSize, moeInterSize, activationType,
+ * quantizationGroupSize; one output tensor).
+ *
+ * Routing: per token, the topK experts with the largest logits (the lower
+ * expert index wins ties), in descending order; gate weights = softmax over
+ * the selected logits (fp32).
+ * Expert FFN (activation 0, SiLU-gated):  g = x Wg_e, u = x Wu_e (W4A16,
+ * fp32 accumulation), h = fp16(silu(g) * u), o = h Wd_e (W4A16).
+ * Combine: Y[t] = fp16( sum_{j < topK} w[t][j] * o[t][j] ), j ascending.
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes moe_w4a16 needs (T tokens, hidden H, intermediate I,
+   E experts, topK).  Layout, in this order, each part 256-byte aligned:
+     int32 offsets[E+1]      first slot of each expert in the sorted order
+     int32 pairs[T*topK]     pair ids p = t*topK + j sorted by expert, then p
+     int32 slot_of[T*topK]   inverse of pairs
+     fp16  h[T*topK][I]      intermediate activations, sorted order
+     fp32  o[T*topK][H]      expert outputs, sorted order
+   The first two parts are part of the documented result (tests read them). */
+QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK);
+
+/* X: fp16 [T][H] hidden states; logits: fp16 [T][E] router logits.
+   w_gate_frag, w_up_frag: E consecutive prepacked matrices of
+     qgemm_w4a16_packed_bytes(H, I) bytes each (K = H rows, N = I columns).
+   w_down_frag: E consecutive prepacked matrices of
+     qgemm_w4a16_packed_bytes(I, H) bytes (K = I, N = H).
+   s_gate, s_up: fp16 [E][H/G][I]; s_down: fp16 [E][I/G][H].
+   Y: fp16 [T][H] (output); topk_ids: int32 [T][topK] (output);
+   topk_w: fp32 [T][topK] (output).
+   Supported: H % 128 == 0, I % 128 == 0, G in {32, 64, 128}, 1 <= topK <= E
+   <= 64, activation == 0.  T == 0 is a successful no-op. */
+QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
+                  const uint8_t* w_up_frag, const uint8_t* w_down_frag, const uint16_t* s_gate,
+                  const uint16_t* s_up, const uint16_t* s_down, uint16_t* Y, int32_t* topk_ids,
+                  float* topk_w, int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK,
+                  int32_t G, int32_t activation, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBQGEMM_H */

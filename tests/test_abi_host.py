@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library loads, exports every function include/libqgemm.h declares, and
+rejects invalid requests with the documented status codes before touching the
+GPU (validation happens before any launch).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libqgemm.h")
+LIB = os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", "libqgemm.so")
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"QGEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import torch  # noqa: F401  -- load torch's HIP runtime first, as the binding does
+    if not os.path.exists(LIB):
+        from bit_quantized_gemm_qgemm_amd import build
+        build.build()
+    import bit_quantized_gemm_qgemm_amd as qg
+    return qg.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert sorted(names) == sorted([
+        "qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
+        "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
+        "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    import bit_quantized_gemm_qgemm_amd as qg
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(qg.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert L.qgemm_abi_version() == 1
+    assert L.qgemm_status_str(0) == b"ok"
+    assert L.qgemm_status_str(4) == b"workspace too small"
+    assert L.qgemm_status_str(99) == b"unknown status"
+
+
+def test_size_queries(L):
+    assert L.qgemm_w4a16_packed_bytes(4096, 11008) == 4096 * 11008 // 2
+    assert L.qgemm_w4a16_packed_bytes(4000, 11008) == 0
+    assert L.qgemm_w4a16_packed_bytes(4096, 100) == 0
+    assert L.qgemm_w4a16_workspace_bytes(1, 11008, 4096, 128) == 0
+    ws = L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2)
+    P_ = 512
+    need = 256 + 2 * 2048 + 2 * P_ * 14336 + 4 * P_ * 4096
+    assert need <= ws <= need + 5 * 256
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def test_w4a16_validation(L):
+    f = L.qgemm_w4a16
+    assert f(None, None, None, None, 0, 128, 128, 128, None, 0, None) == 0  # M == 0: no-op
+    assert f(None, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 128, 128, 128, None, 0, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 128, 96, None, 0, None) == 2  # G does not divide K
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 120, 128, 128, None, 0, None) == 5
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 256, 256, None, 0, None) == 5  # G = 256
+    assert f(FAKE + 2, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE + 8, 4, 128, 128, 128, None, 0, None) == 3
+
+
+def test_prepack_validation(L):
+    f = L.qgemm_w4a16_prepack
+    assert f(None, FAKE, 128, 128, None) == 1
+    assert f(FAKE, FAKE, 0, 128, None) == 0
+    assert f(FAKE, FAKE, 100, 128, None) == 5
+    assert f(FAKE, FAKE + 4, 128, 128, None) == 3
+    assert f(FAKE, FAKE + 4096, 128, 128, None) == 2  # overlapping buffers
+
+
+def test_quant_validation(L):
+    q, d = L.quant_sym_int8, L.dequant_sym_int8
+    assert q(FAKE, FAKE, FAKE, 0, 128, None) == 0
+    assert q(None, FAKE, FAKE, 4, 128, None) == 1
+    assert q(FAKE, FAKE, FAKE, 4, 12, None) == 5
+    assert q(FAKE, FAKE, FAKE, 4, 65544, None) == 5
+    assert q(FAKE + 8, FAKE, FAKE, 4, 128, None) == 3
+    assert d(FAKE, FAKE, None, 4, 128, None) == 1
+    assert d(FAKE, FAKE, FAKE, -4, 128, None) == 2
+    assert d(FAKE, FAKE, FAKE, 4, 100, None) == 5
+
+
+def test_w8a8_validation(L):
+    f = L.qgemm_w8a8_epilogue
+    args = lambda M, N, K, flags=3, bias=FAKE, a=FAKE: (a, FAKE, FAKE, FAKE, bias, 1.0, flags, FAKE,
+                                                         None, M, N, K, None)
+    assert f(*args(0, 128, 128)) == 0
+    assert f(*args(4, 128, 128, bias=None)) == 1      # BIAS flag without a bias
+    assert f(*args(4, 128, 128, flags=8)) == 5        # unknown flag
+    assert f(*args(4, 100, 128)) == 5
+    assert f(*args(4, 128, 133248)) == 5              # accumulator could overflow
+    assert f(*args(4, 128, 128, a=FAKE + 1)) == 3
+    assert f(*args(-4, 128, 128)) == 2
+
+
+def test_moe_validation(L):
+    f = L.moe_w4a16
+    def call(T=4, H=128, I=128, E=4, topK=2, G=128, act=0, ws=FAKE, wsb=1 << 30):
+        return f(*([FAKE] * 11), T, H, I, E, topK, G, act, ws, wsb, None)
+    assert call(T=0) == 0
+    assert call(topK=5) == 2
+    assert call(E=0) == 2
+    assert call(act=1) == 5
+    assert call(E=65, topK=2) == 5
+    assert call(H=192, G=64) == 5
+    assert call(ws=None) == 1
+    assert call(ws=FAKE + 16) == 3
+    assert call(wsb=16) == 4
