@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-GEMM hot path on one MI355X.
+
+Headline workload (one JSON line on stdout): the W4A16 decode GEMV sweep,
+K=4096, N=11008, G=128 (a 7B-class MLP up-projection), fp16 activations with
+M = 1, 4 and 8.  One step = one launch at each M.  Every launch reads a
+different one of 16 weight sets (16 x 23.2 MB > the 256 MB Infinity Cache),
+so the weights stream from HBM.  Steps are recorded once as HIP graphs (the
+library's launches on torch's current stream are captured) and replayed, so
+host launch overhead does not pace the GPU.
+
+value      = algorithmic bytes of a step / time of a step (GB/s, HBM-bound)
+roofline   = the M=1 decode kernel: algorithmic bytes per launch / its mean
+             duration, timed with HIP events around a graph of 48 launches;
+             peak 8000 GB/s (MI355X HBM3E)
+cpu_baseline = the CPU oracle on the same step (all host threads the oracle
+             uses), repeated for about 10 s
+rows       = every other hot-path row, each timed the same way on its own
+             inputs (prefill GEMM, W8A8 GEMM + epilogue, per-token int8
+             quantization, KV-cache quant/dequant, INT4 MoE layer)
+
+Usage: python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+I8_MFMA_PEAK_TOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 op/clk (dense)
+
+DEC_K, DEC_N, DEC_G = 4096, 11008, 128
+DEC_MS = (1, 4, 8)
+ROT = 16
+
+
+def w4a16_bytes(M, N, K, G):
+    return K * N // 2 + 2 * (K // G) * N + 2 * M * K + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_gemm_qgemm_amd as qg
+    import qgemm_inputs as qi
+
+    if not os.path.exists(qg.LIB_PATH):
+        from bit_quantized_gemm_qgemm_amd import build
+        build.build()
+    qg.lib()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    def graph_of(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        return g
+
+    def time_graph(g, launches, reps, warmup=3):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (reps * launches)  # seconds per launch
+
+    # ------------------------------------------------------------ decode inputs
+    log(f"[bench] device {props.name}, {props.multi_processor_count} CUs; building 16 weight sets")
+    sets = []
+    for r in range(ROT):
+        Wb, S = qi.w4a16_weights(DEC_K, DEC_N, DEC_G, 101 + 1000 * r)
+        Wf = qg.qgemm_w4a16_prepack(to_dev(Wb), DEC_K, DEC_N)
+        sets.append((Wf, to_dev(S)))
+    acts = {M: [to_dev(qi.activations(M, DEC_K, 1010 + M + 7919 * r)) for r in range(ROT)]
+            for M in DEC_MS}
+    outs = {M: torch.empty((M, DEC_N), dtype=torch.float16, device=dev) for M in DEC_MS}
+    torch.cuda.synchronize()
+
+    def decode_launch(M, r):
+        Wf, S = sets[r % ROT]
+        return lambda: qg.qgemm_w4a16(acts[M][r % ROT], Wf, S, DEC_G, Y=outs[M])
+
+    # one graph per rotation offset; step k replays graph k % ROT
+    step_graphs = []
+    for k in range(ROT):
+        fns = [decode_launch(M, 3 * k + i) for i, M in enumerate(DEC_MS)]
+        step_graphs.append(graph_of(fns))
+    step_bytes = sum(w4a16_bytes(M, DEC_N, DEC_K, DEC_G) for M in DEC_MS)
+    step_flops = sum(2 * M * DEC_N * DEC_K for M in DEC_MS)
+
+    for k in range(args.warmup):
+        step_graphs[k % ROT].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(args.steps):
+        step_graphs[k % ROT].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    value = step_bytes / step_s / 1e9
+    log(f"[bench] decode step {step_s * 1e6:.2f} us, {value:.1f} GB/s")
+
+    # per-kernel mean durations: graphs of 48 launches of one M, rotating sets
+    per_m = {}
+    for M in DEC_MS:
+        g = graph_of([decode_launch(M, r) for r in range(3 * ROT)])
+        t = time_graph(g, 3 * ROT, reps=max(4, args.steps // 16))
+        b = w4a16_bytes(M, DEC_N, DEC_K, DEC_G)
+        per_m[M] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1),
+                    "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOP/s": round(2 * M * DEC_N * DEC_K / t / 1e12, 3)}
+        log(f"[bench] decode M={M}: {per_m[M]}")
+
+    b1 = w4a16_bytes(1, DEC_N, DEC_K, DEC_G)
+    achieved = b1 / (per_m[1]["us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<128> M=1",
+                "bytes_per_launch": b1}
+
+    rows = {}
+    if not args.no_rows:
+        rows = bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(np, qi, step_bytes, args.cpu_seconds, log)
+
+    line = {
+        "metric": "W4A16 qGEMM TFLOP/s & HBM GB/s (% roofline) at decode M=1 and prefill M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "W4A16 decode GEMV sweep M in {1,4,8}, K=4096 N=11008 G=128, "
+                               "16 rotated weight sets",
+                   "M": list(DEC_MS), "K": DEC_K, "N": DEC_N, "G": DEC_G,
+                   "rotation_sets": ROT, "step_flops": step_flops, "step_bytes": step_bytes,
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": {str(M): v for M, v in per_m.items()},
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def read_traffic():
+    """HBM bytes per launch of the M=1 decode kernel from the committed counter
+    summary, if it was taken on the current kernel source; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", "csrc", "w4a16.hip")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+        if d.get("source_sha256_16") != h:
+            return None
+        return d.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
+    rows = {}
+    dev = torch.device("cuda:0")
+
+    # cfg0: W4A16 M=16 K=N=512 G=128 (launch-latency sized)
+    A, Wb, S = qi.w4a16_problem(16, 512, 512, 128, 100)
+    Wf = qg.qgemm_w4a16_prepack(to_dev(Wb), 512, 512)
+    Ad, Sd = to_dev(A), to_dev(S)
+    Y = torch.empty((16, 512), dtype=torch.float16, device=dev)
+    g = graph_of([lambda: qg.qgemm_w4a16(Ad, Wf, Sd, 128, Y=Y)] * 32)
+    t = time_graph(g, 32, reps=20)
+    b = w4a16_bytes(16, 512, 512, 128)
+    rows["w4a16_cfg0_M16_K512_N512"] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1)}
+    log(f"[bench] cfg0 {rows['w4a16_cfg0_M16_K512_N512']}")
+
+    # cfg2: prefill M=2048 K=N=4096 G=128, 12 rotated sets (12 x 25 MB)
+    M, K, N, G = 2048, 4096, 4096, 128
+    R = 12
+    probs = []
+    for r in range(R):
+        A, Wb, S = qi.w4a16_problem(M, K, N, G, 102 + 1000 * r)
+        probs.append((to_dev(A), qg.qgemm_w4a16_prepack(to_dev(Wb), K, N), to_dev(S)))
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    g = graph_of([(lambda p=p: qg.qgemm_w4a16(p[0], p[1], p[2], G, Y=Y)) for p in probs])
+    t = time_graph(g, R, reps=10)
+    fl = 2 * M * N * K
+    b = w4a16_bytes(M, N, K, G)
+    rows["w4a16_prefill_M2048_K4096_N4096"] = {
+        "us": round(t * 1e6, 2), "TFLOP/s": round(fl / t / 1e12, 1),
+        "mfma_frac": round(fl / t / 1e12 / F16_MFMA_PEAK_TFLOPS, 4), "GB/s": round(b / t / 1e9, 1)}
+    log(f"[bench] prefill {rows['w4a16_prefill_M2048_K4096_N4096']}")
+    del probs
+
+    # cfg3a: W8A8 M=N=K=4096: per-token activation quant + GEMM with epilogue
+    M = N = K = 4096
+    X, Wf16, bias, om = qi.w8a8_problem(M, N, K, 103)
+    Xd = to_dev(X)
+    qw, sw = qg.quant_sym_int8(to_dev(Wf16))
+    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sa = torch.empty(M, dtype=torch.float32, device=dev)
+    biasd = to_dev(bias)
+    Yq = torch.empty((M, N), dtype=torch.int8, device=dev)
+    gq = graph_of([lambda: qg.quant_sym_int8(Xd, Q=qa, scales=sa)] * 8)
+    tq = time_graph(gq, 8, reps=10)
+    qb = 3 * M * K + 4 * M
+    rows["quant_sym_int8_act_4096x4096"] = {"us": round(tq * 1e6, 2), "GB/s": round(qb / tq / 1e9, 1),
+                                            "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4)}
+    qg.quant_sym_int8(Xd, Q=qa, scales=sa)
+    gg = graph_of([lambda: qg.qgemm_w8a8_epilogue(qa, qw, sa, sw, biasd, float(om), 3, Y=Yq)] * 8)
+    tg = time_graph(gg, 8, reps=10)
+    ops = 2 * M * N * K
+    rows["w8a8_gemm_gelu_4096"] = {"us": round(tg * 1e6, 2), "TOPS": round(ops / tg / 1e12, 1),
+                                   "mfma_frac": round(ops / tg / 1e12 / I8_MFMA_PEAK_TOPS, 4)}
+    log(f"[bench] w8a8 {rows['w8a8_gemm_gelu_4096']} quant {rows['quant_sym_int8_act_4096x4096']}")
+    del Xd, qw, qa, Yq
+
+    # cfg3b: KV cache [32, 2048, 128] quant + dequant, 16 rotated sets
+    R = 16
+    kvs = [to_dev(qi.kv_problem(32, 2048, 128, 103 + 1000 * r)) for r in range(R)]
+    Q = torch.empty((32, 2048, 128), dtype=torch.int8, device=dev)
+    Sk = torch.empty(32 * 2048, dtype=torch.float32, device=dev)
+    Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
+    Qs = [torch.empty((32, 2048, 128), dtype=torch.int8, device=dev) for _ in range(R)]
+    Ss = [torch.empty(32 * 2048, dtype=torch.float32, device=dev) for _ in range(R)]
+    for r in range(R):
+        qg.quant_sym_int8(kvs[r], Q=Qs[r], scales=Ss[r])
+    gk = graph_of([(lambda r=r: qg.quant_sym_int8(kvs[r], Q=Q, scales=Sk)) for r in range(R)])
+    tk = time_graph(gk, R, reps=10)
+    gd = graph_of([(lambda r=r: qg.dequant_sym_int8(Qs[r], Ss[r], X=Xo)) for r in range(R)])
+    td = time_graph(gd, R, reps=10)
+    kb = 3 * 65536 * 128 + 4 * 65536
+    rows["kv_quant_32x2048x128"] = {"us": round(tk * 1e6, 2), "GB/s": round(kb / tk / 1e9, 1),
+                                    "hbm_frac": round(kb / tk / 1e9 / HBM_PEAK_GBS, 4)}
+    rows["kv_dequant_32x2048x128"] = {"us": round(td * 1e6, 2), "GB/s": round(kb / td / 1e9, 1),
+                                      "hbm_frac": round(kb / td / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] kv {rows['kv_quant_32x2048x128']} {rows['kv_dequant_32x2048x128']}")
+    del kvs, Qs, Ss
+
+    # cfg4: INT4 MoE T=256 H=4096 I=14336 E=8 top-2 G=128 (760 MB working set)
+    T, H, I, E, topK, G = 256, 4096, 14336, 8, 2, 128
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 104)
+    pg = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wg[e]), H, I) for e in range(E)])
+    pu = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wu[e]), H, I) for e in range(E)])
+    pd = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wd[e]), I, H) for e in range(E)])
+    del Wg, Wu, Wd
+    Xd, Ld, Sgd, Sud, Sdd = (to_dev(a) for a in (X, logits, Sg, Su, Sd))
+    Ym = torch.empty((T, H), dtype=torch.float16, device=dev)
+    ids = torch.empty((T, topK), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, topK), dtype=torch.float32, device=dev)
+    ws = torch.empty(qg.moe_w4a16_workspace_bytes(T, H, I, E, topK), dtype=torch.uint8, device=dev)
+    run = lambda: qg.moe_w4a16(Xd, Ld, pg, pu, pd, Sgd, Sud, Sdd, topK, G, Y=Ym, topk_ids=ids,
+                               topk_w=wts, workspace=ws)
+    gm = graph_of([run] * 4)
+    tm = time_graph(gm, 4, reps=5)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+    hit = int((counts > 0).sum())
+    P = T * topK
+    wbytes = hit * (3 * H * I // 2 + 2 * (2 * (H // G) * I + (I // G) * H))
+    abytes = 2 * T * H + 2 * T * E + 2 * 2 * P * I + 2 * 4 * P * H + 2 * T * H
+    fl = 6 * P * H * I
+    rows["moe_T256_H4096_I14336_E8_top2"] = {
+        "us": round(tm * 1e6, 2), "TFLOP/s": round(fl / tm / 1e12, 1),
+        "mfma_frac": round(fl / tm / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+        "GB/s": round((wbytes + abytes) / tm / 1e9, 1),
+        "hbm_frac": round((wbytes + abytes) / tm / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_expert": counts.tolist()}
+    log(f"[bench] moe {rows['moe_T256_H4096_I14336_E8_top2']}")
+    return rows
+
+
+def cpu_baseline(np, qi, step_bytes, seconds, log):
+    """The oracle, as it stands, on the decode step (full outputs at M=1,4,8)."""
+    import oracle
+    Wb, S = qi.w4a16_weights(DEC_K, DEC_N, DEC_G, 101)
+    acts = {M: qi.activations(M, DEC_K, 1010 + M) for M in DEC_MS}
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for M in DEC_MS:
+            oracle.w4a16(acts[M], Wb, S, DEC_G)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_step = el / reps
+    log(f"[bench] cpu oracle: {reps} steps in {el:.1f} s")
+    return {"value": round(step_bytes / per_step / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} decode steps (M=1,4,8 full outputs, K=4096 N=11008 G=128), "
+                      f"{el:.1f} s, fp64 sums, OpenMP over output columns",
+            "s_per_step": round(per_step, 4)}
+
+
+if __name__ == "__main__":
+    main()

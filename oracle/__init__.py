@@ -43,6 +43,7 @@ _U32 = ctypes.c_uint32
 
 def _declare(lib):
     sig = {
+        "qo_num_threads": (ctypes.c_int, []),
         "qo_f16_to_f64": (ctypes.c_double, [ctypes.c_uint16]),
         "qo_f64_to_f16": (ctypes.c_uint16, [ctypes.c_double]),
         "qo_f16_to_f64_array": (None, [_P, _P, _I64]),
@@ -80,6 +81,11 @@ def _c(a, dtype):
     if a.dtype != dtype:
         raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
     return a
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().qo_num_threads()
 
 
 # ---------------------------------------------------------------- fp16

@@ -42,11 +42,15 @@
  *        quantizationGroupSize).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define QO_API __attribute__((visibility("default")))
+
+/* Number of OpenMP threads the parallel loops below use. */
+QO_API int qo_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16                                                        */
