@@ -32,51 +32,32 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 //
 // Fragment-layout word: eight offset-binary nibbles u = v + 8 holding the
 // weights v_0..v_7 of eight consecutive k of one column, at nibble positions
-// [v0 v2 v4 v6 v1 v3 v5 v7] (bits 0-3 hold v0).  With the fp16 exponent of
-// 1024 or'ed in, a nibble in bits 0-3 (16-19) reads as 1024 + u and a nibble
-// in bits 4-7 (20-23) as 1024 + 16u, so two and-or ops plus one packed add
-// or fma give two exact fp16 integers.
-struct HalfPairs {
-    half2v w01, w23, w45, w67;
-};
-
-__device__ __forceinline__ HalfPairs dequant_pairs(uint32_t d) {
-    const uint32_t magic = 0x64006400u;
-    const uint32_t d8 = d >> 8;
-    const half2v p01 = __builtin_bit_cast(half2v, (d & 0x000f000fu) | magic);
-    const half2v p23 = __builtin_bit_cast(half2v, (d & 0x00f000f0u) | magic);
-    const half2v p45 = __builtin_bit_cast(half2v, (d8 & 0x000f000fu) | magic);
-    const half2v p67 = __builtin_bit_cast(half2v, (d8 & 0x00f000f0u) | magic);
-    const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-    const half2v off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
-    HalfPairs r;
-    r.w01 = p01 + off;
-    r.w45 = p45 + off;
-    r.w23 = __builtin_elementwise_fma(p23, sixteenth, off16);
-    r.w67 = __builtin_elementwise_fma(p67, sixteenth, off16);
-    return r;
+// [v0 v2 v4 v6 v1 v3 v5 v7] (bits 0-3 hold v0).  Masking the low and the
+// high nibble of every byte and splicing each with the byte 0x64 (v_perm_b32)
+// gives fp16 values 1024 + u, exactly, in the order v0..v7:
+//   lo = d & 0x0f0f0f0f holds (v0, v4, v1, v5), hi = (d >> 4) & 0x0f0f0f0f
+//   holds (v2, v6, v3, v7); selector 0x00060004 takes bytes 0 and 2 of the
+//   first operand, 0x00070005 bytes 1 and 3, each under an 0x64.
+// Seven VALU ops per eight weights, all visible to the compiler (inline asm
+// is avoided here: LLVM does not track MFMA hazards across it).
+__device__ __forceinline__ half8 raw8(uint32_t d) {
+    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu, e = 0x64646464u;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 r = {__builtin_amdgcn_perm(lo, e, 0x00060004u), __builtin_amdgcn_perm(hi, e, 0x00060004u),
+                     __builtin_amdgcn_perm(lo, e, 0x00070005u), __builtin_amdgcn_perm(hi, e, 0x00070005u)};
+    return __builtin_bit_cast(half8, r);
 }
 
-// Concatenate four half2 into the 8-element MFMA operand (w0 .. w7).
-// (Built with shufflevector: rewriting the elements of a 4 x u32 vector
-// through __builtin_bit_cast was miscompiled by this toolchain.)
-__device__ __forceinline__ half8 concat8(half2v a, half2v b, half2v c, half2v d) {
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    const half4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-    const half4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
+// Exact fp16 weights v = (1024 + u) - 1032.
 __device__ __forceinline__ half8 dequant8(uint32_t d) {
-    const HalfPairs p = dequant_pairs(d);
-    return concat8(p.w01, p.w23, p.w45, p.w67);
+    const _Float16 c = (_Float16)-1032.0f;
+    return raw8(d) + half8{c, c, c, c, c, c, c, c};
 }
 
 // Same, multiplied by a per-column scale (fp16 rounding of q*s).
 __device__ __forceinline__ half8 dequant8_scaled(uint32_t d, half2v s2) {
-    const HalfPairs p = dequant_pairs(d);
-    return concat8(p.w01 * s2, p.w23 * s2, p.w45 * s2, p.w67 * s2);
+    const half8 s8 = __builtin_shufflevector(s2, s2, 0, 1, 0, 1, 0, 1, 0, 1);
+    return dequant8(d) * s8;
 }
 
 // ---------------------------------------------------------------- fragment layout

@@ -166,18 +166,19 @@ __device__ __forceinline__ void grouped_mainloop(GroupedTile<G, NB>& tile, uint1
             for (int j = 0; j < 16; ++j) tile.acc[b][t][j] = 0.f;
 
     // A staging: 64 rows x 256 bytes = 1024 pieces, 4 per thread
+    // rows past the expert's last one repeat row 0 (unconditional loads; those
+    // accumulator rows are not stored)
     const uint16_t* src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
         const uint16_t* r = row_src(row);
-        src[i] = r ? r + col * 8 : nullptr;
+        src[i] = (r ? r : row_src(0)) + col * 8;
     }
     uintx4 areg[4];
     auto load_a = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            areg[i] = src[i] ? *reinterpret_cast<const uintx4*>(src[i] + c * 128) : uintx4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) areg[i] = *reinterpret_cast<const uintx4*>(src[i] + c * 128);
     };
     auto store_a = [&](int buf) {
 #pragma unroll

@@ -27,68 +27,150 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void w4a16_decode_kernel(const uint16_t* __restrict__ A,
-                                                           const uint8_t* __restrict__ wf,
-                                                           const uint16_t* __restrict__ S,
-                                                           uint16_t* __restrict__ Y, int M, int N,
-                                                           int K) {
-    constexpr int BATCH = 8;  // chunks per wave in flight
-    const int strip = blockIdx.x;
+// Decode kernel.  MT = rows of the MFMA A tile that may be non-zero
+// (M <= MT <= 16); each wave owns NSW 16-column strips and KCW 128-k chunks
+// (NSW * KCW 16-byte weight loads per lane); WK = 32 / KCW waves cover
+// 4096 k, so a workgroup of WK waves holds NSW strips over a whole 4096-k
+// block and reduces its K partials in LDS in a fixed order.
+//
+// Everything a wave needs is staged by that wave alone, in its own slice of
+// LDS, so there is no barrier before the main loop: it issues the loads of
+// its A slice (rows < M), of its group scales and then all eight weight
+// loads; while the weights stream in it writes A and the scales to LDS and
+// forms the per-(row, group) constant C = 1032 * sum_k a_k.  The MFMAs work on
+// the raw fp16 values 1024 + u (raw8, seven VALU ops per eight weights); each
+// group's fp32 partial T becomes acc += s * (T - C).  One A fragment read from
+// LDS feeds the MFMAs of all NSW strips.
+template <int MT, int NSW, int KCW, int G>
+__global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ wf, const uint16_t* __restrict__ Sc,
+    uint16_t* __restrict__ Y, int M, int N, int K) {
+    constexpr int WK = 32 / KCW;                 // waves per workgroup (one 4096-k block)
+    constexpr int KW = KCW * 128;                // k per wave
+    constexpr int LDA = KW + 8;                  // halfs per staged A row (+16 B pad)
+    constexpr int APIECES = MT * KW / 8;         // 16-byte A pieces per wave
+    constexpr int APL = APIECES < 64 ? 1 : APIECES / 64;  // per lane
+    constexpr int NG = 128 / G, KKPG = G / 32;   // groups per chunk, k-steps per group
+    constexpr int GW = KCW * NG;                 // groups per wave
+    constexpr int GP = G / 8;                    // A pieces per group and row
+    constexpr int SPL = GW * NSW * 2;            // 16-byte scale pieces per wave (<= 64)
+    static_assert(APIECES < 64 || APL * 64 == APIECES, "A staging must tile the wave's slice");
+    static_assert(SPL <= 64, "one scale piece per lane");
+    struct WaveLds {
+        _Float16 a[MT * LDA];
+        float c[GW][16];
+        uint16_t s[GW][NSW * 16];
+    };
+    constexpr size_t RED = sizeof(floatx4) * WK * NSW * 64;  // K-partials for the reduction
+    constexpr size_t STAGE = sizeof(WaveLds) * WK;
+    __shared__ __attribute__((aligned(16))) char lds_raw[STAGE > RED ? STAGE : RED];
+    WaveLds* lds = reinterpret_cast<WaveLds*>(lds_raw);
+
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    WaveLds& L = lds[wave];
+    const int strip0 = blockIdx.x * NSW;
     const int cl = lane & 15, q = lane >> 4;
     const int kchunks = K / 128;
-    const int n = strip * 16 + cl;
-    const bool arow_ok = cl < M;  // A-fragment row of this lane is cl
-    const uint16_t* arow = A + (size_t)(arow_ok ? cl : 0) * K + q * 8;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int arow = cl & (MT - 1);  // rows >= MT of the MFMA tile are never stored
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[NSW];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) acc[s] = zero;
 
-    for (int c0 = wave; c0 < kchunks; c0 += 4 * BATCH) {
-        uintx4 raw[BATCH];
+    for (int kb0 = 0; kb0 < K; kb0 += 4096) {
+        const int kw0 = kb0 + wave * KW;             // first k of this wave
+        const int kwl = K - kw0 < KW ? K - kw0 : KW;  // k of this wave in this block (may be <= 0)
+        // Loads, in the order they are needed: A, scales, weights.  Every load
+        // is unconditional (out-of-range requests are clamped to valid data
+        // that is never used): a load under a branch makes the compiler wait
+        // for all outstanding loads at the join, which would serialize the
+        // weight stream behind the staging.  Rows >= M repeat row M-1; they
+        // only feed accumulator rows that are never stored.
+        uintx4 ast[APL];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int c = c0 + 4 * i;
-            raw[i] = c < kchunks ? ldg_nt(reinterpret_cast<const uintx4*>(
-                                       wf + frag_block_offset(strip, c, kchunks) + lane * 16))
-                                 : uintx4{0, 0, 0, 0};
+        for (int p = 0; p < APL; ++p) {
+            const int idx = lane + 64 * p;
+            const int row = idx / (KW / 8) < M ? idx / (KW / 8) : M - 1;
+            const int c8 = (idx < APIECES && (idx % (KW / 8)) * 8 < kwl) ? idx % (KW / 8) : 0;
+            ast[p] = *reinterpret_cast<const uintx4*>(A + (size_t)row * K + kw0 * (kwl > 0) + c8 * 8);
         }
+        const int sp_g = lane / (NSW * 2), sp_r = lane % (NSW * 2);  // group, 8-column piece
+        const bool sp_ok = lane < SPL && sp_g * G < kwl;
+        const uintx4 sreg = *reinterpret_cast<const uintx4*>(
+            Sc + (sp_ok ? (size_t)(kw0 / G + sp_g) * N + strip0 * 16 + sp_r * 8 : 0));
+        uintx4 braw[KCW][NSW];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int c = c0 + 4 * i;
-            if (c >= kchunks) break;
+        for (int i = 0; i < KCW; ++i)
+#pragma unroll
+            for (int s = 0; s < NSW; ++s) {
+                const int c = i * 128 < kwl ? kw0 / 128 + i : 0;
+                braw[i][s] = ldg_nt(reinterpret_cast<const uintx4*>(
+                    wf + frag_block_offset(strip0 + s, c, kchunks) + lane * 16));
+            }
+        // keep every load above ahead of the first use of any of them
+        __builtin_amdgcn_sched_barrier(0);
+        // stage A and C; rows < MT only, pieces of a (row, group) sit in GP adjacent lanes
+#pragma unroll
+        for (int p = 0; p < APL; ++p) {
+            const int idx = lane + 64 * p, row = idx / (KW / 8), c8 = idx % (KW / 8);
+            // (Whole-vector bit casts only: a bit cast of one element of a
+            // u32x4 was miscompiled by this toolchain into element 0.)
+            const half8 h = __builtin_bit_cast(half8, ast[p]);
+            float part = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part += (float)h[j];
+#pragma unroll
+            for (int off = 1; off < GP; off <<= 1) part += __shfl_xor(part, off);
+            if (idx < APIECES) {
+                *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
+                if (c8 % GP == 0) L.c[c8 / GP][row] = part * 1032.0f;
+            }
+        }
+        if (lane < SPL) *reinterpret_cast<uintx4*>(&L.s[sp_g][sp_r * 8]) = sreg;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < KCW; ++i) {
+            if (i * 128 >= kwl) break;
+            const _Float16* ap = L.a + arow * LDA + i * 128 + q * 8;
             half8 a[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                a[kk] = arow_ok ? *reinterpret_cast<const half8*>(arow + c * 128 + kk * 32)
-                                : half8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-            const uint32_t d[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-            constexpr int KK_PER_G = G / 32;  // MFMA k-steps per scale group
+            for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const half8*>(ap + kk * 32);
 #pragma unroll
-            for (int g0 = 0; g0 < 4; g0 += KK_PER_G) {
-                floatx4 tmp = mfma16(a[g0], dequant8(d[g0]), zero);
+            for (int g = 0; g < NG; ++g) {
+                const int gl = i * NG + g;
+                const floatx4 cc = *reinterpret_cast<const floatx4*>(&L.c[gl][4 * q]);
 #pragma unroll
-                for (int kk = g0 + 1; kk < g0 + KK_PER_G; ++kk) tmp = mfma16(a[kk], dequant8(d[kk]), tmp);
-                const float s = h2f(S[(size_t)((c * 128 + g0 * 32) / G) * N + n]);
+                for (int s = 0; s < NSW; ++s) {
+                    const uint32_t d[4] = {braw[i][s].x, braw[i][s].y, braw[i][s].z, braw[i][s].w};
+                    floatx4 tmp = zero;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(tmp[j], s, acc[j]);
+                    for (int kk = g * KKPG; kk < (g + 1) * KKPG; ++kk)
+                        tmp = mfma16(a[kk], raw8(d[kk]), tmp);
+                    const float sv = h2f(L.s[gl][s * 16 + cl]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[s][j] = __builtin_fmaf(tmp[j] - cc[j], sv, acc[s][j]);
+                }
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
 
-    __shared__ floatx4 red[4][64];
-    red[wave][lane] = acc;
+    // K partials of the workgroup's strips, added in wave order
     __syncthreads();
-    if (wave == 0) {
-        floatx4 s = red[0][lane];
-        s += red[1][lane];
-        s += red[2][lane];
-        s += red[3][lane];
+    floatx4* red = reinterpret_cast<floatx4*>(lds_raw);
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) red[(wave * NSW + s) * 64 + lane] = acc[s];
+    __syncthreads();
+    // wave w < NSW finalizes strip w
+    if (wave < NSW) {
+        floatx4 t = red[wave * 64 + lane];
+        for (int w = 1; w < WK; ++w) t += red[(w * NSW + wave) * 64 + lane];
+        const int n = (strip0 + wave) * 16 + cl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 4 * q + j;  // accumulator layout: rows 4*(l/16)+j, column l%16
-            if (row < M) Y[(size_t)row * N + n] = f2h(s[j]);
+            if (row < M) Y[(size_t)row * N + n] = f2h(t[j]);
         }
     }
 }
@@ -126,8 +208,8 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
         for (int i = 0; i < 8; ++i) {
             const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
             const int gm = m0 + row;
-            areg[i] = gm < M ? *reinterpret_cast<const uintx4*>(A + (size_t)gm * K + c * 128 + col * 8)
-                             : uintx4{0, 0, 0, 0};
+            // rows >= M repeat row M-1 (unconditional load; those rows are not stored)
+            areg[i] = *reinterpret_cast<const uintx4*>(A + (size_t)(gm < M ? gm : M - 1) * K + c * 128 + col * 8);
         }
     };
     auto store_a = [&](int buf) {
@@ -190,8 +272,23 @@ template <int G>
 int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, uint16_t* Y, int M,
                      int N, int K, hipStream_t st) {
     if (M <= 16) {
-        hipLaunchKernelGGL(w4a16_decode_kernel<G>, dim3(N / 16), dim3(256), 0, st, A, wf, S, Y, M,
-                           N, K);
+        // (MT, NSW, KCW): rows of the MFMA tile, 16-column strips per wave, 128-k
+        // chunks per wave; the workgroup is 32 / KCW waves over NSW strips
+        if (M == 1)
+            hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 8, G>), dim3(N / 16), dim3(256), 0, st,
+                               A, wf, S, Y, M, N, K);
+        else if (M == 2)
+            hipLaunchKernelGGL((w4a16_decode_kernel<2, 1, 8, G>), dim3(N / 16), dim3(256), 0, st,
+                               A, wf, S, Y, M, N, K);
+        else if (M <= 4)
+            hipLaunchKernelGGL((w4a16_decode_kernel<4, 2, 4, G>), dim3(N / 32), dim3(512), 0, st,
+                               A, wf, S, Y, M, N, K);
+        else if (M <= 8)
+            hipLaunchKernelGGL((w4a16_decode_kernel<8, 2, 4, G>), dim3(N / 32), dim3(512), 0, st,
+                               A, wf, S, Y, M, N, K);
+        else
+            hipLaunchKernelGGL((w4a16_decode_kernel<16, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
+                               A, wf, S, Y, M, N, K);
     } else {
         dim3 grid(N / PF_BN, (M + PF_BM - 1) / PF_BM);
         hipLaunchKernelGGL(w4a16_prefill_kernel<G>, grid, dim3(256), 0, st, A, wf, S, Y, M, N, K);

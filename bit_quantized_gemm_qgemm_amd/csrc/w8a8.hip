@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + 256 * i, row = idx >> 3, col = idx & 7;
             const int gm = m0 + row;
-            ra[i] = gm < M ? *reinterpret_cast<const uintx4*>(A + (size_t)gm * K + c * BK + col * 16)
-                           : uintx4{0, 0, 0, 0};
+            // rows >= M repeat row M-1 (unconditional load; those rows are not stored)
+            ra[i] = *reinterpret_cast<const uintx4*>(A + (size_t)(gm < M ? gm : M - 1) * K + c * BK + col * 16);
             rw[i] = *reinterpret_cast<const uintx4*>(W + (size_t)(n0 + row) * K + c * BK + col * 16);
         }
     };
