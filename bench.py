@@ -52,6 +52,12 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile", default=None,
+                    choices=["decode1", "decode4", "decode8", "prefill", "w8a8", "quant_act",
+                             "kvquant", "kvdequant", "moe", "copy"],
+                    help="launch one workload's kernels --launches times (eagerly) and exit; "
+                         "for rocprofv3 runs")
+    ap.add_argument("--launches", type=int, default=20)
     return ap.parse_args()
 
 
@@ -77,6 +83,10 @@ def main():
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.profile:
+        profile_one(args.profile, args.launches, qg, qi, np, torch, to_dev)
+        return
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -189,6 +199,80 @@ def main():
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
+
+
+def profile_one(name, launches, qg, qi, np, torch, to_dev):
+    """Eager launches of one workload, for counter collection.  Weight sets
+    rotate as in the timed runs so reads come from HBM."""
+    dev = torch.device("cuda:0")
+    if name.startswith("decode"):
+        M = int(name[len("decode"):])
+        sets = []
+        for r in range(ROT):
+            Wb, S = qi.w4a16_weights(DEC_K, DEC_N, DEC_G, 101 + 1000 * r)
+            sets.append((qg.qgemm_w4a16_prepack(to_dev(Wb), DEC_K, DEC_N), to_dev(S)))
+        A = to_dev(qi.activations(M, DEC_K, 1010 + M))
+        Y = torch.empty((M, DEC_N), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            Wf, S = sets[i % ROT]
+            qg.qgemm_w4a16(A, Wf, S, DEC_G, Y=Y)
+    elif name == "prefill":
+        M, K, N, G = 2048, 4096, 4096, 128
+        probs = []
+        for r in range(4):
+            A, Wb, S = qi.w4a16_problem(M, K, N, G, 102 + 1000 * r)
+            probs.append((to_dev(A), qg.qgemm_w4a16_prepack(to_dev(Wb), K, N), to_dev(S)))
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            p = probs[i % len(probs)]
+            qg.qgemm_w4a16(p[0], p[1], p[2], G, Y=Y)
+    elif name in ("w8a8", "quant_act"):
+        M = N = K = 4096
+        X, Wf16, bias, om = qi.w8a8_problem(M, N, K, 103)
+        Xd = to_dev(X)
+        qw, sw = qg.quant_sym_int8(to_dev(Wf16))
+        qa, sa = qg.quant_sym_int8(Xd)
+        biasd = to_dev(bias)
+        Yq = torch.empty((M, N), dtype=torch.int8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            if name == "w8a8":
+                qg.qgemm_w8a8_epilogue(qa, qw, sa, sw, biasd, float(om), 3, Y=Yq)
+            else:
+                qg.quant_sym_int8(Xd, Q=qa, scales=sa)
+    elif name in ("kvquant", "kvdequant"):
+        kvs = [to_dev(qi.kv_problem(32, 2048, 128, 103 + 1000 * r)) for r in range(16)]
+        Q = torch.empty((32, 2048, 128), dtype=torch.int8, device=dev)
+        Sk = torch.empty(32 * 2048, dtype=torch.float32, device=dev)
+        Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
+        qs = [qg.quant_sym_int8(kv) for kv in kvs]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            if name == "kvquant":
+                qg.quant_sym_int8(kvs[i % 16], Q=Q, scales=Sk)
+            else:
+                qg.dequant_sym_int8(qs[i % 16][0], qs[i % 16][1], X=Xo)
+    elif name == "moe":
+        T, H, I, E, topK, G = 256, 4096, 14336, 8, 2, 128
+        X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 104)
+        pg = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wg[e]), H, I) for e in range(E)])
+        pu = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wu[e]), H, I) for e in range(E)])
+        pd = torch.cat([qg.qgemm_w4a16_prepack(to_dev(Wd[e]), I, H) for e in range(E)])
+        args = [to_dev(a) for a in (X, logits)] + [pg, pu, pd] + [to_dev(a) for a in (Sg, Su, Sd)]
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            qg.moe_w4a16(*args, topK, G)
+    elif name == "copy":
+        # a plain copy of known size, to calibrate the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profiled {name} x{launches}", file=sys.stderr, flush=True)
 
 
 def read_traffic():

@@ -3,17 +3,22 @@
 //
 // Int4 Groupwise GEMM Plugin V2 page (class summary: inputs, output and the
 // fragment-layout weights; configurePlugin: the token count M steers the
-// kernel choice).  Two regimes, chosen by M:
-//   decode  (M <= 16): HBM-bound weight stream.  One workgroup per 16-column
-//       strip, four waves splitting K; every lane issues its 16-byte weight
-//       loads for the whole K slice up front, dequantizes in registers to
-//       exact fp16 integers, and v_mfma_f32_16x16x32_f16 forms per-group
-//       partial sums (rows >= M are zero) that are scaled in fp32.  The four
-//       K partials are added in LDS in a fixed order.
-//   prefill (M > 16): MFMA-bound.  128x128 output tiles, four waves of 64x64;
-//       A tiles double-buffered through LDS, B fragments straight from the
-//       fragment layout into registers, dequantized with the group scale
-//       folded in, v_mfma_f32_32x32x16_f16.
+// kernel choice).  Three kernels, chosen by M:
+//   decode  (M <= 16): HBM-bound weight stream.  Each wave owns NSW 16-column
+//       strips and KCW 128-k chunks; it issues every weight, A and scale load
+//       of its slice before its first wait, stages A and scales in its own
+//       LDS slice (no workgroup barrier before the main loop) and runs
+//       v_mfma_f32_16x16x32_f16 on the raw fp16 values 1024 + u; per-group
+//       fp32 partials are corrected and scaled, and the K partials of the
+//       workgroup's waves are added in LDS in a fixed order.
+//   prefill (16 < M <= 512): 128x128 output tiles, four waves of 64x64,
+//       A tiles double-buffered through LDS via registers, B fragments read
+//       straight from the fragment layout into registers and dequantized with
+//       the group scale folded in, v_mfma_f32_32x32x16_f16.
+//   large prefill (M > 512): 256x128 tiles, four waves of 128x64; A tiles go
+//       global -> LDS by direct DMA with an XOR swizzle, B as above.
+// Both prefill kernels map the 1-D workgroup index column-major over tiles so
+// that the workgroups resident on one XCD share weight columns in its L2.
 #include "common.hpp"
 #include "w4_tile.hpp"
 
@@ -188,7 +193,10 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][PF_BM * PF_LDA];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * PF_BM, n0 = blockIdx.x * PF_BN;
+    // tile (x, y) of workgroup id L: y = L % (row tiles), see the large kernel
+    const int mtiles = (M + PF_BM - 1) / PF_BM;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * PF_BM, n0 = (L / mtiles) * PF_BN;
     const int kchunks = K / 128;
     const int h = lane >> 5, c32 = lane & 31;
     const int ncol0 = n0 + wn * 64;
@@ -220,38 +228,45 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
         }
     };
 
-    BChunk<2, G> bcur, bnext;
-    load_a(0);
-    load_b_chunk<2, G>(bcur, wf, S, N, kchunks, 0, ncol0, lane);
-    store_a(0);
-    __syncthreads();
-
-    for (int c = 0; c < kchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < kchunks;
-        if (more) {
-            load_a(c + 1);
-            load_b_chunk<2, G>(bnext, wf, S, N, kchunks, c + 1, ncol0, lane);
-        }
-        const uint16_t* sa = sA[buf];
+    auto compute = [&](const uint16_t* sa, const BChunk<2, G>& b) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int kg = kgroup_of_step(s, h);
-            half8 a[2], b[2];
+            half8 a[2], bf[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 a[i] = *reinterpret_cast<const half8*>(&sa[(wm * 64 + i * 32 + c32) * PF_LDA + kg * 8]);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) b[t] = b_frag<2, G>(bcur, t, s);
+            for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G>(b, t, s);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t], acc[i][t]);
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
         }
-        if (more) {
-            store_a(buf ^ 1);
-            bcur = bnext;
-        }
+    };
+
+    // Two B register sets used alternately (no copies) and unconditional
+    // prefetches (the chunk index is clamped; a repeated last chunk is never
+    // consumed): a load under a branch, or a register copy of in-flight
+    // data, would make the compiler wait for the prefetch before computing.
+    BChunk<2, G> b0, b1;
+    load_a(0);
+    load_b_chunk<2, G>(b0, wf, S, N, kchunks, 0, ncol0, lane);
+    store_a(0);
+    __syncthreads();
+    for (int c = 0; c < kchunks; c += 2) {
+        const int c1 = c + 1 < kchunks ? c + 1 : c;
+        load_a(c1);
+        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c1, ncol0, lane);
+        compute(sA[0], b0);
+        store_a(1);
+        __syncthreads();
+        if (c + 1 >= kchunks) break;
+        const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
+        load_a(c2);
+        load_b_chunk<2, G>(b0, wf, S, N, kchunks, c2, ncol0, lane);
+        compute(sA[1], b1);
+        store_a(0);
         __syncthreads();
     }
 
@@ -268,6 +283,127 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
         }
 }
 
+// Large-M prefill: 256x128 output tiles, four waves of 128x64 (4 x 2
+// v_mfma_f32_32x32x16_f16 tiles, accumulators in the unified VGPR/AGPR file),
+// one workgroup per CU at M = 2048.  Taller wave tiles halve the dequant work
+// per MFMA (each B fragment feeds four MFMAs) while LDS traffic stays at one
+// 1 KB A fragment per two MFMAs.
+// A (64 KB per 128-k chunk) goes global -> LDS with global_load_lds_dwordx4:
+// no registers and no VALU.  A wave's DMA instruction fills 1 KB of LDS in lane
+// order (four 256-byte rows); the lane that fills position pos of row r
+// fetches piece pos ^ (r & 15) of that row, so the MFMA fragment reads, 16
+// rows at one k-group, hit 16 distinct 16-byte bank groups.  B: two register
+// sets used alternately, prefetched one chunk ahead.
+constexpr int PL_BM = 256, PL_BN = 128;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt with only the vector-memory counter constrained
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint16_t* __restrict__ A,
+                                                                      const uint8_t* __restrict__ wf,
+                                                                      const uint16_t* __restrict__ S,
+                                                                      uint16_t* __restrict__ Y, int M,
+                                                                      int N, int K) {
+    constexpr int SLAB = PL_BM * 128;  // halfs per LDS buffer (64 KB)
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * SLAB];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile (x, y) of
+    // id L has y = L % (row tiles), so with 8 row tiles the workgroups on one
+    // XCD share their A row tile in that XCD's L2 and stream distinct B tiles.
+    const int mtiles = (M + PL_BM - 1) / PL_BM;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * PL_BM, n0 = (L / mtiles) * PL_BN;
+    const int kchunks = K / 128;
+    const int h = lane >> 5, c32 = lane & 31;
+    const int ncol0 = n0 + wn * 64;
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
+
+    // This lane's DMA source for wave instruction j: row 4 * (16 * wave + j) + lane / 16,
+    // piece (lane % 16) ^ (row & 15).  Rows >= M repeat row M - 1 (never stored).
+    const int rsub = lane >> 4, pos = lane & 15;
+    auto dma_a = [&](int c, int buf) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = 4 * (16 * wave + j) + rsub;
+            const int gm = m0 + r < M ? m0 + r : M - 1;
+            const uint16_t* src = A + (size_t)gm * K + c * 128 + ((pos ^ (r & 15)) * 8);
+            __builtin_amdgcn_global_load_lds(src, sA + buf * SLAB + (16 * wave + j) * 512, 16, 0, 0);
+        }
+    };
+    auto compute = [&](const uint16_t* sa, const BChunk<2, G>& b) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int kg = kgroup_of_step(s, h);
+            half8 a[4], bf[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G>(b, t, s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * 128 + i * 32 + c32;
+                a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
+        }
+    };
+    // loads issued after a chunk's DMA: the B loads (2 per column tile) and scales
+    constexpr int BLOADS = 2 * (2 + BChunk<2, G>::NG);
+
+    BChunk<2, G> b0, b1;
+    dma_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b_chunk<2, G>(b0, wf, S, N, kchunks, 0, ncol0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<BLOADS>();
+    __syncthreads();
+    for (int c = 0; c < kchunks; c += 2) {
+        const int c1 = c + 1 < kchunks ? c + 1 : c;
+        dma_a(c1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c1, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA, b0);
+        wait_vmcnt<BLOADS>();  // chunk c1's A has landed in LDS
+        __syncthreads();
+        if (c + 1 >= kchunks) break;
+        const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
+        dma_a(c2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b_chunk<2, G>(b0, wf, S, N, kchunks, c2, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA + SLAB, b1);
+        wait_vmcnt<BLOADS>();
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = ncol0 + t * 32 + c32;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + wm * 128 + i * 32 + acc_row(j, lane);
+                if (row < M) Y[(size_t)row * N + col] = f2h(acc[i][t][j]);
+            }
+        }
+}
+
 template <int G>
 int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, uint16_t* Y, int M,
                      int N, int K, hipStream_t st) {
@@ -275,23 +411,27 @@ int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, ui
         // (MT, NSW, KCW): rows of the MFMA tile, 16-column strips per wave, 128-k
         // chunks per wave; the workgroup is 32 / KCW waves over NSW strips
         if (M == 1)
-            hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 8, G>), dim3(N / 16), dim3(256), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, G>), dim3(N / 16), dim3(512), 0, st,
                                A, wf, S, Y, M, N, K);
         else if (M == 2)
-            hipLaunchKernelGGL((w4a16_decode_kernel<2, 1, 8, G>), dim3(N / 16), dim3(256), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<2, 1, 4, G>), dim3(N / 16), dim3(512), 0, st,
                                A, wf, S, Y, M, N, K);
         else if (M <= 4)
-            hipLaunchKernelGGL((w4a16_decode_kernel<4, 2, 4, G>), dim3(N / 32), dim3(512), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<4, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
                                A, wf, S, Y, M, N, K);
         else if (M <= 8)
-            hipLaunchKernelGGL((w4a16_decode_kernel<8, 2, 4, G>), dim3(N / 32), dim3(512), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<8, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
                                A, wf, S, Y, M, N, K);
         else
             hipLaunchKernelGGL((w4a16_decode_kernel<16, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
                                A, wf, S, Y, M, N, K);
-    } else {
-        dim3 grid(N / PF_BN, (M + PF_BM - 1) / PF_BM);
+    } else if (M <= 512) {
+        dim3 grid((N / PF_BN) * ((M + PF_BM - 1) / PF_BM));
         hipLaunchKernelGGL(w4a16_prefill_kernel<G>, grid, dim3(256), 0, st, A, wf, S, Y, M, N, K);
+    } else {
+        dim3 grid((N / PL_BN) * ((M + PL_BM - 1) / PL_BM));
+        hipLaunchKernelGGL(w4a16_prefill_large_kernel<G>, grid, dim3(256), 0, st, A, wf, S, Y, M, N,
+                           K);
     }
     return qgh::launch_status();
 }
