@@ -164,7 +164,7 @@ def main():
     achieved = b1 / (per_m[1]["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<128> M=1",
+                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<MT=1,NSW=1,KCW=4,G=128> (M=1)",
                 "bytes_per_launch": b1}
 
     rows = {}
@@ -265,12 +265,13 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
         for _ in range(launches):
             qg.moe_w4a16(*args, topK, G)
     elif name == "copy":
-        # a plain copy of known size, to calibrate the HBM byte counters
+        # an elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB),
+        # to calibrate the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(launches):
-            dst.copy_(src)
+            torch.add(src, 1, out=dst)
     torch.cuda.synchronize()
     print(f"profiled {name} x{launches}", file=sys.stderr, flush=True)
 

@@ -71,6 +71,16 @@ __device__ __forceinline__ size_t frag_block_offset(int strip, int chunk, int kc
     return ((size_t)(strip >> 3) * kchunks + chunk) * 8192u + (size_t)(strip & 7) * 1024u;
 }
 
+// Workgroups of a 1-D grid are dispatched round-robin over the eight XCDs
+// (workgroup b runs on XCD b % 8).  xcd_contiguous(b, n) is a bijection of
+// [0, n) that hands each XCD one contiguous run of work items, so items that
+// share cache lines (neighbouring column strips reading one row of scales)
+// meet in the same L2.
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+    const int x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
 // ---------------------------------------------------------------- loads
 
 template <typename T>

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     WaveLds& L = lds[wave];
-    const int strip0 = blockIdx.x * NSW;
+    const int strip0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSW;
     const int cl = lane & 15, q = lane >> 4;
     const int kchunks = K / 128;
     const int arow = cl & (MT - 1);  // rows >= MT of the MFMA tile are never stored
