@@ -55,8 +55,8 @@ __device__ __forceinline__ half8 dequant8(uint32_t d) {
 }
 
 // Same, multiplied by a per-column scale (fp16 rounding of q*s).
-__device__ __forceinline__ half8 dequant8_scaled(uint32_t d, half2v s2) {
-    const half8 s8 = __builtin_shufflevector(s2, s2, 0, 1, 0, 1, 0, 1, 0, 1);
+__device__ __forceinline__ half8 dequant8_scaled(uint32_t d, _Float16 s) {
+    const half8 s8 = {s, s, s, s, s, s, s, s};
     return dequant8(d) * s8;
 }
 
@@ -82,6 +82,15 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n) {
 }
 
 // ---------------------------------------------------------------- loads
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt with only the vector-memory counter constrained).  Loads,
+// including global -> LDS DMA, complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) {

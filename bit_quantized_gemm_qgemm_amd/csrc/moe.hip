@@ -9,9 +9,10 @@
 //   3. gate/up: per expert, a W4A16 MFMA GEMM over that expert's gathered
 //               token rows with both the gate and the up matrix, fused with
 //               h = fp16(silu(g) * u);
-//   4. down:    per expert, W4A16 MFMA GEMM of h with the down matrix, fp32
-//               results per slot;
-//   5. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending.
+//   4. down:    per expert, W4A16 MFMA GEMM of h with the down matrix, K
+//               split over workgroups, fp32 partial results per slot;
+//   5. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending,
+//               o being the K-split partials added in split order.
 // Every reduction has a fixed order, so the layer is deterministic.
 #include "common.hpp"
 #include "w4_tile.hpp"
@@ -20,8 +21,6 @@ namespace {
 
 using namespace qg;
 
-constexpr int MBM = 64, MBN = 128, MLDA = 136;
-
 struct Work {
     int32_t* offsets;
     int32_t* pairs;
@@ -29,6 +28,15 @@ struct Work {
     uint16_t* h;
     float* o;
 };
+
+// K splits of the down projection: double until the workgroups cover the
+// chip about four times, keeping whole 128-k chunks per split.
+__host__ __device__ inline int down_splits(int H, int I, int E) {
+    const int tiles = E * (H / 128), kc = I / 128;
+    int ks = 1;
+    while (ks < 8 && tiles * ks < 1024 && kc % (2 * ks) == 0) ks *= 2;
+    return ks;
+}
 
 __host__ __device__ inline void workspace_layout(int T, int H, int I, int E, int topK, size_t* off) {
     const size_t P = (size_t)T * topK;
@@ -42,7 +50,7 @@ __host__ __device__ inline void workspace_layout(int T, int H, int I, int E, int
     off[3] = x;
     x = (x + sizeof(uint16_t) * P * I + 255) & ~(size_t)255;
     off[4] = x;
-    x = (x + sizeof(float) * P * H + 255) & ~(size_t)255;
+    x = (x + sizeof(float) * down_splits(H, I, E) * P * H + 255) & ~(size_t)255;
     off[5] = x;
 }
 
@@ -141,170 +149,197 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 
 // ------------------------------------------------------------------ grouped GEMMs
 
-// Shared main loop: 64 x 128 output tile of one expert; four waves of 32 x 64
-// (one 32-row MFMA tile, two 32-column tiles); NB = number of weight
-// matrices sharing the A rows (2 for gate/up, 1 for down).
-template <int G, int NB>
-struct GroupedTile {
-    floatx16 acc[NB][2];
-};
+// One kernel for both projections.  A workgroup owns one expert and one
+// 128-column tile of its weight matrices (NB = 2: gate and up, which share
+// the A rows; NB = 1: down) and runs every row of that expert through it, in
+// passes of up to 128 rows, so each weight byte is read from HBM once per
+// pass (one pass unless an expert holds more than 96 rows for gate/up, 128
+// for down: the gate/up pass keeps 2 x 3 accumulator tiles in registers).  Wave w owns
+// columns 32w .. 32w + 31 of the tile for all rows: it dequantizes its B
+// fragments once per k-step and feeds them to the NRB 32-row MFMA blocks.
+// A rows (gathered tokens for gate/up, contiguous h rows for down) go
+// global -> LDS by DMA, double-buffered, with the XOR swizzle of the prefill
+// kernel; B fragments are prefetched one 128-k chunk ahead in registers.
+// The down projection splits K over KS workgroups (fp32 partials, added in
+// split order by the combine) so that it has enough workgroups.
 
-template <int G, int NB, typename RowSrc>
-__device__ __forceinline__ void grouped_mainloop(GroupedTile<G, NB>& tile, uint16_t* sA,
-                                                 RowSrc row_src, const uint8_t* const* wf,
-                                                 const uint16_t* const* S, int N, int K,
-                                                 int ncol0) {
+constexpr int XP_SLAB = 128 * 128;  // halfs per LDS A buffer: 128 rows of 128 k (32 KB)
+
+// MODE 0: gate/up, h[slot][n] = fp16(silu(g) * u).  MODE 1: down, fp32
+// partial o[ks][slot][n].
+template <int G, int NB, int NRB, int MODE, typename RowOff>
+__device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowOff row_off, int R,
+                                            const uint8_t* const* wf, const uint16_t* const* S,
+                                            int N, int kchunks, int c0, int c1, int ncol0,
+                                            int slot0, void* out) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1;
     const int h = lane >> 5, c32 = lane & 31;
-    const int kchunks = K / 128;
+    floatx16 acc[NB][NRB];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < NRB; ++i)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) tile.acc[b][t][j] = 0.f;
+            for (int j = 0; j < 16; ++j) acc[b][i][j] = 0.f;
 
-    // A staging: 64 rows x 256 bytes = 1024 pieces, 4 per thread
-    // rows past the expert's last one repeat row 0 (unconditional loads; those
-    // accumulator rows are not stored)
-    const uint16_t* src[4];
+    // DMA: the workgroup's 8 NRB wave instructions each fill 1 KB of LDS =
+    // rows 4g .. 4g+3 (g = 2 NRB wave + j); lane l fetches piece
+    // (l % 16) ^ (row % 16) of row 4g + l / 16.  Rows >= R repeat row R - 1.
+    const int rsub = lane >> 4, pos = lane & 15;
+    uint32_t src[2 * NRB];  // element offsets from abase
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
-        const uint16_t* r = row_src(row);
-        src[i] = (r ? r : row_src(0)) + col * 8;
+    for (int j = 0; j < 2 * NRB; ++j) {
+        const int r = 4 * (2 * NRB * wave + j) + rsub;
+        src[j] = row_off(r < R ? r : R - 1) + ((pos ^ (r & 15)) * 8);
     }
-    uintx4 areg[4];
-    auto load_a = [&](int c) {
+    auto dma_a = [&](int c, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) areg[i] = *reinterpret_cast<const uintx4*>(src[i] + c * 128);
+        for (int j = 0; j < 2 * NRB; ++j)
+            __builtin_amdgcn_global_load_lds(abase + src[j] + c * 128,
+                                             sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, 16, 0, 0);
     };
-    auto store_a = [&](int buf) {
+    auto load_b = [&](BChunk<1, G>* bs, int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
-            *reinterpret_cast<uintx4*>(&sA[buf * MBM * MLDA + row * MLDA + col * 8]) = areg[i];
-        }
+        for (int b = 0; b < NB; ++b) load_b_chunk<1, G>(bs[b], wf[b], S[b], N, kchunks, c, ncol0, lane);
     };
-
-    BChunk<2, G> bcur[NB], bnext[NB];
-    load_a(0);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) load_b_chunk<2, G>(bcur[b], wf[b], S[b], N, kchunks, 0, ncol0, lane);
-    store_a(0);
-    __syncthreads();
-    for (int c = 0; c < kchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < kchunks;
-        if (more) {
-            load_a(c + 1);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                load_b_chunk<2, G>(bnext[b], wf[b], S[b], N, kchunks, c + 1, ncol0, lane);
-        }
-        const uint16_t* sa = sA + buf * MBM * MLDA;
+    auto compute = [&](const uint16_t* sa, const BChunk<1, G>* bs) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int kg = kgroup_of_step(s, h);
-            const half8 a = *reinterpret_cast<const half8*>(&sa[(wm * 32 + c32) * MLDA + kg * 8]);
+            half8 bf[NB], a[NRB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G>(bs[b], 0, s);
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    tile.acc[b][t] = mfma32(a, b_frag<2, G>(bcur[b], t, s), tile.acc[b][t]);
+            for (int i = 0; i < NRB; ++i) {
+                const int r = i * 32 + c32;
+                a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
+            }
+#pragma unroll
+            for (int i = 0; i < NRB; ++i)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b][i] = mfma32(a[i], bf[b], acc[b][i]);
+            // keep each step's operands short-lived: in issue order the next
+            // step's dequant still runs while these MFMAs execute
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
-            store_a(buf ^ 1);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) bcur[b] = bnext[b];
-        }
+    };
+    // loads issued after a chunk's DMA: per matrix two B pieces and NG scales
+    constexpr int BLOADS = NB * (2 + BChunk<1, G>::NG);
+
+    // Two chunks per trip, no branch inside the trip: a load placed before a
+    // branch but used only after it may be sunk past it by the compiler,
+    // which then waits for every outstanding load (the prefetch is lost).
+    // The last trip reloads its second chunk when the count is even; an odd
+    // count leaves one chunk, already staged, for the tail.
+    BChunk<1, G> b0[NB], b1[NB];
+    dma_a(c0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(b0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<BLOADS>();
+    __syncthreads();
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
+        dma_a(c + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(b1, c + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA, b0);
+        wait_vmcnt<BLOADS>();  // chunk c + 1's A has landed in LDS
+        __syncthreads();
+        const int cm = c + 2 < c1 ? c + 2 : c + 1;
+        dma_a(cm, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(b0, cm);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA + XP_SLAB, b1);
+        wait_vmcnt<BLOADS>();
         __syncthreads();
     }
-}
+    if (c < c1) compute(sA, b0);
 
-template <int G>
-__global__ __launch_bounds__(256, 2) void moe_gateup_kernel(
-    const uint16_t* __restrict__ X, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
-    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su, Work wk, int T, int H, int I,
-    int topK, int mtiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * MBM * MLDA];
-    const int e = blockIdx.y / mtiles, mt = blockIdx.y % mtiles;
-    const int off = wk.offsets[e], me = wk.offsets[e + 1] - off;
-    const int r0 = mt * MBM;
-    if (r0 >= me) return;
-    const int rows = me - r0 < MBM ? me - r0 : MBM;
-    const int slot0 = off + r0;
-    auto row_src = [&](int row) -> const uint16_t* {
-        if (row >= rows) return nullptr;
-        const int token = wk.pairs[slot0 + row] / topK;
-        return X + (size_t)token * H;
-    };
-    const size_t wbytes = (size_t)H * I / 2;
-    const size_t sn = (size_t)(H / G) * I;
-    const uint8_t* wf[2] = {wg + e * wbytes, wu + e * wbytes};
-    const uint16_t* S[2] = {sg + e * sn, su + e * sn};
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ncol0 = blockIdx.x * MBN + (wave & 1) * 64;
-    GroupedTile<G, 2> tile;
-    grouped_mainloop<G, 2>(tile, sA, row_src, wf, S, I, H, ncol0);
-    const int wm = wave >> 1;
+    const int col = ncol0 + c32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int col = ncol0 + t * 32 + (lane & 31);
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int row = wm * 32 + acc_row(j, lane);
-            if (row < rows) {
-                const float g = tile.acc[0][t][j], u = tile.acc[1][t][j];
-                const float silu = g / (1.0f + expf(-g));
-                wk.h[(size_t)(slot0 + row) * I + col] = f2h(silu * u);
+            const int row = i * 32 + acc_row(j, lane);
+            if (row < R) {
+                const size_t o = (size_t)(slot0 + row) * N + col;
+                if constexpr (MODE == 0) {
+                    const float g = acc[0][i][j], u = acc[NB - 1][i][j];
+                    const float silu = g / (1.0f + expf(-g));
+                    static_cast<uint16_t*>(out)[o] = f2h(silu * u);
+                } else {
+                    static_cast<float*>(out)[o] = acc[0][i][j];
+                }
             }
         }
-    }
 }
 
-template <int G>
-__global__ __launch_bounds__(256, 2) void moe_down_kernel(const uint8_t* __restrict__ wd,
-                                                          const uint16_t* __restrict__ sd, Work wk,
-                                                          int H, int I, int mtiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * MBM * MLDA];
-    const int e = blockIdx.y / mtiles, mt = blockIdx.y % mtiles;
+// Workgroup L: expert L % E, then column tile, then K split.
+template <int G, int MODE>
+__global__ __launch_bounds__(256, 2) void moe_expert_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
+    const uint16_t* __restrict__ s0, const uint16_t* __restrict__ s1, Work wk, int T, int H, int I,
+    int E, int topK, int splits) {
+    constexpr int NB = MODE == 0 ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * XP_SLAB];
+    const int L = blockIdx.x;
+    const int e = L % E, rest = L / E;
+    const int N = MODE == 0 ? I : H, K = MODE == 0 ? H : I;
+    const int ntiles = N / 128;
+    const int ct = rest % ntiles, ks = rest / ntiles;
     const int off = wk.offsets[e], me = wk.offsets[e + 1] - off;
-    const int r0 = mt * MBM;
-    if (r0 >= me) return;
-    const int rows = me - r0 < MBM ? me - r0 : MBM;
-    const int slot0 = off + r0;
-    const uint16_t* hb = wk.h;
-    auto row_src = [&](int row) -> const uint16_t* {
-        return row < rows ? hb + (size_t)(slot0 + row) * I : nullptr;
-    };
-    const uint8_t* wf[1] = {wd + e * ((size_t)I * H / 2)};
-    const uint16_t* S[1] = {sd + e * ((size_t)(I / G) * H)};
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ncol0 = blockIdx.x * MBN + (wave & 1) * 64;
-    GroupedTile<G, 1> tile;
-    grouped_mainloop<G, 1>(tile, sA, row_src, wf, S, H, I, ncol0);
-    const int wm = wave >> 1;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int col = ncol0 + t * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int row = wm * 32 + acc_row(j, lane);
-            if (row < rows) wk.o[(size_t)(slot0 + row) * H + col] = tile.acc[0][t][j];
+    if (me == 0) return;
+    const int kchunks = K / 128, per = kchunks / splits;
+    const int c0 = ks * per, c1 = c0 + per;
+    const size_t wbytes = (size_t)K * N / 2, sn = (size_t)(K / G) * N;
+    const uint8_t* wf[NB];
+    const uint16_t* S[NB];
+    wf[0] = w0 + e * wbytes;
+    S[0] = s0 + e * sn;
+    if constexpr (NB == 2) {
+        wf[1] = w1 + e * wbytes;
+        S[1] = s1 + e * sn;
+    }
+    const int ncol0 = ct * 128 + (threadIdx.x >> 6) * 32;
+    void* out = MODE == 0 ? static_cast<void*>(wk.h)
+                          : static_cast<void*>(wk.o + (size_t)ks * T * topK * H);
+    constexpr int PASS = MODE == 0 ? 96 : 128;  // rows per pass
+    const uint16_t* abase = MODE == 0 ? X : wk.h;
+    for (int r0 = 0; r0 < me; r0 += PASS) {
+        const int R = me - r0 < PASS ? me - r0 : PASS;
+        const int slot0 = off + r0;
+        // element offset of A row r of this pass (rows < 2^31 / H elements)
+        auto row_off = [&](int r) -> uint32_t {
+            if constexpr (MODE == 0) return (uint32_t)(wk.pairs[slot0 + r] / topK) * (uint32_t)H;
+            else return (uint32_t)(slot0 + r) * (uint32_t)I;
+        };
+        switch ((R + 31) / 32) {
+            case 1: expert_pass<G, NB, 1, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 2: expert_pass<G, NB, 2, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 3: expert_pass<G, NB, 3, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            default:
+                if constexpr (PASS == 128)
+                    expert_pass<G, NB, 4, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out);
+                break;
         }
+        __syncthreads();  // the next pass refills both LDS buffers
     }
 }
 
 // ------------------------------------------------------------------ combine
 
+// y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending; o = the K-split
+// partials added in split order.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ w, Work wk,
                                                           uint16_t* __restrict__ Y, int T, int H,
-                                                          int topK) {
+                                                          int topK, int splits) {
     const int per_row = H / 8;
     const size_t total = (size_t)T * per_row;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t split_stride = (size_t)T * topK * H;
     for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
         const int t = (int)(c / per_row), c8 = (int)(c % per_row);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -312,8 +347,12 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
             const int p = t * topK + j;
             const float wj = w[p];
             const float* o = wk.o + (size_t)wk.slot_of[p] * H + c8 * 8;
-            const floatx4 lo = *reinterpret_cast<const floatx4*>(o);
-            const floatx4 hi = *reinterpret_cast<const floatx4*>(o + 4);
+            floatx4 lo = *reinterpret_cast<const floatx4*>(o);
+            floatx4 hi = *reinterpret_cast<const floatx4*>(o + 4);
+            for (int k = 1; k < splits; ++k) {
+                lo += *reinterpret_cast<const floatx4*>(o + k * split_stride);
+                hi += *reinterpret_cast<const floatx4*>(o + k * split_stride + 4);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[i] = __builtin_fmaf(wj, lo[i], acc[i]);
@@ -338,15 +377,15 @@ int32_t launch_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* wg,
                        E, topK);
     hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(1024), 0, st, ids, P, E, wk.offsets,
                        wk.pairs, wk.slot_of);
-    const int mtiles = (T + MBM - 1) / MBM;  // an expert sees each token at most once
-    hipLaunchKernelGGL(moe_gateup_kernel<G>, dim3(I / MBN, E * mtiles), dim3(256), 0, st, X, wg, wu,
-                       sg, su, wk, T, H, I, topK, mtiles);
-    hipLaunchKernelGGL(moe_down_kernel<G>, dim3(H / MBN, E * mtiles), dim3(256), 0, st, wd, sd, wk,
-                       H, I, mtiles);
+    const int splits = down_splits(H, I, E);
+    hipLaunchKernelGGL((moe_expert_kernel<G, 0>), dim3(E * (I / 128)), dim3(256), 0, st, X, wg, wu,
+                       sg, su, wk, T, H, I, E, topK, 1);
+    hipLaunchKernelGGL((moe_expert_kernel<G, 1>), dim3(E * (H / 128) * splits), dim3(256), 0, st, X,
+                       wd, wd, sd, sd, wk, T, H, I, E, topK, splits);
     const size_t chunks = (size_t)T * H / 8;
     const size_t want = (chunks + 255) / 256;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
-                       w, wk, Y, T, H, topK);
+                       w, wk, Y, T, H, topK, splits);
     return qgh::launch_status();
 }
 
@@ -373,7 +412,8 @@ extern "C" int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const ui
         !Y || !topk_ids || !topk_w || !workspace)
         return QGEMM_NULL_PTR;
     if (activation != 0 || E > 64 || H == 0 || I == 0 || H % 128 != 0 || I % 128 != 0 ||
-        (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30)
+        (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30 ||
+        (size_t)T * H >= (size_t)1 << 32 || (size_t)T * topK * I >= (size_t)1 << 32)
         return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(X, 16) || !qgh::aligned(logits, 2) || !qgh::aligned(w_gate_frag, 16) ||
         !qgh::aligned(w_up_frag, 16) || !qgh::aligned(w_down_frag, 16) || !qgh::aligned(s_gate, 4) ||

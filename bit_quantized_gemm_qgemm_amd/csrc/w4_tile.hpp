@@ -26,11 +26,13 @@ __device__ __forceinline__ int group_of_step(int s) {
 }
 
 // Raw B data of WTN 32-column MFMA tiles for one 128-k chunk, plus scales.
+// Scales stay scalar until use: nothing consumes a load right after it is
+// issued, so the loads of a prefetched chunk are never waited for early.
 template <int WTN, int G>
 struct BChunk {
     static constexpr int NG = 128 / G;
     uintx4 raw[WTN][2];
-    half2v sc[WTN][NG];
+    uint32_t sc[WTN][NG];  // fp16 bits, zero-extended (one register each)
 };
 
 // Fetch the chunk c of columns ncol0 .. ncol0 + 32*WTN - 1 (ncol0 % 32 == 0).
@@ -48,9 +50,7 @@ __device__ __forceinline__ void load_b_chunk(BChunk<WTN, G>& b, const uint8_t* _
         b.raw[t][1] = ldg_nt(reinterpret_cast<const uintx4*>(blk + (cl + 16 * (h + 2)) * 16));
 #pragma unroll
         for (int g = 0; g < BChunk<WTN, G>::NG; ++g) {
-            const uint16_t sb = S[(size_t)(c * BChunk<WTN, G>::NG + g) * N + n];
-            const _Float16 sh = __builtin_bit_cast(_Float16, sb);
-            b.sc[t][g] = half2v{sh, sh};
+            b.sc[t][g] = S[(size_t)(c * BChunk<WTN, G>::NG + g) * N + n];
         }
     }
 }
@@ -60,7 +60,7 @@ __device__ __forceinline__ half8 b_frag(const BChunk<WTN, G>& b, int t, int s) {
     const uintx4 r = b.raw[t][s >> 2];
     const int kk = s & 3;
     const uint32_t d = kk == 0 ? r.x : kk == 1 ? r.y : kk == 2 ? r.z : r.w;
-    return dequant8_scaled(d, b.sc[t][group_of_step<G>(s)]);
+    return dequant8_scaled(d, __builtin_bit_cast(_Float16, (uint16_t)b.sc[t][group_of_step<G>(s)]));
 }
 
 __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {

@@ -245,30 +245,37 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
         }
     };
 
-    // Two B register sets used alternately (no copies) and unconditional
-    // prefetches (the chunk index is clamped; a repeated last chunk is never
-    // consumed): a load under a branch, or a register copy of in-flight
-    // data, would make the compiler wait for the prefetch before computing.
+    // Two B register sets used alternately (no copies), two chunks per trip
+    // and no branch inside a trip: a load under a branch, a load issued
+    // before a branch but used only after it, or a register copy of in-flight
+    // data makes the compiler wait for the prefetch before computing.  The
+    // scheduling barriers keep the prefetch loads ahead of the compute.  The
+    // last trip reloads its second chunk when the count is even; an odd count
+    // leaves one staged chunk for the tail.
     BChunk<2, G> b0, b1;
     load_a(0);
     load_b_chunk<2, G>(b0, wf, S, N, kchunks, 0, ncol0, lane);
     store_a(0);
     __syncthreads();
-    for (int c = 0; c < kchunks; c += 2) {
-        const int c1 = c + 1 < kchunks ? c + 1 : c;
-        load_a(c1);
-        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c1, ncol0, lane);
+    int c = 0;
+    for (; c + 1 < kchunks; c += 2) {
+        load_a(c + 1);
+        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c + 1, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
         compute(sA[0], b0);
+        __builtin_amdgcn_sched_barrier(0);
         store_a(1);
         __syncthreads();
-        if (c + 1 >= kchunks) break;
         const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
         load_a(c2);
         load_b_chunk<2, G>(b0, wf, S, N, kchunks, c2, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
         compute(sA[1], b1);
+        __builtin_amdgcn_sched_barrier(0);
         store_a(0);
         __syncthreads();
     }
+    if (c < kchunks) compute(sA[0], b0);
 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -295,13 +302,6 @@ __global__ __launch_bounds__(256, 2) void w4a16_prefill_kernel(const uint16_t* _
 // rows at one k-group, hit 16 distinct 16-byte bank groups.  B: two register
 // sets used alternately, prefetched one chunk ahead.
 constexpr int PL_BM = 256, PL_BN = 128;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    // s_waitcnt with only the vector-memory counter constrained
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int G>
 __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint16_t* __restrict__ A,
@@ -364,6 +364,11 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
     // loads issued after a chunk's DMA: the B loads (2 per column tile) and scales
     constexpr int BLOADS = 2 * (2 + BChunk<2, G>::NG);
 
+    // Two chunks per trip and no branch inside a trip: a load issued before a
+    // branch but used only after it may be sunk past the branch, after which
+    // the compiler waits for every outstanding load and the prefetch is lost.
+    // The last trip reloads its second chunk when the count is even; an odd
+    // count leaves one staged chunk for the tail.
     BChunk<2, G> b0, b1;
     dma_a(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -371,16 +376,15 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<BLOADS>();
     __syncthreads();
-    for (int c = 0; c < kchunks; c += 2) {
-        const int c1 = c + 1 < kchunks ? c + 1 : c;
-        dma_a(c1, 1);
+    int c = 0;
+    for (; c + 1 < kchunks; c += 2) {
+        dma_a(c + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c1, ncol0, lane);
+        load_b_chunk<2, G>(b1, wf, S, N, kchunks, c + 1, ncol0, lane);
         __builtin_amdgcn_sched_barrier(0);
         compute(sA, b0);
-        wait_vmcnt<BLOADS>();  // chunk c1's A has landed in LDS
+        wait_vmcnt<BLOADS>();  // chunk c + 1's A has landed in LDS
         __syncthreads();
-        if (c + 1 >= kchunks) break;
         const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
         dma_a(c2, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -390,6 +394,7 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
         wait_vmcnt<BLOADS>();
         __syncthreads();
     }
+    if (c < kchunks) compute(sA, b0);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)

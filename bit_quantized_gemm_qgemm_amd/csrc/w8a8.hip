@@ -97,13 +97,7 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
         }
     };
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int c = 0; c < kchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < kchunks;
-        if (more) load(c + 1);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             // step s covers k = 32 s .. 32 s + 31; lane half h holds 16 of them
@@ -120,7 +114,23 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
 #pragma unroll
                 for (int t = 0; t < 2; ++t) acc[i][t] = mfma_i8(a[i], b[t], acc[i][t]);
         }
-        if (more) store(buf ^ 1);
+    };
+
+    // Prefetch of the next chunk into registers, unconditional (the index is
+    // clamped) and kept ahead of the compute by scheduling barriers: a load
+    // under a branch makes the compiler wait for it at the join, and a load
+    // sunk next to its LDS store would not overlap the MFMAs.  The last
+    // iteration refills the idle buffer with a chunk nobody reads.
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < kchunks; ++c) {
+        const int buf = c & 1;
+        load(c + 1 < kchunks ? c + 1 : c);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf);
+        __builtin_amdgcn_sched_barrier(0);
+        store(buf ^ 1);
         __syncthreads();
     }
 

@@ -186,7 +186,10 @@ QGEMM_API int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const fl
      int32 pairs[T*topK]     pair ids p = t*topK + j sorted by expert, then p
      int32 slot_of[T*topK]   inverse of pairs
      fp16  h[T*topK][I]      intermediate activations, sorted order
-     fp32  o[T*topK][H]      expert outputs, sorted order
+     fp32  o[S][T*topK][H]   partial expert outputs, sorted order, one slice
+                             per split of the down projection's K; S starts
+                             at 1 and doubles while S < 8, E*(H/128)*S < 1024
+                             and (I/128) % (2*S) == 0
    The first two parts are part of the documented result (tests read them). */
 QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK);
 
@@ -199,7 +202,8 @@ QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int3
    Y: fp16 [T][H] (output); topk_ids: int32 [T][topK] (output);
    topk_w: fp32 [T][topK] (output).
    Supported: H % 128 == 0, I % 128 == 0, G in {32, 64, 128}, 1 <= topK <= E
-   <= 64, activation == 0.  T == 0 is a successful no-op. */
+   <= 64, activation == 0, T*H < 2^32 and T*topK*I < 2^32.  T == 0 is a
+   successful no-op. */
 QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
                   const uint8_t* w_up_frag, const uint8_t* w_down_frag, const uint16_t* s_gate,
                   const uint16_t* s_up, const uint16_t* s_down, uint16_t* Y, int32_t* topk_ids,
