@@ -92,6 +92,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until this wave's LDS (and scalar memory) operations are done.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) {
     return __builtin_nontemporal_load(p);

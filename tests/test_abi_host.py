@@ -62,7 +62,12 @@ def test_size_queries(L):
     assert L.qgemm_w4a16_workspace_bytes(1, 11008, 4096, 128) == 0
     ws = L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2)
     P_ = 512
-    need = 256 + 2 * 2048 + 2 * P_ * 14336 + 4 * P_ * 4096
+    # down-projection K splits, by the rule the header states
+    splits, E, H, I = 1, 8, 4096, 14336
+    while splits < 8 and E * (H // 128) * splits < 1024 and (I // 128) % (2 * splits) == 0:
+        splits *= 2
+    assert splits == 4
+    need = 256 + 2 * 2048 + 2 * P_ * I + 4 * splits * P_ * H
     assert need <= ws <= need + 5 * 256
 
 
