@@ -154,6 +154,141 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
     }
 }
 
+// Large shapes (M >= 256, N % 256 == 0): 256x256 output tiles, eight waves
+// (two per SIMD) of 128x64 (4 x 2 v_mfma_i32_32x32x32_i8 tiles, 128
+// accumulators per lane); one workgroup per CU at M = N = 4096.  Per 128-k
+// chunk a workgroup stages 32 KB of A and 32 KB of W by global -> LDS DMA
+// (two buffers each, one array, compile-time offsets), so each operand byte
+// fetched feeds 256 output columns or rows (a 128x128 tile fetches twice as
+// much per MFMA).  A DMA instruction fills 1 KB = 8 rows of 128 bytes in lane
+// order; the lane that fills position pos of row r fetches piece
+// pos ^ ((r >> 1) & 7), so the MFMA operand reads (32 rows at one 16-byte
+// piece) are free of bank conflicts.  The k-steps are software-pipelined:
+// the operand reads of step s + 1 are interleaved with the MFMAs of step s.
+constexpr int LB = 256;
+
+__global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ W, const float* __restrict__ sa,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, float out_mult, uint32_t flags,
+    int8_t* __restrict__ Y, int32_t* __restrict__ acc_out, int M, int N, int K) {
+    constexpr int SL = LB * 128;  // bytes per operand buffer
+    __shared__ __attribute__((aligned(1024))) int8_t lds[4 * SL];  // A0, A1, W0, W1
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    // tile (x, y) of workgroup L: y = L % (row tiles), so workgroups on one
+    // XCD (dealt round-robin by id) share their A row tiles in its L2
+    const int mtiles = (M + LB - 1) / LB;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * LB, n0 = (L / mtiles) * LB;
+    const int kchunks = K / 128, last = kchunks - 1;
+    const int h = lane >> 5, c32 = lane & 31;
+
+    intx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0;
+
+    // wave w issues DMA instructions 4w .. 4w + 3 of each operand tile; rows
+    // past the last valid one repeat it (their results are never stored).
+    // Sources are 32-bit byte offsets from a wave-uniform base (rows * K <
+    // 2^32 is checked at launch).
+    const int rsub = lane >> 3, pos = lane & 7;
+    uint32_t offa[4], offw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (4 * wave + j) + rsub;
+        const uint32_t piece = (uint32_t)((pos ^ ((r >> 1) & 7)) * 16);
+        offa[j] = (uint32_t)(m0 + r < M ? m0 + r : M - 1) * (uint32_t)K + piece;
+        offw[j] = (uint32_t)(n0 + r) * (uint32_t)K + piece;
+    }
+    auto dma = [&](const int8_t* base, const uint32_t (&off)[4], int8_t* dst) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(base + off[j], dst + (4 * wave + j) * 1024, 16, 0, 0);
+    };
+    auto operands = [&](const int8_t* ab, const int8_t* wb, int s, intx4 (&a)[4], intx4 (&b)[2]) {
+        const int p = 2 * s + h;  // 16-byte piece of k = 32 s + 16 h .. + 15
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + c32;
+            a[i] = *reinterpret_cast<const intx4*>(ab + r * 128 + ((p ^ ((r >> 1) & 7)) * 16));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int r = wn * 64 + t * 32 + c32;
+            b[t] = *reinterpret_cast<const intx4*>(wb + r * 128 + ((p ^ ((r >> 1) & 7)) * 16));
+        }
+    };
+    auto compute = [&](const int8_t* ab, const int8_t* wb) {
+        intx4 a[4], b[2];
+        operands(ab, wb, 0, a, b);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            intx4 an[4], bn[2];
+            if (s < 3) operands(ab, wb, s + 1, an, bn);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma_i8(a[i], b[t], acc[i][t]);
+            if (s < 3) {
+#pragma unroll
+                for (int q = 0; q < 6; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = an[i];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) b[t] = bn[t];
+        }
+    };
+
+    dma(A, offa, lds);
+    dma(W, offw, lds + 2 * SL);
+    wait_vmcnt<0>();
+    __syncthreads();
+    // one trip per chunk: DMA of chunk c + 1 into the idle buffers, MFMAs on
+    // chunk c, then wait for this wave's DMA and a bare barrier (buffer
+    // indices are literals at every call so that the compiler can tell the
+    // DMA targets from the buffers being read)
+    auto trip = [&](int c, int buf) __attribute__((always_inline)) {
+        const int cn = c + 1 < last ? c + 1 : last;
+        dma(A + cn * 128, offa, lds + (buf ^ 1) * SL);
+        dma(W + cn * 128, offw, lds + (2 + (buf ^ 1)) * SL);
+        compute(lds + buf * SL, lds + (2 + buf) * SL);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int c = 0; c < kchunks; c += 2) {
+        trip(c, 0);
+        if (c + 1 < kchunks) trip(c + 1, 1);
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int col = n0 + wn * 64 + t * 32 + c32;
+        const float swv = sw[col];
+        const float bv = (flags & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + wm * 128 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+                if (row < M) {
+                    const int32_t a = acc[i][t][j];
+                    if (acc_out) acc_out[(size_t)row * N + col] = a;
+                    Y[(size_t)row * N + col] = requant(a, sa[row], swv, bv, out_mult, flags);
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const float* a_scale,
@@ -170,8 +305,14 @@ extern "C" int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const f
         !qgh::aligned(a_scale, 4) || !qgh::aligned(w_scale, 4) || (bias && !qgh::aligned(bias, 2)) ||
         (acc_out && !qgh::aligned(acc_out, 16)))
         return QGEMM_MISALIGNED;
-    dim3 grid(N / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL(w8a8_kernel, grid, dim3(256), 0, (hipStream_t)stream, A, W, a_scale, w_scale,
-                       bias, out_mult, flags, Y, acc_out, (int)M, (int)N, (int)K);
+    if (M >= LB && N % LB == 0 && (size_t)M * K < ((size_t)1 << 32) && (size_t)N * K < ((size_t)1 << 32)) {
+        dim3 grid((N / LB) * ((M + LB - 1) / LB));
+        hipLaunchKernelGGL(w8a8_large_kernel, grid, dim3(512), 0, (hipStream_t)stream, A, W, a_scale,
+                           w_scale, bias, out_mult, flags, Y, acc_out, (int)M, (int)N, (int)K);
+    } else {
+        dim3 grid(N / BN, (M + BM - 1) / BM);
+        hipLaunchKernelGGL(w8a8_kernel, grid, dim3(256), 0, (hipStream_t)stream, A, W, a_scale,
+                           w_scale, bias, out_mult, flags, Y, acc_out, (int)M, (int)N, (int)K);
+    }
     return qgh::launch_status();
 }
