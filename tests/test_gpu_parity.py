@@ -115,6 +115,16 @@ def test_w4a16_prefill_small(qg, M, G):
     assert_fp16_close(run_w4a16(qg, A, Wb, S, G), oracle.w4a16(A, Wb, S, G), f"M={M} G={G}")
 
 
+# M > 512 takes the 128x256 DMA kernel when N % 256 == 0: ragged M, every
+# group size, one chunk and a count that leaves a partial six-trip pass;
+# N = 384 checks that such M falls back to the 128x128 kernel
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M,K,N", [(513, 128, 256), (640, 896, 512), (1100, 384, 256), (600, 256, 384)])
+def test_w4a16_prefill_large(qg, M, K, N, G):
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 450 + M + K + G)
+    assert_fp16_close(run_w4a16(qg, A, Wb, S, G), oracle.w4a16(A, Wb, S, G), f"M={M} K={K} N={N} G={G}")
+
+
 def test_w4a16_prefill_cfg2_sampled(qg):
     M, K, N, G = 2048, 4096, 4096, 128
     A, Wb, S = qi.w4a16_problem(M, K, N, G, 102)
@@ -196,6 +206,21 @@ def test_w8a8_small(qg, M, N, K, flags):
     assert np.array_equal(host(Y), Yr)
 
 
+# M >= 256 with N % 256 == 0 takes the 256x256 DMA kernel: ragged M, one and
+# three 128-k chunks; every output compared (int32 and int8 bit-exact)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 512, 384), (517, 256, 256)])
+def test_w8a8_large(qg, M, N, K):
+    X, Wf, bias, om = qi.w8a8_problem(M, N, K, 750 + M + N + K)
+    qa, sa = oracle.quant_sym_int8(X)
+    qw, sw = oracle.quant_sym_int8(Wf)
+    om = np.float32(om * 2)
+    Yr, accr = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, om, 3, want_acc=True)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    Y = qg.qgemm_w8a8_epilogue(dev(qa), dev(qw), dev(sa), dev(sw), dev(bias), om, 3, acc_out=acc)
+    assert np.array_equal(host(acc), accr)
+    assert np.array_equal(host(Y), Yr)
+
+
 def test_w8a8_cfg3_sampled(qg):
     M = N = K = 4096
     X, Wf, bias, om = qi.w8a8_problem(M, N, K, 103)
@@ -235,8 +260,11 @@ def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G):
     return host(Y), host(ids), host(w), off, pairs
 
 
+# the last case routes all 300 tokens to both experts: several row passes in
+# both projections (96 rows per gate/up pass, 128 per down pass)
 @pytest.mark.parametrize("T,H,I,E,topK,G", [(37, 256, 384, 4, 2, 128), (70, 256, 256, 8, 2, 64),
-                                             (5, 128, 256, 3, 3, 32), (130, 128, 128, 2, 1, 128)])
+                                             (5, 128, 256, 3, 3, 32), (130, 128, 128, 2, 1, 128),
+                                             (300, 128, 256, 2, 2, 128)])
 def test_moe_small(qg, T, H, I, E, topK, G):
     X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 800 + T)
     logits[3] = logits[3, 0]  # an all-tie row: lower expert index wins
