@@ -65,17 +65,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     const bool live = row < rows;
     const int nchunk = cols / 8;
     const uint16_t* x = X + (size_t)(live ? row : 0) * cols;
+    // Every load is unconditional (a chunk past the row end reads chunk 0 and
+    // is then zeroed): a load under a branch makes the compiler wait for all
+    // outstanding loads at the join, serializing the lane's loads.
     uintx4 v[CPL];
-    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        if (live && c < nchunk) {
-            v[i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + c);
-            amax = fmaxf(amax, absmax8(v[i]));
-        } else {
-            v[i] = uintx4{0, 0, 0, 0};
-        }
+        v[i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + (c < nchunk ? c : 0));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
+        amax = fmaxf(amax, absmax8(v[i]));
     }
     amax = group_max<LPR>(amax);
     if (!live) return;
