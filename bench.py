@@ -6,8 +6,9 @@ K=4096, N=11008, G=128 (a 7B-class MLP up-projection), fp16 activations with
 M = 1, 4 and 8.  One step = one launch at each M.  Every launch reads a
 different one of 16 weight sets (16 x 23.2 MB > the 256 MB Infinity Cache),
 so the weights stream from HBM.  Steps are recorded once as HIP graphs (the
-library's launches on torch's current stream are captured) and replayed, so
-host launch overhead does not pace the GPU.
+library's launches on torch's current stream are captured) and replayed,
+16 consecutive steps per graph, so host and graph launch overhead does not
+pace the GPU (as in a decode loop).
 
 value      = algorithmic bytes of a step / time of a step (GB/s, HBM-bound)
 roofline   = the M=1 decode kernel: algorithmic bytes per launch / its mean
@@ -127,22 +128,31 @@ def main():
         Wf, S = sets[r % ROT]
         return lambda: qg.qgemm_w4a16(acts[M][r % ROT], Wf, S, DEC_G, Y=outs[M])
 
-    # one graph per rotation offset; step k replays graph k % ROT
+    # Step k runs M = 1, 4, 8 on weight sets 3k, 3k+1, 3k+2 (mod ROT).  Steps
+    # are replayed from HIP graphs: one graph holds ROT consecutive steps (all
+    # rotation offsets, 3 * ROT launches) so that graph-launch overhead is
+    # shared as in a decode loop; a remainder of steps uses one-step graphs.
     step_graphs = []
     for k in range(ROT):
         fns = [decode_launch(M, 3 * k + i) for i, M in enumerate(DEC_MS)]
         step_graphs.append(graph_of(fns))
+    block_graph = graph_of([decode_launch(M, 3 * k + i) for k in range(ROT)
+                            for i, M in enumerate(DEC_MS)])
     step_bytes = sum(w4a16_bytes(M, DEC_N, DEC_K, DEC_G) for M in DEC_MS)
     step_flops = sum(2 * M * DEC_N * DEC_K for M in DEC_MS)
 
-    for k in range(args.warmup):
-        step_graphs[k % ROT].replay()
+    def run_steps(n):
+        for _ in range(n // ROT):
+            block_graph.replay()
+        for k in range(n % ROT):
+            step_graphs[k].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for k in range(args.steps):
-        step_graphs[k % ROT].replay()
+    run_steps(args.steps)
     e1.record()
     torch.cuda.synchronize()
     step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
@@ -191,7 +201,8 @@ def main():
         "config": {"workload": "W4A16 decode GEMV sweep M in {1,4,8}, K=4096 N=11008 G=128, "
                                "16 rotated weight sets",
                    "M": list(DEC_MS), "K": DEC_K, "N": DEC_N, "G": DEC_G,
-                   "rotation_sets": ROT, "step_flops": step_flops, "step_bytes": step_bytes,
+                   "rotation_sets": ROT, "steps_per_graph": ROT, "step_flops": step_flops,
+                   "step_bytes": step_bytes,
                    "device": props.name, "cus": props.multi_processor_count},
         "roofline": roofline,
         "cpu_baseline": cpu,
