@@ -61,6 +61,12 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
     constexpr int SPL = GW * NSW * 2;            // 16-byte scale pieces per wave (<= 64)
     static_assert(APIECES < 64 || APL * 64 == APIECES, "A staging must tile the wave's slice");
     static_assert(SPL <= 64, "one scale piece per lane");
+    // C = 1032 * sum_k a_k per (row, group): by VALU during staging, except
+    // for 16-row tiles over several strips, where an extra MFMA per k-step
+    // against a constant 1032 operand (shared by the strips) is cheaper than
+    // sixteen rows of sums and shuffles (measured: M = 16 8.8 us instead of
+    // 9.6; for M <= 8 the VALU sums are faster)
+    constexpr bool CM = NSW >= 2 && MT >= 16;
     struct WaveLds {
         _Float16 a[MT * LDA];
         float c[GW][16];
@@ -121,14 +127,18 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
             // (Whole-vector bit casts only: a bit cast of one element of a
             // u32x4 was miscompiled by this toolchain into element 0.)
             const half8 h = __builtin_bit_cast(half8, ast[p]);
-            float part = 0.f;
+            if constexpr (CM) {
+                if (idx < APIECES) *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
+            } else {
+                float part = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) part += (float)h[j];
+                for (int j = 0; j < 8; ++j) part += (float)h[j];
 #pragma unroll
-            for (int off = 1; off < GP; off <<= 1) part += __shfl_xor(part, off);
-            if (idx < APIECES) {
-                *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
-                if (c8 % GP == 0) L.c[c8 / GP][row] = part * 1032.0f;
+                for (int off = 1; off < GP; off <<= 1) part += __shfl_xor(part, off);
+                if (idx < APIECES) {
+                    *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
+                    if (c8 % GP == 0) L.c[c8 / GP][row] = part * 1032.0f;
+                }
             }
         }
         if (lane < SPL) *reinterpret_cast<uintx4*>(&L.s[sp_g][sp_r * 8]) = sreg;
@@ -143,7 +153,16 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int gl = i * NG + g;
-                const floatx4 cc = *reinterpret_cast<const floatx4*>(&L.c[gl][4 * q]);
+                floatx4 cc;
+                if constexpr (CM) {
+                    const _Float16 k1032 = (_Float16)1032.0f;
+                    const half8 c1032 = {k1032, k1032, k1032, k1032, k1032, k1032, k1032, k1032};
+                    cc = zero;
+#pragma unroll
+                    for (int kk = g * KKPG; kk < (g + 1) * KKPG; ++kk) cc = mfma16(a[kk], c1032, cc);
+                } else {
+                    cc = *reinterpret_cast<const floatx4*>(&L.c[gl][4 * q]);
+                }
 #pragma unroll
                 for (int s = 0; s < NSW; ++s) {
                     const uint32_t d[4] = {braw[i][s].x, braw[i][s].y, braw[i][s].z, braw[i][s].w};
