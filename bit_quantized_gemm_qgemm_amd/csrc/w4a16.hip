@@ -4,8 +4,8 @@
 // Int4 Groupwise GEMM Plugin V2 page (class summary: inputs, output and the
 // fragment-layout weights; configurePlugin: the token count M steers the
 // kernel choice).  Three kernels, chosen by M:
-//   decode  (M <= 16): HBM-bound weight stream.  Each wave owns NSW 16-column
-//       strips and KCW 128-k chunks; it issues every weight, A and scale load
+//   decode  (M <= 16): HBM-bound weight stream.  Each wave owns up to NSW
+//       16-column strips and KCW 128-k chunks; it issues every weight, A and scale load
 //       of its slice before its first wait, stages A and scales in its own
 //       LDS slice (no workgroup barrier before the main loop) and runs
 //       v_mfma_f32_16x16x32_f16 on the raw fp16 values 1024 + u; per-group
@@ -33,10 +33,12 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
 }
 
 // Decode kernel.  MT = rows of the MFMA A tile that may be non-zero
-// (M <= MT <= 16); each wave owns NSW 16-column strips and KCW 128-k chunks
-// (NSW * KCW 16-byte weight loads per lane); WK = 32 / KCW waves cover
-// 4096 k, so a workgroup of WK waves holds NSW strips over a whole 4096-k
-// block and reduces its K partials in LDS in a fixed order.
+// (M <= MT <= 16); each wave owns up to NSW 16-column strips and KCW 128-k
+// chunks (NSW * KCW 16-byte weight loads per lane); WK = 32 / KCW waves cover
+// 4096 k, so a workgroup of WK waves holds its strips over a whole 4096-k
+// block and reduces its K partials in LDS in a fixed order.  With BAL the
+// grid is sized to the chip and each workgroup takes a contiguous range of
+// strips (NSW at most).
 //
 // Everything a wave needs is staged by that wave alone, in its own slice of
 // LDS, so there is no barrier before the main loop: it issues the loads of
@@ -46,7 +48,7 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
 // the raw fp16 values 1024 + u (raw8, seven VALU ops per eight weights); each
 // group's fp32 partial T becomes acc += s * (T - C).  One A fragment read from
 // LDS feeds the MFMAs of all NSW strips.
-template <int MT, int NSW, int KCW, int G>
+template <int MT, int NSW, int KCW, int G, bool BAL>
 __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ wf, const uint16_t* __restrict__ Sc,
     uint16_t* __restrict__ Y, int M, int N, int K) {
@@ -79,7 +81,18 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     WaveLds& L = lds[wave];
-    const int strip0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSW;
+    // BAL: the workgroups share the N / 16 strips in contiguous ranges of
+    // NSW - 1 or NSW strips (every CU busy when N / 16 is not a multiple of
+    // NSW x 256); a slot past the range repeats its last strip and is not stored
+    int strip0, nst;
+    if constexpr (BAL) {
+        const int wg = xcd_contiguous(blockIdx.x, gridDim.x), nstrips = N / 16;
+        strip0 = (int)((long)wg * nstrips / gridDim.x);
+        nst = (int)((long)(wg + 1) * nstrips / gridDim.x) - strip0;
+    } else {
+        strip0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSW;
+        nst = NSW;
+    }
     const int cl = lane & 15, q = lane >> 4;
     const int kchunks = K / 128;
     const int arow = cl & (MT - 1);  // rows >= MT of the MFMA tile are never stored
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
             ast[p] = *reinterpret_cast<const uintx4*>(A + (size_t)row * K + kw0 * (kwl > 0) + c8 * 8);
         }
         const int sp_g = lane / (NSW * 2), sp_r = lane % (NSW * 2);  // group, 8-column piece
-        const bool sp_ok = lane < SPL && sp_g * G < kwl;
+        const bool sp_ok = lane < SPL && sp_g * G < kwl && sp_r < 2 * nst;
         const uintx4 sreg = *reinterpret_cast<const uintx4*>(
             Sc + (sp_ok ? (size_t)(kw0 / G + sp_g) * N + strip0 * 16 + sp_r * 8 : 0));
         uintx4 braw[KCW][NSW];
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
             for (int s = 0; s < NSW; ++s) {
                 const int c = i * 128 < kwl ? kw0 / 128 + i : 0;
                 braw[i][s] = ldg_nt(reinterpret_cast<const uintx4*>(
-                    wf + frag_block_offset(strip0 + s, c, kchunks) + lane * 16));
+                    wf + frag_block_offset(strip0 + (s < nst ? s : nst - 1), c, kchunks) + lane * 16));
             }
         // keep every load above ahead of the first use of any of them
         __builtin_amdgcn_sched_barrier(0);
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
     for (int s = 0; s < NSW; ++s) red[(wave * NSW + s) * 64 + lane] = acc[s];
     __syncthreads();
     // wave w < NSW finalizes strip w
-    if (wave < NSW) {
+    if (wave < nst) {
         floatx4 t = red[wave * 64 + lane];
         for (int w = 1; w < WK; ++w) t += red[(w * NSW + wave) * 64 + lane];
         const int n = (strip0 + wave) * 16 + cl;
@@ -515,20 +528,27 @@ int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, ui
         // (MT, NSW, KCW): rows of the MFMA tile, 16-column strips per wave, 128-k
         // chunks per wave; the workgroup is 32 / KCW waves over NSW strips
         if (M == 1)
-            hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, G>), dim3(N / 16), dim3(512), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<1, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st,
                                A, wf, S, Y, M, N, K);
         else if (M == 2)
-            hipLaunchKernelGGL((w4a16_decode_kernel<2, 1, 4, G>), dim3(N / 16), dim3(512), 0, st,
+            hipLaunchKernelGGL((w4a16_decode_kernel<2, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st,
                                A, wf, S, Y, M, N, K);
-        else if (M <= 4)
-            hipLaunchKernelGGL((w4a16_decode_kernel<4, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
-                               A, wf, S, Y, M, N, K);
-        else if (M <= 8)
-            hipLaunchKernelGGL((w4a16_decode_kernel<8, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
-                               A, wf, S, Y, M, N, K);
-        else
-            hipLaunchKernelGGL((w4a16_decode_kernel<16, 4, 2, G>), dim3(N / 64), dim3(1024), 0, st,
-                               A, wf, S, Y, M, N, K);
+        else {
+            // at least one workgroup per CU where there are enough strips,
+            // each over a contiguous range of at most three strips
+            const int nstrips = N / 16;
+            int nwg = nstrips < 256 ? nstrips : 256;
+            if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
+            if (M <= 4)
+                hipLaunchKernelGGL((w4a16_decode_kernel<4, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st,
+                                   A, wf, S, Y, M, N, K);
+            else if (M <= 8)
+                hipLaunchKernelGGL((w4a16_decode_kernel<8, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st,
+                                   A, wf, S, Y, M, N, K);
+            else
+                hipLaunchKernelGGL((w4a16_decode_kernel<16, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st,
+                                   A, wf, S, Y, M, N, K);
+        }
     } else if (M <= 512 || N % PL_BN != 0) {
         dim3 grid((N / PF_BN) * ((M + PF_BM - 1) / PF_BM));
         hipLaunchKernelGGL(w4a16_prefill_kernel<G>, grid, dim3(256), 0, st, A, wf, S, Y, M, N, K);
