@@ -174,7 +174,7 @@ def main():
     achieved = b1 / (per_m[1]["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<MT=1,NSW=1,KCW=4,G=128> (M=1)",
+                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<MT=1,NSW=1,KCW=4,G=128,BAL=false> (M=1)",
                 "bytes_per_launch": b1}
 
     rows = {}
