@@ -202,59 +202,84 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
 #pragma unroll
         for (int b = 0; b < NB; ++b) load_b_chunk<1, G>(bs[b], wf[b], S[b], N, kchunks, c, ncol0, lane);
     };
+    // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
+    // are interleaved with the MFMAs of step s (one MFMA, then at most one
+    // LDS read and a share of the dequant VALU ops), so the wave keeps the
+    // MFMA unit busy while it prepares the next operands.
+    auto operands = [&](const uint16_t* sa, const BChunk<1, G>* bs, int s, half8 (&a)[NRB],
+                        half8 (&bf)[NB]) {
+        const int kg = kgroup_of_step(s, h);
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) {
+            const int r = i * 32 + c32;
+            a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G>(bs[b], 0, s);
+    };
+    constexpr int NM = NB * NRB;                 // MFMAs per k-step
+    constexpr int VPER = (15 * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
     auto compute = [&](const uint16_t* sa, const BChunk<1, G>* bs) {
+        half8 a[NRB], bf[NB];
+        operands(sa, bs, 0, a, bf);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int kg = kgroup_of_step(s, h);
-            half8 bf[NB], a[NRB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G>(bs[b], 0, s);
-#pragma unroll
-            for (int i = 0; i < NRB; ++i) {
-                const int r = i * 32 + c32;
-                a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
-            }
+            half8 an[NRB], bn[NB];
+            if (s < 7) operands(sa, bs, s + 1, an, bn);
 #pragma unroll
             for (int i = 0; i < NRB; ++i)
 #pragma unroll
                 for (int b = 0; b < NB; ++b) acc[b][i] = mfma32(a[i], bf[b], acc[b][i]);
-            // keep each step's operands short-lived: in issue order the next
-            // step's dequant still runs while these MFMAs execute
-            __builtin_amdgcn_sched_barrier(0);
+            if (s < 7) {
+#pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NRB; ++i) a[i] = an[i];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) bf[b] = bn[b];
         }
     };
     // loads issued after a chunk's DMA: per matrix two B pieces and NG scales
     constexpr int BLOADS = NB * (2 + BChunk<1, G>::NG);
 
-    // Two chunks per trip, no branch inside the trip: a load placed before a
-    // branch but used only after it may be sunk past it by the compiler,
-    // which then waits for every outstanding load (the prefetch is lost).
-    // The last trip reloads its second chunk when the count is even; an odd
-    // count leaves one chunk, already staged, for the tail.
+    // Chunk c runs from LDS buffer c % 2 and register set b[c % 2] while A
+    // and B of chunk c + 1 are in flight into the other buffer and set.  A
+    // trip ends with a full wait: while an LDS-DMA load is outstanding, every
+    // wait the compiler itself places on a register load becomes a full
+    // wait, so the B registers a trip consumes must be complete before it
+    // issues the next DMA.  Two trips per loop pass keep the buffer indices
+    // literals; the prefetch past the last chunk reloads the last chunk and
+    // an odd chunk count leaves one chunk, already staged, for the tail.
     BChunk<1, G> b0[NB], b1[NB];
+    const int last = c1 - 1;
     dma_a(c0, 0);
     __builtin_amdgcn_sched_barrier(0);
     load_b(b0, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<BLOADS>();
-    __syncthreads();
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    auto trip = [&](int c, int abuf, const BChunk<1, G>* bc, BChunk<1, G>* bn) __attribute__((always_inline)) {
+        const int cn = c + 1 < c1 ? c + 1 : last;
+        dma_a(cn, abuf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(bn, cn);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA + abuf * XP_SLAB, bc);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+    };
+    // No branch inside a loop pass: loads used only on one side of a branch
+    // are sunk into it by the compiler (the prefetch is lost).
     int c = c0;
     for (; c + 1 < c1; c += 2) {
-        dma_a(c + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(b1, c + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sA, b0);
-        wait_vmcnt<BLOADS>();  // chunk c + 1's A has landed in LDS
-        __syncthreads();
-        const int cm = c + 2 < c1 ? c + 2 : c + 1;
-        dma_a(cm, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(b0, cm);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sA + XP_SLAB, b1);
-        wait_vmcnt<BLOADS>();
-        __syncthreads();
+        trip(c, 0, b0, b1);
+        trip(c + 1, 1, b1, b0);
     }
     if (c < c1) compute(sA, b0);
 
