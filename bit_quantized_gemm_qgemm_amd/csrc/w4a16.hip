@@ -32,6 +32,29 @@ __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// v plus the value of lane l' of the same 16-lane row, l' given by a DPP
+// control (quad permutation or row mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                     0xf, 0xf, false));
+}
+
+// Sum of v over each aligned group of N adjacent lanes (N = 4, 8 or 16),
+// delivered to every lane of the group: lane ^ 1 and lane ^ 2 (quad
+// permutations) give quad sums, the half-row mirror (lane 7 - i within 8)
+// adds the other quad and the row mirror (lane 15 - i within 16) the other
+// half.  Register moves only, no LDS round trips.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    v = dpp_add<0xB1>(v);                          // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);                          // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
+    if constexpr (N >= 16) v = dpp_add<0x140>(v);  // row_mirror
+    return v;
+}
+
 // Decode kernel.  MT = rows of the MFMA A tile that may be non-zero
 // (M <= MT <= 16); each wave owns up to NSW 16-column strips and KCW 128-k
 // chunks (NSW * KCW 16-byte weight loads per lane); WK = 32 / KCW waves cover
@@ -146,8 +169,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void w4a16_decode_kernel(
                 float part = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) part += (float)h[j];
-#pragma unroll
-                for (int off = 1; off < GP; off <<= 1) part += __shfl_xor(part, off);
+                part = group_sum<GP>(part);
                 if (idx < APIECES) {
                     *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
                     if (c8 % GP == 0) L.c[c8 / GP][row] = part * 1032.0f;
