@@ -20,10 +20,34 @@ namespace {
 using qg::uintx2;
 using qg::uintx4;
 
+// max(v, value of another lane of the same 16-lane row), the lane given by a
+// DPP control (quad permutation or row mirror)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                          CTRL, 0xf, 0xf, false)));
+}
+
+// Maximum over each aligned group of LPR lanes (16 or 64), delivered to every
+// lane of the group, by register moves only: within a 16-lane row lane ^ 1,
+// lane ^ 2 (quad permutations), then the half-row and row mirrors; a whole
+// wave then combines its four row maxima read from lanes 0, 16, 32 and 48.
+// The maximum is exact, so the order does not matter.
 template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, LPR));
+    static_assert(LPR == 16 || LPR == 64, "rows of 16 lanes or whole waves");
+    v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror
+    if constexpr (LPR == 64) {
+        const int b = __builtin_bit_cast(int, v);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+        v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    }
     return v;
 }
 
