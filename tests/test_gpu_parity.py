@@ -277,6 +277,26 @@ def test_moe_small(qg, T, H, I, E, topK, G):
     assert_fp16_close(Y, Yr, "moe small")
 
 
+# degenerate routings: every token sent to experts 2 and 5 (six experts hold no
+# row and their workgroups exit at once), and a single token
+@pytest.mark.parametrize("T,H,I,E,topK,G,skew", [(90, 256, 256, 8, 2, 128, True),
+                                                  (1, 128, 256, 4, 2, 64, False)])
+def test_moe_degenerate_routing(qg, T, H, I, E, topK, G, skew):
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 850 + T)
+    if skew:
+        logits[:, 2] += np.float16(8)
+        logits[:, 5] += np.float16(7)
+    Y, ids, w, off, pairs = moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G)
+    Yr, idr, wr = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G)
+    assert np.array_equal(ids, idr)
+    if skew:
+        assert set(np.unique(idr)) == {2, 5}
+    offr, pairsr = oracle.moe_permute(idr, E)
+    assert np.array_equal(off, offr) and np.array_equal(pairs, pairsr)
+    assert np.allclose(w, wr, rtol=1e-6, atol=0)
+    assert_fp16_close(Y, Yr, f"moe degenerate T={T}")
+
+
 def test_moe_cfg4_sampled(qg):
     T, H, I, E, topK, G = 256, 4096, 14336, 8, 2, 128
     X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 104)
