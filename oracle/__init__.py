@@ -65,6 +65,14 @@ def _declare(lib):
         "qo_moe_permute": (None, [_P, _I32, _I32, _I32, _P, _P]),
         "qo_moe": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32]),
+        "qo_e4m3_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
+        "qo_f64_to_e4m3": (ctypes.c_uint8, [ctypes.c_double]),
+        "qo_e4m3_to_f64_array": (None, [_P, _P, _I64]),
+        "qo_f64_to_e4m3_array": (None, [_P, _P, _I64]),
+        "qo_quant_fp8": (None, [_P, _P, _P, _I64, _I32, _I32]),
+        "qo_dequant_fp8": (None, [_P, _P, _P, _I64, _I32, _I32]),
+        "qo_fp8_gemm": (None, [_P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32]),
+        "qo_fp8_gemm_at": (None, [_P, _P, _P, _I32, _P, _I32, _I64, _P, _P, _P, _I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -178,6 +186,73 @@ def dequant_sym_int8(Q, S):
     X = np.empty(Q.shape, np.float16)
     _load().qo_dequant_sym_int8(_ptr(Q), _ptr(S), _ptr(X), rows, cols)
     return X
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+
+def e4m3_to_f64(codes):
+    b = _c(codes, np.uint8)
+    out = np.empty(b.shape, np.float64)
+    _load().qo_e4m3_to_f64_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def f64_to_e4m3(x):
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    _load().qo_f64_to_e4m3_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def quant_fp8(X, per_row=True):
+    """Codes uint8 [rows][cols] and scales fp32 ([rows] per row, [1] per tensor)."""
+    X = _c(X, np.float16)
+    rows, cols = X.reshape(-1, X.shape[-1]).shape
+    Q = np.empty(X.shape, np.uint8)
+    S = np.empty(rows if per_row else 1, np.float32)
+    _load().qo_quant_fp8(_ptr(X), _ptr(Q), _ptr(S), rows, cols, 1 if per_row else 0)
+    return Q, S
+
+
+def dequant_fp8(Q, S, per_row=True):
+    Q = _c(Q, np.uint8)
+    S = _c(S, np.float32)
+    rows, cols = Q.reshape(-1, Q.shape[-1]).shape
+    assert S.size == (rows if per_row else 1)
+    X = np.empty(Q.shape, np.float16)
+    _load().qo_dequant_fp8(_ptr(Q), _ptr(S), _ptr(X), rows, cols, 1 if per_row else 0)
+    return X
+
+
+def fp8_gemm(A, W, sa, sw, want_f64=False):
+    """A e4m3 codes [M][K], W e4m3 codes [N][K]; sa of size M or 1, sw of size N or 1."""
+    A = _c(A, np.uint8)
+    W = _c(W, np.uint8)
+    sa = _c(sa, np.float32).ravel()
+    sw = _c(sw, np.float32).ravel()
+    M, K = A.shape
+    N = W.shape[0]
+    assert W.shape[1] == K and sa.size in (1, M) and sw.size in (1, N)
+    Y = np.empty((M, N), np.float16)
+    Y64 = np.empty((M, N), np.float64) if want_f64 else None
+    _load().qo_fp8_gemm(_ptr(A), _ptr(W), _ptr(sa), int(sa.size == M and M > 1), _ptr(sw),
+                        int(sw.size == N and N > 1), _ptr(Y), _ptr(Y64), M, N, K)
+    return (Y, Y64) if want_f64 else Y
+
+
+def fp8_gemm_at(A, W, sa, sw, ms, ns):
+    A = _c(A, np.uint8)
+    W = _c(W, np.uint8)
+    sa = _c(sa, np.float32).ravel()
+    sw = _c(sw, np.float32).ravel()
+    ms = _c(ms, np.int32)
+    ns = _c(ns, np.int32)
+    M, K = A.shape
+    N = W.shape[0]
+    Y = np.empty(ms.size, np.float16)
+    _load().qo_fp8_gemm_at(_ptr(A), _ptr(W), _ptr(sa), int(sa.size == M and M > 1), _ptr(sw),
+                           int(sw.size == N and N > 1), ms.size, _ptr(ms), _ptr(ns), _ptr(Y), K)
+    return Y
 
 
 # ---------------------------------------------------------------- W8A8

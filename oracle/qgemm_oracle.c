@@ -29,6 +29,9 @@
  *        per-token symmetric quantization; rescale + bias + GELU, then
  *        requantize), answer step 1 (scale = 127 / max|x|), knowledge point 5
  *        (saturation to [-127, 127]).
+ *   [P2] FP8 vs INT8 low-precision inference in TensorRT-LLM (itzkxy.com):
+ *        FP8 E4M3 for GEMMs and the KV cache, per-tensor scaling factors
+ *        derived from the activation A-max.
  *   [P3] "Int4 Groupwise GEMM Plugin V2" (TensorRT-Edge-LLM C++ API docs):
  *        class summary (W4A16 group-wise GEMM; inputs: fp16 activations
  *        [b,seq,K], int4 weights, fp16 scales [ceil(K/G), N]; output fp16
@@ -463,4 +466,129 @@ QO_API void qo_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* Wg,
     free(o);
     free(hb);
     free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3  [P2: FP8 E4M3 GEMM with per-tensor scaling factors derived     */
+/* from the activation A-max, and the FP8 KV cache]                          */
+/* Format: OCP "E4M3FN" -- sign, 4 exponent bits (bias 7), 3 mantissa bits; */
+/* no infinities; exponent and mantissa all ones is NaN; largest finite     */
+/* 448, smallest normal 2^-6, subnormals m * 2^-9.                          */
+/* ------------------------------------------------------------------------ */
+
+/* code -> exact binary64 value (NaN for the two NaN codes) */
+QO_API double qo_e4m3_to_f64(uint8_t b) {
+    const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* binary64 -> code: round to nearest, ties to the even mantissa; |x| >= 448
+   saturates to +-448 (the quantizer clamps first, so this only matters for
+   direct calls).  NaN input is outside the contract. */
+QO_API uint8_t qo_f64_to_e4m3(double x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7e;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal binade: multiples of 2^-9; 8 * 2^-9 is the smallest normal (code 0x08) */
+        return sign | (uint8_t)nearbyint(a * 512.0);
+    }
+    int e;
+    frexp(a, &e);                                  /* a in [2^(e-1), 2^e) */
+    double q = nearbyint(ldexp(a, 4 - e));         /* 8 + mantissa, in [8, 16] */
+    int E = e + 6;                                 /* exponent field of 2^(e-1) */
+    if (q == 16.0) { q = 8.0; E += 1; }
+    return sign | (uint8_t)(E << 3) | (uint8_t)(q - 8.0);
+}
+
+QO_API void qo_e4m3_to_f64_array(const uint8_t* b, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = qo_e4m3_to_f64(b[i]);
+}
+QO_API void qo_f64_to_e4m3_array(const double* x, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = qo_f64_to_e4m3(x[i]);
+}
+
+/* Symmetric FP8 quantization, per row (per_row != 0: one scale per row, as
+   the per-token KV cache) or per tensor (one scale for all rows):
+     amax = max |x|;  if amax == 0: s = 0, codes 0
+     else m = fl32(448 / amax); s = fl32(amax / 448);
+          q = e4m3(clamp(fl32(x * m), -448, 448))
+   S receives rows scales (per row) or one scale (per tensor). */
+QO_API void qo_quant_fp8(const uint16_t* X, uint8_t* Q, float* S, int64_t rows, int32_t cols,
+                         int32_t per_row) {
+    const int64_t groups = per_row ? rows : 1;
+    const int64_t grows = per_row ? 1 : rows;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < groups; ++g) {
+        const uint16_t* x = X + g * grows * cols;
+        uint8_t* q = Q + g * grows * cols;
+        const int64_t n = grows * cols;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < n; ++i) {
+            const float a = fabsf(qo_f16_to_f32(x[i]));
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0f) {
+            S[g] = 0.0f;
+            for (int64_t i = 0; i < n; ++i) q[i] = 0;
+            continue;
+        }
+        const float mult = 448.0f / amax;
+        S[g] = amax / 448.0f;
+        for (int64_t i = 0; i < n; ++i) {
+            float t = qo_f16_to_f32(x[i]) * mult;
+            if (t > 448.0f) t = 448.0f;
+            if (t < -448.0f) t = -448.0f;
+            q[i] = qo_f64_to_e4m3((double)t);
+        }
+    }
+}
+
+/* Dequantization: x = fp16(fl32(e4m3 value * s)), s per row or one per tensor. */
+QO_API void qo_dequant_fp8(const uint8_t* Q, const float* S, uint16_t* X, int64_t rows,
+                           int32_t cols, int32_t per_row) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float s = S[per_row ? r : 0];
+        for (int32_t c = 0; c < cols; ++c) {
+            const float p = (float)qo_e4m3_to_f64(Q[r * cols + c]) * s;
+            X[r * cols + c] = qo_f64_to_f16((double)p);
+        }
+    }
+}
+
+/* FP8 GEMM: A e4m3 [M][K], W e4m3 [N][K] (one row per output column);
+     acc = sum_k A[m][k] * W[n][k]  (every product and partial sum exact in fp64)
+     Y[m][n] = fp16(acc * sa[m or 0] * sw[n or 0])  (fp64 products, one rounding) */
+static double qo_fp8_dot(const uint8_t* a, const uint8_t* w, int32_t K) {
+    double acc = 0.0;
+    for (int32_t k = 0; k < K; ++k) acc += qo_e4m3_to_f64(a[k]) * qo_e4m3_to_f64(w[k]);
+    return acc;
+}
+
+QO_API void qo_fp8_gemm(const uint8_t* A, const uint8_t* W, const float* sa, int32_t sa_per_row,
+                        const float* sw, int32_t sw_per_row, uint16_t* Y, double* Y64, int32_t M,
+                        int32_t N, int32_t K) {
+#pragma omp parallel for schedule(static)
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t n = 0; n < N; ++n) {
+            const double acc = qo_fp8_dot(A + (int64_t)m * K, W + (int64_t)n * K, K);
+            const double y = acc * (double)sa[sa_per_row ? m : 0] * (double)sw[sw_per_row ? n : 0];
+            Y[(int64_t)m * N + n] = qo_f64_to_f16(y);
+            if (Y64) Y64[(int64_t)m * N + n] = y;
+        }
+}
+
+/* Same definition at the listed (m, n) positions. */
+QO_API void qo_fp8_gemm_at(const uint8_t* A, const uint8_t* W, const float* sa, int32_t sa_per_row,
+                           const float* sw, int32_t sw_per_row, int64_t count, const int32_t* ms,
+                           const int32_t* ns, uint16_t* Y, int32_t K) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        const int32_t m = ms[i], n = ns[i];
+        const double acc = qo_fp8_dot(A + (int64_t)m * K, W + (int64_t)n * K, K);
+        Y[i] = qo_f64_to_f16(acc * (double)sa[sa_per_row ? m : 0] * (double)sw[sw_per_row ? n : 0]);
+    }
 }
