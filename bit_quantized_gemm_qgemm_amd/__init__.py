@@ -27,6 +27,9 @@ HIP_ERROR = 6
 EPI_BIAS = 1
 EPI_GELU = 2
 
+FP8_PER_TENSOR = 0
+FP8_PER_ROW = 1
+
 _lib = None
 
 
@@ -76,6 +79,9 @@ def _declare(L):
                                        _I32, _I32, _I32, _P]),
         "moe_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
         "moe_w4a16": (_I32, [_P] * 11 + [_I32] * 7 + [_P, _SZ, _P]),
+        "quant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
+        "dequant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
+        "qgemm_fp8": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -85,7 +91,8 @@ def _declare(L):
 
 EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
-           "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16")
+           "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
+           "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8")
 
 
 def _ptr(t):
@@ -245,3 +252,59 @@ def moe_w4a16(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_do
                            _ptr(topk_ids), _ptr(topk_w), T, H, I, E, topK, G, activation,
                            _ptr(workspace), workspace.numel(), _stream()))
     return Y, topk_ids, topk_w, workspace
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+
+def quant_fp8_e4m3(X, per_row=True, Q=None, scales=None):
+    """E4M3 codes (uint8) and fp32 scales ([rows] per row, [1] per tensor) of fp16 X [..., cols]."""
+    _need(X, torch.float16, "X")
+    cols = X.shape[-1]
+    rows = X.numel() // cols if cols else 0
+    if Q is None:
+        Q = torch.empty(X.shape, dtype=torch.uint8, device=X.device)
+    if scales is None:
+        n = rows if per_row else 1
+        scales = torch.empty(max(n, 1), dtype=torch.float32, device=X.device)[:n]
+    _need(Q, torch.uint8, "Q")
+    _need(scales, torch.float32, "scales")
+    _check("quant_fp8_e4m3", lib().quant_fp8_e4m3(_ptr(X), _ptr(Q), _ptr(scales), rows, cols,
+                                                   FP8_PER_ROW if per_row else FP8_PER_TENSOR, _stream()))
+    return Q, scales
+
+
+def dequant_fp8_e4m3(Q, scales, per_row=True, X=None):
+    _need(Q, torch.uint8, "Q")
+    _need(scales, torch.float32, "scales")
+    cols = Q.shape[-1]
+    rows = Q.numel() // cols if cols else 0
+    if X is None:
+        X = torch.empty(Q.shape, dtype=torch.float16, device=Q.device)
+    _need(X, torch.float16, "X")
+    _check("dequant_fp8_e4m3", lib().dequant_fp8_e4m3(_ptr(Q), _ptr(scales), _ptr(X), rows, cols,
+                                                       FP8_PER_ROW if per_row else FP8_PER_TENSOR, _stream()))
+    return X
+
+
+def qgemm_fp8(A, W, a_scale, w_scale, Y=None):
+    """fp16 Y[M, N] from E4M3 codes A [M, K] and W [N, K]; a scale vector of one
+    element is per tensor, of M (N) elements per row (column)."""
+    _need(A, torch.uint8, "A")
+    _need(W, torch.uint8, "W")
+    _need(a_scale, torch.float32, "a_scale")
+    _need(w_scale, torch.float32, "w_scale")
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("A and W disagree on K")
+    a_per_row = 1 if (a_scale.numel() == M and M > 1) else 0
+    w_per_row = 1 if (w_scale.numel() == N and N > 1) else 0
+    if (not a_per_row and a_scale.numel() != 1) or (not w_per_row and w_scale.numel() != 1):
+        raise ValueError("a scale vector must have one element or one per row / column")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    _need(Y, torch.float16, "Y")
+    _check("qgemm_fp8", lib().qgemm_fp8(_ptr(A), _ptr(W), _ptr(a_scale), a_per_row, _ptr(w_scale),
+                                         w_per_row, _ptr(Y), M, N, K, _stream()))
+    return Y
+

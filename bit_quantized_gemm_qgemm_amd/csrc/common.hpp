@@ -28,6 +28,15 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// fp16 of fl32(a * s): the fp32 product, then its fp16 rounding (two
+// roundings, as the dequantizers define it).  Without the canonicalize
+// between them the compiler fuses the multiply and the conversion into one
+// mixed-precision FMA with a +0 addend, which rounds only once and returns +0
+// where the product is -0.
+__device__ __forceinline__ uint16_t f2h_of_product(float a, float s) {
+    return f2h(__builtin_canonicalizef(a * s));
+}
+
 // ---------------------------------------------------------------- int4 -> fp16
 //
 // Fragment-layout word: eight offset-binary nibbles u = v + 8 holding the
@@ -98,6 +107,51 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) {
     return __builtin_nontemporal_load(p);
+}
+
+// ---- row reductions (int8 and fp8 quantizers)
+
+// max(v, value of another lane of the same 16-lane row), the lane given by a
+// DPP control (quad permutation or row mirror)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                          CTRL, 0xf, 0xf, false)));
+}
+
+// Maximum over each aligned group of LPR lanes (16 or 64), delivered to every
+// lane of the group, by register moves only: within a 16-lane row lane ^ 1,
+// lane ^ 2 (quad permutations), then the half-row and row mirrors; a whole
+// wave then combines its four row maxima read from lanes 0, 16, 32 and 48.
+// The maximum is exact, so the order does not matter.
+template <int LPR>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(LPR == 16 || LPR == 64, "rows of 16 lanes or whole waves");
+    v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_max<0x141>(v);  // row_half_mirror
+    v = dpp_max<0x140>(v);  // row_mirror
+    if constexpr (LPR == 64) {
+        const int b = __builtin_bit_cast(int, v);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+        v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    }
+    return v;
+}
+
+__device__ __forceinline__ float absmax8(uintx4 v) {
+    // |x| of eight fp16 values: clear the sign bits, compare as fp16
+    float m = 0.0f;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, h2f(w[i] & 0x7fffu));
+        m = fmaxf(m, h2f((w[i] >> 16) & 0x7fffu));
+    }
+    return m;
 }
 
 }  // namespace qg

@@ -1,0 +1,350 @@
+// FP8 (OCP E4M3) path: symmetric quantization, dequantization and an FP8
+// GEMM with fp16 output.
+//
+// FP8-vs-INT8 article for TensorRT-LLM (itzkxy.com): the E4M3 format for the
+// GEMMs and the KV cache, per-tensor scaling factors derived from the
+// activation A-max, FP8 operands fed straight to the matrix units.
+//
+// Encoding: v_cvt_pk_fp8_f32 on gfx950 produces OCP E4M3 (E4M3FN: bias 7,
+// largest finite 448, S.1111.111 = NaN) and rounds to nearest even; it turns
+// magnitudes above 464 into NaN, so every value is clamped to [-448, 448]
+// first (the clamp is exact).  The quantizer's arithmetic is the fp32
+// sequence of the header: m = 448 / amax, s = amax / 448,
+// code = e4m3(clamp(x * m)) -- correctly rounded division, no contraction.
+//
+// GEMM: v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation).  Lane l
+// holds row (A) / column (B) l % 32 and 32 consecutive k bytes of a 64-k
+// step, the same (lane half, byte) -> k assignment for both operands, so the
+// K-contiguous rows of A [M][K] and W [N][K] feed it directly.  The tiling is
+// that of the int8 W8A8 kernel: 256x256 output tiles, eight waves (two per
+// SIMD) of 128x64, operands by global -> LDS DMA (two buffers each, one LDS
+// array, compile-time offsets), XOR-swizzled 16-byte pieces, software-
+// pipelined steps.
+#include "common.hpp"
+
+namespace {
+
+using namespace qg;
+
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// four fp16 values (two words) times mult, clamped, -> four E4M3 codes in one word
+__device__ __forceinline__ uint32_t fp8x4(uint32_t h01, uint32_t h23, float mult) {
+    float x[4] = {h2f(h01 & 0xffffu), h2f(h01 >> 16), h2f(h23 & 0xffffu), h2f(h23 >> 16)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(x[i] * mult, -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);  // bytes 0, 1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);       // bytes 2, 3
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ uintx2 fp8x8(uintx4 v, float mult) {
+    return uintx2{fp8x4(v.x, v.y, mult), fp8x4(v.z, v.w, mult)};
+}
+
+// ------------------------------------------------------------------ per-row quant
+
+// Rows held in registers: each of LPR lanes holds CPL chunks of 8 values;
+// the row's amax by DPP moves, codes written from the same registers.
+template <int LPR, int CPL>
+__global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __restrict__ X,
+                                                             uint8_t* __restrict__ Q,
+                                                             float* __restrict__ S, int rows,
+                                                             int cols) {
+    constexpr int RPB = 256 / LPR;  // rows per block
+    const int lane = threadIdx.x % LPR;
+    const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+    const bool live = row < rows;
+    const int nchunk = cols / 8;
+    const uint16_t* x = X + (size_t)(live ? row : 0) * cols;
+    // unconditional loads (a chunk past the row end reads chunk 0 and is zeroed)
+    uintx4 v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + i * LPR;
+        v[i] = ldg_nt(reinterpret_cast<const uintx4*>(x) + (c < nchunk ? c : 0));
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
+        amax = fmaxf(amax, absmax8(v[i]));
+    }
+    amax = group_max<LPR>(amax);
+    if (!live) return;
+    const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    if (lane == 0) S[row] = amax > 0.0f ? amax / 448.0f : 0.0f;
+    uintx2* q = reinterpret_cast<uintx2*>(Q + (size_t)row * cols);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + i * LPR;
+        if (c < nchunk) q[c] = fp8x8(v[i], mult);
+    }
+}
+
+// ------------------------------------------------------------------ per-tensor quant
+
+// The tensor's amax is built in the scale slot itself: it is zeroed, every
+// block raises it with an integer atomic max on the fp32 bit pattern (|x| >= 0
+// orders like its bits, and a maximum does not depend on the order of the
+// updates, so the result is deterministic), the codes are written with
+// m = 448 / amax, and the slot is finally turned into s = amax / 448.  Four
+// stream-ordered launches; no memset (the sequence may be graph-captured).
+__global__ void fp8_slot_zero_kernel(uint32_t* slot) { *slot = 0u; }
+
+__global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t* __restrict__ X, size_t nchunk,
+                                                       uint32_t* __restrict__ slot) {
+    __shared__ float part[4];
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    float amax = 0.0f;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride)
+        amax = fmaxf(amax, absmax8(ldg_nt(reinterpret_cast<const uintx4*>(X) + c)));
+    amax = group_max<64>(amax);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+        atomicMax(slot, __builtin_bit_cast(uint32_t, m));
+    }
+}
+
+__global__ __launch_bounds__(256) void fp8_quant_tensor_kernel(const uint16_t* __restrict__ X,
+                                                               uint8_t* __restrict__ Q, size_t nchunk,
+                                                               const uint32_t* __restrict__ slot) {
+    const float amax = __builtin_bit_cast(float, *slot);
+    const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride)
+        reinterpret_cast<uintx2*>(Q)[c] = fp8x8(ldg_nt(reinterpret_cast<const uintx4*>(X) + c), mult);
+}
+
+__global__ void fp8_slot_finalize_kernel(float* slot) {
+    const float amax = *slot;
+    *slot = amax > 0.0f ? amax / 448.0f : 0.0f;
+}
+
+// ------------------------------------------------------------------ dequant
+
+// Each lane turns a chunk of 8 codes into 8 fp16 values (cols % 8 == 0, so a
+// chunk never straddles rows); grid-stride over chunks.
+__global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ Q,
+                                                          const float* __restrict__ S,
+                                                          uint16_t* __restrict__ X, size_t nchunk,
+                                                          int chunks_per_row, int per_row) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
+        const uintx2 q = ldg_nt(reinterpret_cast<const uintx2*>(Q) + c);
+        const float s = S[per_row ? c / chunks_per_row : 0];
+        const uint32_t w[2] = {q.x, q.y};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t h0 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0), s);
+            const uint32_t h1 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 1), s);
+            const uint32_t h2 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2), s);
+            const uint32_t h3 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 3), s);
+            o[2 * i] = h0 | (h1 << 16);
+            o[2 * i + 1] = h2 | (h3 << 16);
+        }
+        reinterpret_cast<uintx4*>(X)[c] = uintx4{o[0], o[1], o[2], o[3]};
+    }
+}
+
+// ------------------------------------------------------------------ GEMM
+
+constexpr int FB = 256;  // output tile edge
+
+__device__ __forceinline__ floatx16 mfma_fp8(intx8 a, intx8 b, floatx16 c) {
+    // format 0 for both operands = E4M3; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ W,
+                                                          const float* __restrict__ sa, int sa_per_row,
+                                                          const float* __restrict__ sw, int sw_per_row,
+                                                          uint16_t* __restrict__ Y, int M, int N, int K) {
+    constexpr int SL = FB * 128;  // bytes per operand buffer (256 rows x 128 k)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * SL];  // A0, A1, W0, W1
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    // tile (x, y) of workgroup L: y = L % (row tiles), so the workgroups on
+    // one XCD (dealt round-robin by id) share their A row tiles in its L2
+    const int mtiles = (M + FB - 1) / FB;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * FB, n0 = (L / mtiles) * FB;
+    const int kchunks = K / 128, last = kchunks - 1;
+    const int h = lane >> 5, c32 = lane & 31;
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
+
+    // wave w issues DMA instructions 4w .. 4w + 3 of each operand tile (1 KB =
+    // 8 rows of 128 bytes each); the lane filling position pos of row r
+    // fetches piece pos ^ ((r >> 1) & 7).  Rows past M or N repeat the last
+    // row (never stored).  Sources are 32-bit byte offsets from the operand
+    // base (rows * K < 2^32 is checked at launch).
+    const int rsub = lane >> 3, pos = lane & 7;
+    uint32_t offa[4], offw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (4 * wave + j) + rsub;
+        const uint32_t piece = (uint32_t)((pos ^ ((r >> 1) & 7)) * 16);
+        offa[j] = (uint32_t)(m0 + r < M ? m0 + r : M - 1) * (uint32_t)K + piece;
+        offw[j] = (uint32_t)(n0 + r < N ? n0 + r : N - 1) * (uint32_t)K + piece;
+    }
+    auto dma = [&](const uint8_t* base, const uint32_t (&off)[4], uint8_t* dst) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(base + off[j], dst + (4 * wave + j) * 1024, 16, 0, 0);
+    };
+    // operand of row r for 64-k step s: bytes k = 64 s + 32 h .. + 31 = pieces
+    // 4 s + 2 h and 4 s + 2 h + 1 of the row
+    auto frag = [&](const uint8_t* buf, int r, int s) {
+        const int p = 4 * s + 2 * h, sw = (r >> 1) & 7;
+        const intx4 lo = *reinterpret_cast<const intx4*>(buf + r * 128 + ((p ^ sw) * 16));
+        const intx4 hi = *reinterpret_cast<const intx4*>(buf + r * 128 + (((p + 1) ^ sw) * 16));
+        return intx8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    auto operands = [&](const uint8_t* ab, const uint8_t* wb, int s, intx8 (&a)[4], intx8 (&b)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = frag(ab, wm * 128 + i * 32 + c32, s);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) b[t] = frag(wb, wn * 64 + t * 32 + c32, s);
+    };
+    // two 64-k steps per chunk; the operand reads of step 1 are interleaved
+    // with the MFMAs of step 0
+    auto compute = [&](const uint8_t* ab, const uint8_t* wb) {
+        intx8 a[4], b[2], an[4], bn[2];
+        operands(ab, wb, 0, a, b);
+        operands(ab, wb, 1, an, bn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[i][t] = mfma_fp8(a[i], b[t], acc[i][t]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[i][t] = mfma_fp8(an[i], bn[t], acc[i][t]);
+    };
+
+    dma(A, offa, lds);
+    dma(W, offw, lds + 2 * SL);
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    // one trip per chunk: DMA of chunk c + 1 into the idle buffers, MFMAs on
+    // chunk c, then a wait for this wave's DMA and a bare barrier (buffer
+    // indices are literals at every call so that the compiler can tell the
+    // DMA targets from the buffers being read)
+    auto trip = [&](int c, int buf) __attribute__((always_inline)) {
+        const int cn = c + 1 < last ? c + 1 : last;
+        dma(A + cn * 128, offa, lds + (buf ^ 1) * SL);
+        dma(W + cn * 128, offw, lds + (2 + (buf ^ 1)) * SL);
+        compute(lds + buf * SL, lds + (2 + buf) * SL);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int c = 0; c < kchunks; c += 2) {
+        trip(c, 0);
+        if (c + 1 < kchunks) trip(c + 1, 1);
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int col = n0 + wn * 64 + t * 32 + c32;
+        if (col >= N) continue;
+        const float swv = sw[sw_per_row ? col : 0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + wm * 128 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+                if (row < M) Y[(size_t)row * N + col] = f2h((acc[i][t][j] * sa[sa_per_row ? row : 0]) * swv);
+            }
+        }
+    }
+}
+
+int grid_for(size_t nchunk) {
+    const size_t want = (nchunk + 255) / 256;
+    return (int)(want < 8192 ? (want > 0 ? want : 1) : 8192);
+}
+
+}  // namespace
+
+extern "C" int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, int32_t rows,
+                                  int32_t cols, int32_t per_row, void* stream) {
+    if (rows < 0 || cols < 0) return QGEMM_BAD_SHAPE;
+    if (rows == 0) return QGEMM_OK;
+    if (!X || !Q || !scales) return QGEMM_NULL_PTR;
+    if (cols == 0 || cols % 8 != 0 || (per_row && cols > 4096) || (per_row != 0 && per_row != 1))
+        return QGEMM_UNSUPPORTED;
+    if (!qgh::aligned(X, 16) || !qgh::aligned(Q, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
+    hipStream_t st = (hipStream_t)stream;
+    if (per_row) {
+        if (cols <= 256) {
+            hipLaunchKernelGGL((fp8_quant_rows_kernel<16, 2>), dim3((rows + 15) / 16), dim3(256), 0, st, X, Q,
+                               scales, rows, cols);
+        } else {
+            hipLaunchKernelGGL((fp8_quant_rows_kernel<64, 8>), dim3((rows + 3) / 4), dim3(256), 0, st, X, Q,
+                               scales, rows, cols);
+        }
+        return qgh::launch_status();
+    }
+    const size_t nchunk = (size_t)rows * cols / 8;
+    uint32_t* slot = reinterpret_cast<uint32_t*>(scales);
+    hipLaunchKernelGGL(fp8_slot_zero_kernel, dim3(1), dim3(1), 0, st, slot);
+    hipLaunchKernelGGL(fp8_amax_kernel, dim3(grid_for(nchunk)), dim3(256), 0, st, X, nchunk, slot);
+    hipLaunchKernelGGL(fp8_quant_tensor_kernel, dim3(grid_for(nchunk)), dim3(256), 0, st, X, Q, nchunk,
+                       (const uint32_t*)slot);
+    hipLaunchKernelGGL(fp8_slot_finalize_kernel, dim3(1), dim3(1), 0, st, scales);
+    return qgh::launch_status();
+}
+
+extern "C" int32_t dequant_fp8_e4m3(const uint8_t* Q, const float* scales, uint16_t* X, int32_t rows,
+                                    int32_t cols, int32_t per_row, void* stream) {
+    if (rows < 0 || cols < 0) return QGEMM_BAD_SHAPE;
+    if (rows == 0) return QGEMM_OK;
+    if (!Q || !scales || !X) return QGEMM_NULL_PTR;
+    if (cols == 0 || cols % 8 != 0 || (per_row != 0 && per_row != 1)) return QGEMM_UNSUPPORTED;
+    if (!qgh::aligned(Q, 16) || !qgh::aligned(X, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
+    const size_t nchunk = (size_t)rows * cols / 8;
+    hipLaunchKernelGGL(fp8_dequant_kernel, dim3(grid_for(nchunk)), dim3(256), 0, (hipStream_t)stream, Q, scales,
+                       X, nchunk, cols / 8, per_row);
+    return qgh::launch_status();
+}
+
+extern "C" int32_t qgemm_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale, int32_t a_per_row,
+                             const float* w_scale, int32_t w_per_row, uint16_t* Y, int32_t M, int32_t N,
+                             int32_t K, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return QGEMM_BAD_SHAPE;
+    if (M == 0 || N == 0) return QGEMM_OK;
+    if (!A || !W || !a_scale || !w_scale || !Y) return QGEMM_NULL_PTR;
+    if (K == 0 || K % 128 != 0 || (a_per_row != 0 && a_per_row != 1) || (w_per_row != 0 && w_per_row != 1) ||
+        (size_t)M * K >= ((size_t)1 << 32) || (size_t)N * K >= ((size_t)1 << 32))
+        return QGEMM_UNSUPPORTED;
+    if (!qgh::aligned(A, 16) || !qgh::aligned(W, 16) || !qgh::aligned(Y, 16) || !qgh::aligned(a_scale, 4) ||
+        !qgh::aligned(w_scale, 4))
+        return QGEMM_MISALIGNED;
+    const int grid = ((N + FB - 1) / FB) * ((M + FB - 1) / FB);
+    hipLaunchKernelGGL(fp8_gemm_kernel, dim3(grid), dim3(512), 0, (hipStream_t)stream, A, W, a_scale, a_per_row,
+                       w_scale, w_per_row, Y, M, N, K);
+    return qgh::launch_status();
+}

@@ -20,37 +20,6 @@ namespace {
 using qg::uintx2;
 using qg::uintx4;
 
-// max(v, value of another lane of the same 16-lane row), the lane given by a
-// DPP control (quad permutation or row mirror)
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                          CTRL, 0xf, 0xf, false)));
-}
-
-// Maximum over each aligned group of LPR lanes (16 or 64), delivered to every
-// lane of the group, by register moves only: within a 16-lane row lane ^ 1,
-// lane ^ 2 (quad permutations), then the half-row and row mirrors; a whole
-// wave then combines its four row maxima read from lanes 0, 16, 32 and 48.
-// The maximum is exact, so the order does not matter.
-template <int LPR>
-__device__ __forceinline__ float group_max(float v) {
-    static_assert(LPR == 16 || LPR == 64, "rows of 16 lanes or whole waves");
-    v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-    v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-    v = dpp_max<0x141>(v);  // row_half_mirror
-    v = dpp_max<0x140>(v);  // row_mirror
-    if constexpr (LPR == 64) {
-        const int b = __builtin_bit_cast(int, v);
-        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
-        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
-        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
-        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
-        v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-    }
-    return v;
-}
-
 __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float mult) {
     // four fp16 values (two words) -> four int8 codes in one word
     const float x[4] = {qg::h2f(h01 & 0xffffu), qg::h2f(h01 >> 16), qg::h2f(h23 & 0xffffu),
@@ -63,18 +32,6 @@ __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float mul
         out |= ((uint32_t)(int32_t)v & 0xffu) << (8 * i);
     }
     return out;
-}
-
-__device__ __forceinline__ float absmax8(uintx4 v) {
-    // |x| of eight fp16 values: clear the sign bits, compare as fp16
-    float m = 0.0f;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, qg::h2f(w[i] & 0x7fffu));
-        m = fmaxf(m, qg::h2f((w[i] >> 16) & 0x7fffu));
-    }
-    return m;
 }
 
 // Rows held in registers: each of LPR lanes holds CPL chunks of 8 values.
@@ -102,9 +59,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
-        amax = fmaxf(amax, absmax8(v[i]));
+        amax = fmaxf(amax, qg::absmax8(v[i]));
     }
-    amax = group_max<LPR>(amax);
+    amax = qg::group_max<LPR>(amax);
     if (!live) return;
     const float mult = amax > 0.0f ? 127.0f / amax : 0.0f;
     if (lane == 0) S[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
@@ -131,8 +88,8 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
     const int nchunk = cols / 8;
     const uintx4* x = reinterpret_cast<const uintx4*>(X + (size_t)row * cols);
     float amax = 0.0f;
-    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, absmax8(x[c]));
-    amax = group_max<64>(amax);
+    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, qg::absmax8(x[c]));
+    amax = qg::group_max<64>(amax);
     const float mult = amax > 0.0f ? 127.0f / amax : 0.0f;
     if (lane == 0) S[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
     uintx2* q = reinterpret_cast<uintx2*>(Q + (size_t)row * cols);
@@ -158,9 +115,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float a = (float)(int8_t)((w[i] >> (16 * j)) & 0xffu) * s;
-                const float b = (float)(int8_t)((w[i] >> (16 * j + 8)) & 0xffu) * s;
-                o[2 * i + j] = (uint32_t)qg::f2h(a) | ((uint32_t)qg::f2h(b) << 16);
+                const uint32_t a = qg::f2h_of_product((float)(int8_t)((w[i] >> (16 * j)) & 0xffu), s);
+                const uint32_t b = qg::f2h_of_product((float)(int8_t)((w[i] >> (16 * j + 8)) & 0xffu), s);
+                o[2 * i + j] = a | (b << 16);
             }
         }
         reinterpret_cast<uintx4*>(X)[c] = uintx4{o[0], o[1], o[2], o[3]};

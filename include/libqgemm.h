@@ -23,7 +23,8 @@
  *     the per-row/per-column vectors (scales, bias, routing outputs), which
  *     need 4-byte alignment.
  *   - Results are deterministic: fixed reduction orders, no floating-point
- *     atomics; two calls with the same inputs give identical bits.
+ *     atomics (the one atomic, in per-tensor FP8 quantization, is an integer
+ *     maximum); two calls with the same inputs give identical bits.
  */
 #ifndef LIBQGEMM_H
 #define LIBQGEMM_H
@@ -210,6 +211,52 @@ QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uin
                   float* topk_w, int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK,
                   int32_t G, int32_t activation, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 E4M3  (FP8-vs-INT8 article for TensorRT-LLM: the E4M3 format for the
+ * GEMMs and the KV cache, scaling factors from the activation A-max,
+ * per-tensor scaling sufficing for FP8).
+ *
+ * Format: OCP E4M3 ("E4M3FN"): sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities; S.1111.111 is NaN; largest finite 448.  Codes are
+ * passed as uint8_t.  NaN or infinite inputs are outside the contract.
+ * ---------------------------------------------------------------------- */
+#define QGEMM_FP8_PER_TENSOR 0 /* one scale for the whole [rows][cols] tensor */
+#define QGEMM_FP8_PER_ROW 1    /* one scale per row (per token / per channel) */
+
+/* Symmetric FP8 quantization of fp16 X [rows][cols] into codes Q [rows][cols]:
+     amax = max |x| over a row (per row) or over the tensor (per tensor);
+     if amax == 0: scale 0 and every code 0x00;
+     else m = fl32(448 / amax); s = fl32(amax / 448);
+          Q = e4m3_rne(clamp(fl32(x * m), -448, 448))   (ties to even)
+   scales: fp32, [rows] per row or [1] per tensor (output: s).
+   per_row: QGEMM_FP8_PER_ROW or QGEMM_FP8_PER_TENSOR.
+   cols must be a multiple of 8 (per row also at most 4096); rows == 0 is a
+   no-op.  Codes and scales are bit-exact functions of X.  Per tensor, the
+   amax is accumulated in scales[0] (by an integer atomic max on its bits,
+   whose result does not depend on order) over four stream-ordered launches,
+   so scales must not be read before the call has completed on the stream. */
+QGEMM_API int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, int32_t rows,
+                                 int32_t cols, int32_t per_row, void* stream);
+
+/* X[r][c] = fp16( fl32( e4m3_value(Q[r][c]) * s ) ), round to nearest even,
+   s = scales[r] (per row) or scales[0] (per tensor).  cols % 8 == 0. */
+QGEMM_API int32_t dequant_fp8_e4m3(const uint8_t* Q, const float* scales, uint16_t* X, int32_t rows,
+                                   int32_t cols, int32_t per_row, void* stream);
+
+/* FP8 GEMM with fp16 output:
+     acc[m][n] = sum_k e4m3(A[m][k]) * e4m3(W[n][k])     (fp32 accumulation)
+     Y[m][n]   = fp16( fl32( fl32(acc * sa) * sw ) )
+   with sa = a_scale[m] (a_per_row = 1) or a_scale[0] (0), and
+   sw = w_scale[n] (w_per_row = 1) or w_scale[0] (0).
+   A: E4M3 codes [M][K]; W: E4M3 codes [N][K] (one row per output column,
+   both K-contiguous); Y: fp16 [M][N] (output).
+   Supported: K % 128 == 0, M*K < 2^32, N*K < 2^32; any M, N >= 1 (M == 0
+   or N == 0 is a no-op).  The accumulation order is fixed, so results are
+   reproducible; they match the exact sum within fp32 rounding. */
+QGEMM_API int32_t qgemm_fp8(const uint8_t* A, const uint8_t* W, const float* a_scale,
+                            int32_t a_per_row, const float* w_scale, int32_t w_per_row, uint16_t* Y,
+                            int32_t M, int32_t N, int32_t K, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     assert sorted(names) == sorted([
         "qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
         "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
-        "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16"])
+        "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
+        "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -105,6 +106,28 @@ def test_quant_validation(L):
     assert d(FAKE, FAKE, None, 4, 128, None) == 1
     assert d(FAKE, FAKE, FAKE, -4, 128, None) == 2
     assert d(FAKE, FAKE, FAKE, 4, 100, None) == 5
+
+
+def test_fp8_validation(L):
+    q, d, g = L.quant_fp8_e4m3, L.dequant_fp8_e4m3, L.qgemm_fp8
+    assert q(FAKE, FAKE, FAKE, 0, 128, 1, None) == 0
+    assert q(None, FAKE, FAKE, 4, 128, 1, None) == 1
+    assert q(FAKE, FAKE, FAKE, -1, 128, 1, None) == 2
+    assert q(FAKE, FAKE, FAKE, 4, 12, 1, None) == 5
+    assert q(FAKE, FAKE, FAKE, 4, 4104, 1, None) == 5      # per row: at most 4096 columns
+    assert q(FAKE, FAKE, FAKE, 4, 128, 2, None) == 5       # granularity is 0 or 1
+    assert q(FAKE + 8, FAKE, FAKE, 4, 128, 0, None) == 3
+    assert d(FAKE, FAKE, None, 4, 128, 1, None) == 1
+    assert d(FAKE, FAKE, FAKE, 4, 100, 0, None) == 5
+    assert d(FAKE, FAKE + 2, FAKE, 4, 128, 0, None) == 3
+    assert g(FAKE, FAKE, FAKE, 1, FAKE, 1, FAKE, 0, 256, 256, None) == 0
+    assert g(FAKE, FAKE, FAKE, 1, FAKE, 1, FAKE, 4, 0, 256, None) == 0
+    assert g(FAKE, None, FAKE, 1, FAKE, 1, FAKE, 4, 256, 256, None) == 1
+    assert g(FAKE, FAKE, FAKE, 1, FAKE, 1, FAKE, -4, 256, 256, None) == 2
+    assert g(FAKE, FAKE, FAKE, 1, FAKE, 1, FAKE, 4, 256, 200, None) == 5   # K % 128
+    assert g(FAKE, FAKE, FAKE, 3, FAKE, 1, FAKE, 4, 256, 256, None) == 5   # a_per_row 0 or 1
+    assert g(FAKE, FAKE, FAKE, 1, FAKE, 1, FAKE, 1 << 20, 256, 4096, None) == 5  # M*K >= 2^32
+    assert g(FAKE + 16, FAKE + 8, FAKE, 1, FAKE, 1, FAKE, 4, 256, 256, None) == 3
 
 
 def test_w8a8_validation(L):

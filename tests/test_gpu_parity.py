@@ -309,3 +309,89 @@ def test_moe_cfg4_sampled(qg):
     toks = [0, 1, 77, 128, 200, 255]
     Yr, _, _ = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=toks)
     assert_fp16_close(Y[toks], Yr[toks], "moe cfg4 sampled tokens")
+
+
+# ------------------------------------------------------------------ FP8 E4M3
+# codes, scales and dequantized values bit-exact; the FP8 GEMM within the
+# fp16 tolerance above (fp32 accumulation against the exact sum)
+
+FP8_FINITE = np.array([c for c in range(256) if c & 0x7f != 0x7f], np.uint8)
+
+
+@pytest.mark.parametrize("per_row", [True, False])
+@pytest.mark.parametrize("cols", [8, 128, 256, 264, 4096])
+@pytest.mark.parametrize("rows", [1, 3, 17, 100])
+def test_fp8_quant_shapes_and_edge_rows(qg, rows, cols, per_row):
+    X = qi.activations(rows, cols, 900 + rows + cols)
+    X[0, :] = 0                               # all-zero row
+    if rows > 1:
+        X[1, :] = np.float16(-0.0)
+        # amax 448 (m = 1): exact codes, ties between neighbours (17 -> 16, 19 -> 20), 448
+        X[1, :8] = np.array([448, 17, 19, -17, -448, 0, 0.0029296875, 1], np.float16)
+    if rows > 2:
+        X[2, :] *= np.float16(1e-4)           # tiny values
+    Q, S = qg.quant_fp8_e4m3(dev(X), per_row=per_row)
+    Qr, Sr = oracle.quant_fp8(X, per_row=per_row)
+    assert np.array_equal(host(Q), Qr)
+    assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32))
+    Xd = host(qg.dequant_fp8_e4m3(Q, S, per_row=per_row))
+    assert np.array_equal(bits(Xd), bits(oracle.dequant_fp8(Qr, Sr, per_row=per_row)))
+
+
+def test_fp8_dequant_every_code(qg):
+    Q = np.tile(FP8_FINITE, (3, 1))[:, :248]
+    S = np.array([1.0, 0.37, 3e-3], np.float32)
+    for per_row in (True, False):
+        Sx = S if per_row else S[:1]
+        Xd = host(qg.dequant_fp8_e4m3(dev(Q), dev(Sx), per_row=per_row))
+        assert np.array_equal(bits(Xd), bits(oracle.dequant_fp8(Q, Sx, per_row=per_row)))
+
+
+@pytest.mark.parametrize("per_row", [True, False])
+def test_fp8_kv_cache(qg, per_row):
+    X = qi.kv_problem(32, 2048, 128, 105)
+    Q, S = qg.quant_fp8_e4m3(dev(X), per_row=per_row)
+    Qr, Sr = oracle.quant_fp8(X.reshape(-1, 128), per_row=per_row)
+    assert np.array_equal(host(Q).reshape(-1, 128), Qr)
+    assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32))
+    Xd = host(qg.dequant_fp8_e4m3(Q, S, per_row=per_row))
+    assert np.array_equal(bits(Xd).reshape(-1, 128), bits(oracle.dequant_fp8(Qr, Sr, per_row=per_row)))
+
+
+def fp8_operands(M, N, K, seed):
+    r = np.random.default_rng(seed)
+    A = r.choice(FP8_FINITE, (M, K)).astype(np.uint8)
+    W = r.choice(FP8_FINITE, (N, K)).astype(np.uint8)
+    sa = r.uniform(1e-4, 1e-3, M).astype(np.float32)
+    sw = r.uniform(1e-4, 1e-3, N).astype(np.float32)
+    return A, W, sa, sw
+
+
+# several 256x256 tiles, ragged M and N, one and three K chunks, per-row and
+# per-tensor scales
+@pytest.mark.parametrize("scales", ["row", "tensor"])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (64, 256, 256), (300, 512, 384), (257, 300, 256),
+                                   (512, 256, 128)])
+def test_fp8_gemm_small(qg, M, N, K, scales):
+    A, W, sa, sw = fp8_operands(M, N, K, 950 + M + N + K)
+    if scales == "tensor":
+        sa, sw = sa[:1], sw[:1]
+    Y = host(qg.qgemm_fp8(dev(A), dev(W), dev(sa), dev(sw)))
+    assert_fp16_close(Y, oracle.fp8_gemm(A, W, sa, sw), f"fp8 M={M} N={N} K={K} {scales}")
+
+
+def test_fp8_gemm_4096_sampled(qg):
+    # activations and weights through the GPU quantizer (per tensor), as a
+    # serving path would produce them
+    M = N = K = 4096
+    X, Wf, _, _ = qi.w8a8_problem(M, N, K, 106)
+    qa, sa = qg.quant_fp8_e4m3(dev(X), per_row=False)
+    qw, sw = qg.quant_fp8_e4m3(dev(Wf), per_row=False)
+    A, Wc = host(qa), host(qw)
+    Y = host(qg.qgemm_fp8(qa, qw, sa, sw))
+    ms, ns = qi.sample_positions(M, N, 4000, 11)
+    ref = oracle.fp8_gemm_at(A, Wc, host(sa), host(sw), ms, ns)
+    assert_fp16_close(Y[ms, ns], ref, "fp8 4096 sampled")
+    # deterministic
+    Y2 = host(qg.qgemm_fp8(qa, qw, sa, sw))
+    assert np.array_equal(bits(Y2), bits(Y))
