@@ -18,7 +18,8 @@ cpu_baseline = the CPU oracle on the same step (all host threads the oracle
              uses), repeated for about 10 s
 rows       = every other hot-path row, each timed the same way on its own
              inputs (prefill GEMM, W8A8 GEMM + epilogue, per-token int8
-             quantization, KV-cache quant/dequant, INT4 MoE layer)
+             quantization, KV-cache quant/dequant, INT4 MoE layer, and the
+             FP8 E4M3 path: per-tensor quantization, FP8 GEMM, FP8 KV cache)
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu]
 """
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 I8_MFMA_PEAK_TOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 op/clk (dense)
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense E4M3 MFMA, AMD's published MI355X figure
 
 DEC_K, DEC_N, DEC_G = 4096, 11008, 128
 DEC_MS = (1, 4, 8)
@@ -412,6 +414,49 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
         "hbm_frac": round((wbytes + abytes) / tm / 1e9 / HBM_PEAK_GBS, 4),
         "tokens_per_expert": counts.tolist()}
     log(f"[bench] moe {rows['moe_T256_H4096_I14336_E8_top2']}")
+    del pg, pu, pd, Xd, Ld, Sgd, Sud, Sdd, ws
+
+    # FP8 E4M3: per-tensor activation quant 4096 x 4096, FP8 GEMM M=N=K=4096
+    # (fp16 out), per-row KV cache [32, 2048, 128] quant + dequant (16 rotated sets)
+    M = N = K = 4096
+    X, Wf16, _, _ = qi.w8a8_problem(M, N, K, 106)
+    Xd = to_dev(X)
+    qw8, sw8 = qg.quant_fp8_e4m3(to_dev(Wf16), per_row=False)
+    qa8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa8 = torch.empty(1, dtype=torch.float32, device=dev)
+    Y8 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    gq = graph_of([lambda: qg.quant_fp8_e4m3(Xd, per_row=False, Q=qa8, scales=sa8)] * 8)
+    tq = time_graph(gq, 8, reps=10)
+    qb = 3 * M * K + 4
+    rows["fp8_quant_per_tensor_4096x4096"] = {"us": round(tq * 1e6, 2), "GB/s": round(qb / tq / 1e9, 1),
+                                              "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4)}
+    qg.quant_fp8_e4m3(Xd, per_row=False, Q=qa8, scales=sa8)
+    gg = graph_of([lambda: qg.qgemm_fp8(qa8, qw8, sa8, sw8, Y=Y8)] * 8)
+    tg = time_graph(gg, 8, reps=10)
+    fl = 2 * M * N * K
+    rows["fp8_gemm_4096"] = {"us": round(tg * 1e6, 2), "TFLOP/s": round(fl / tg / 1e12, 1),
+                             "mfma_frac": round(fl / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)}
+    log(f"[bench] fp8 gemm {rows['fp8_gemm_4096']} quant {rows['fp8_quant_per_tensor_4096x4096']}")
+    del Xd, qw8, qa8, Y8
+    R = 16
+    kvs = [to_dev(qi.kv_problem(32, 2048, 128, 105 + 1000 * r)) for r in range(R)]
+    Q8 = torch.empty((32, 2048, 128), dtype=torch.uint8, device=dev)
+    Sk = torch.empty(32 * 2048, dtype=torch.float32, device=dev)
+    Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
+    Qs = [torch.empty((32, 2048, 128), dtype=torch.uint8, device=dev) for _ in range(R)]
+    Ss = [torch.empty(32 * 2048, dtype=torch.float32, device=dev) for _ in range(R)]
+    for r in range(R):
+        qg.quant_fp8_e4m3(kvs[r], Q=Qs[r], scales=Ss[r])
+    gk = graph_of([(lambda r=r: qg.quant_fp8_e4m3(kvs[r], Q=Q8, scales=Sk)) for r in range(R)])
+    tk = time_graph(gk, R, reps=10)
+    gd = graph_of([(lambda r=r: qg.dequant_fp8_e4m3(Qs[r], Ss[r], X=Xo)) for r in range(R)])
+    td = time_graph(gd, R, reps=10)
+    kb = 3 * 65536 * 128 + 4 * 65536
+    rows["fp8_kv_quant_32x2048x128"] = {"us": round(tk * 1e6, 2), "GB/s": round(kb / tk / 1e9, 1),
+                                        "hbm_frac": round(kb / tk / 1e9 / HBM_PEAK_GBS, 4)}
+    rows["fp8_kv_dequant_32x2048x128"] = {"us": round(td * 1e6, 2), "GB/s": round(kb / td / 1e9, 1),
+                                          "hbm_frac": round(kb / td / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] fp8 kv {rows['fp8_kv_quant_32x2048x128']} {rows['fp8_kv_dequant_32x2048x128']}")
     return rows
 
 

@@ -92,13 +92,22 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
 // stream-ordered launches; no memset (the sequence may be graph-captured).
 __global__ void fp8_slot_zero_kernel(uint32_t* slot) { *slot = 0u; }
 
+// A few blocks per CU, four loads in flight per lane, one atomic per block.
+constexpr int AMAX_BLOCKS = 1024;
+
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t* __restrict__ X, size_t nchunk,
                                                        uint32_t* __restrict__ slot) {
     __shared__ float part[4];
     const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const uintx4* x = reinterpret_cast<const uintx4*>(X);
     float amax = 0.0f;
-    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride)
-        amax = fmaxf(amax, absmax8(ldg_nt(reinterpret_cast<const uintx4*>(X) + c)));
+    size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; c + 3 * stride < nchunk; c += 4 * stride) {
+        const uintx4 v0 = ldg_nt(x + c), v1 = ldg_nt(x + c + stride);
+        const uintx4 v2 = ldg_nt(x + c + 2 * stride), v3 = ldg_nt(x + c + 3 * stride);
+        amax = fmaxf(amax, fmaxf(fmaxf(absmax8(v0), absmax8(v1)), fmaxf(absmax8(v2), absmax8(v3))));
+    }
+    for (; c < nchunk; c += stride) amax = fmaxf(amax, absmax8(ldg_nt(x + c)));
     amax = group_max<64>(amax);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
     __syncthreads();
@@ -311,7 +320,8 @@ extern "C" int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, 
     const size_t nchunk = (size_t)rows * cols / 8;
     uint32_t* slot = reinterpret_cast<uint32_t*>(scales);
     hipLaunchKernelGGL(fp8_slot_zero_kernel, dim3(1), dim3(1), 0, st, slot);
-    hipLaunchKernelGGL(fp8_amax_kernel, dim3(grid_for(nchunk)), dim3(256), 0, st, X, nchunk, slot);
+    const int ablocks = grid_for(nchunk) < AMAX_BLOCKS ? grid_for(nchunk) : AMAX_BLOCKS;
+    hipLaunchKernelGGL(fp8_amax_kernel, dim3(ablocks), dim3(256), 0, st, X, nchunk, slot);
     hipLaunchKernelGGL(fp8_quant_tensor_kernel, dim3(grid_for(nchunk)), dim3(256), 0, st, X, Q, nchunk,
                        (const uint32_t*)slot);
     hipLaunchKernelGGL(fp8_slot_finalize_kernel, dim3(1), dim3(1), 0, st, scales);
