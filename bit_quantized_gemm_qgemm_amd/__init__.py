@@ -147,7 +147,9 @@ def qgemm_w4a16_workspace_bytes(M, N, K, G):
 
 
 def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
-    """Y[M, N] = A[M, K] (fp16) x dequant(w_frag, scales [K/G, N] fp16)."""
+    """Y[M, N] = A[M, K] (fp16) x dequant(w_frag, scales [K/G, N] fp16).  Without a
+    workspace the one the library asks for (mid M) is allocated here; an empty
+    tensor selects the kernels that need none."""
     _need(A, torch.float16, "A")
     _need(w_frag, torch.uint8, "w_frag")
     _need(scales, torch.float16, "scales")
@@ -156,9 +158,13 @@ def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
     _need(Y, torch.float16, "Y")
+    if workspace is None:
+        need = qgemm_w4a16_workspace_bytes(M, N, K, G)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("qgemm_w4a16", lib().qgemm_w4a16(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
-                                             _ptr(workspace), ws, _stream()))
+                                             _ptr(workspace) if ws else None, ws, _stream()))
     return Y
 
 

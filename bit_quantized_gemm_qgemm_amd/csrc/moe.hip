@@ -15,7 +15,7 @@
 //               o being the K-split partials added in split order.
 // Every reduction has a fixed order, so the layer is deterministic.
 #include "common.hpp"
-#include "w4_tile.hpp"
+#include "w4_pass.hpp"
 
 namespace {
 
@@ -162,145 +162,6 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 // kernel; B fragments are prefetched one 128-k chunk ahead in registers.
 // The down projection splits K over KS workgroups (fp32 partials, added in
 // split order by the combine) so that it has enough workgroups.
-
-constexpr int XP_SLAB = 128 * 128;  // halfs per LDS A buffer: 128 rows of 128 k (32 KB)
-
-// MODE 0: gate/up, h[slot][n] = fp16(silu(g) * u).  MODE 1: down, fp32
-// partial o[ks][slot][n].
-template <int G, int NB, int NRB, int MODE, typename RowOff>
-__device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowOff row_off, int R,
-                                            const uint8_t* const* wf, const uint16_t* const* S,
-                                            int N, int kchunks, int c0, int c1, int ncol0,
-                                            int slot0, void* out) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int h = lane >> 5, c32 = lane & 31;
-    floatx16 acc[NB][NRB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < NRB; ++i)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[b][i][j] = 0.f;
-
-    // DMA: the workgroup's 8 NRB wave instructions each fill 1 KB of LDS =
-    // rows 4g .. 4g+3 (g = 2 NRB wave + j); lane l fetches piece
-    // (l % 16) ^ (row % 16) of row 4g + l / 16.  Rows >= R repeat row R - 1.
-    const int rsub = lane >> 4, pos = lane & 15;
-    uint32_t src[2 * NRB];  // element offsets from abase
-#pragma unroll
-    for (int j = 0; j < 2 * NRB; ++j) {
-        const int r = 4 * (2 * NRB * wave + j) + rsub;
-        src[j] = row_off(r < R ? r : R - 1) + ((pos ^ (r & 15)) * 8);
-    }
-    auto dma_a = [&](int c, int buf) {
-#pragma unroll
-        for (int j = 0; j < 2 * NRB; ++j)
-            __builtin_amdgcn_global_load_lds(abase + src[j] + c * 128,
-                                             sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, 16, 0, 0);
-    };
-    auto load_b = [&](BChunk<1, G>* bs, int c) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) load_b_chunk<1, G>(bs[b], wf[b], S[b], N, kchunks, c, ncol0, lane);
-    };
-    // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
-    // are interleaved with the MFMAs of step s (one MFMA, then at most one
-    // LDS read and a share of the dequant VALU ops), so the wave keeps the
-    // MFMA unit busy while it prepares the next operands.
-    auto operands = [&](const uint16_t* sa, const BChunk<1, G>* bs, int s, half8 (&a)[NRB],
-                        half8 (&bf)[NB]) {
-        const int kg = kgroup_of_step(s, h);
-#pragma unroll
-        for (int i = 0; i < NRB; ++i) {
-            const int r = i * 32 + c32;
-            a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G>(bs[b], 0, s);
-    };
-    constexpr int NM = NB * NRB;                 // MFMAs per k-step
-    constexpr int VPER = (15 * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
-    auto compute = [&](const uint16_t* sa, const BChunk<1, G>* bs) {
-        half8 a[NRB], bf[NB];
-        operands(sa, bs, 0, a, bf);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            half8 an[NRB], bn[NB];
-            if (s < 7) operands(sa, bs, s + 1, an, bn);
-#pragma unroll
-            for (int i = 0; i < NRB; ++i)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[b][i] = mfma32(a[i], bf[b], acc[b][i]);
-            if (s < 7) {
-#pragma unroll
-                for (int q = 0; q < NM; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NRB; ++i) a[i] = an[i];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) bf[b] = bn[b];
-        }
-    };
-    // loads issued after a chunk's DMA: per matrix two B pieces and NG scales
-    constexpr int BLOADS = NB * (2 + BChunk<1, G>::NG);
-
-    // Chunk c runs from LDS buffer c % 2 and register set b[c % 2] while A
-    // and B of chunk c + 1 are in flight into the other buffer and set.  A
-    // trip ends with a full wait: while an LDS-DMA load is outstanding, every
-    // wait the compiler itself places on a register load becomes a full
-    // wait, so the B registers a trip consumes must be complete before it
-    // issues the next DMA.  Two trips per loop pass keep the buffer indices
-    // literals; the prefetch past the last chunk reloads the last chunk and
-    // an odd chunk count leaves one chunk, already staged, for the tail.
-    BChunk<1, G> b0[NB], b1[NB];
-    const int last = c1 - 1;
-    dma_a(c0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(b0, c0);
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
-    auto trip = [&](int c, int abuf, const BChunk<1, G>* bc, BChunk<1, G>* bn) __attribute__((always_inline)) {
-        const int cn = c + 1 < c1 ? c + 1 : last;
-        dma_a(cn, abuf ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(bn, cn);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sA + abuf * XP_SLAB, bc);
-        wait_vmcnt<0>();
-        wait_lgkmcnt0();
-        __builtin_amdgcn_s_barrier();
-    };
-    // No branch inside a loop pass: loads used only on one side of a branch
-    // are sunk into it by the compiler (the prefetch is lost).
-    int c = c0;
-    for (; c + 1 < c1; c += 2) {
-        trip(c, 0, b0, b1);
-        trip(c + 1, 1, b1, b0);
-    }
-    if (c < c1) compute(sA, b0);
-
-    const int col = ncol0 + c32;
-#pragma unroll
-    for (int i = 0; i < NRB; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int row = i * 32 + acc_row(j, lane);
-            if (row < R) {
-                const size_t o = (size_t)(slot0 + row) * N + col;
-                if constexpr (MODE == 0) {
-                    const float g = acc[0][i][j], u = acc[NB - 1][i][j];
-                    const float silu = g / (1.0f + expf(-g));
-                    static_cast<uint16_t*>(out)[o] = f2h(silu * u);
-                } else {
-                    static_cast<float*>(out)[o] = acc[0][i][j];
-                }
-            }
-        }
-}
 
 // Workgroup L: expert L % E, then column tile, then K split.
 template <int G, int MODE>

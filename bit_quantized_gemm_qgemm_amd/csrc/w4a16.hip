@@ -11,7 +11,14 @@
 //       v_mfma_f32_16x16x32_f16 on the raw fp16 values 1024 + u; per-group
 //       fp32 partials are corrected and scaled, and the K partials of the
 //       workgroup's waves are added in LDS in a fixed order.
-//   prefill (16 < M <= 512): 128x128 output tiles, four waves of 64x64,
+//   mid (16 < M <= 128, with the workspace qgemm_w4a16_workspace_bytes
+//       asks for): split-K.  A workgroup owns 128 columns and a K range and
+//       runs all M rows through them (the B-stationary pass of the MoE
+//       GEMMs), writing fp32 partials; a second
+//       launch adds the splits in a fixed order and rounds to fp16.  A single
+//       pass over K with 128-column tiles would leave most CUs idle (86
+//       workgroups for N = 11008).
+//   prefill (16 < M <= 512 otherwise): 128x128 output tiles, four waves of 64x64,
 //       A tiles double-buffered through LDS via registers, B fragments read
 //       straight from the fragment layout into registers and dequantized with
 //       the group scale folded in, v_mfma_f32_32x32x16_f16.
@@ -20,7 +27,7 @@
 // Both prefill kernels map the 1-D workgroup index column-major over tiles so
 // that the workgroups resident on one XCD share weight columns in its L2.
 #include "common.hpp"
-#include "w4_tile.hpp"
+#include "w4_pass.hpp"
 
 namespace {
 
@@ -543,6 +550,92 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
         }
 }
 
+// ------------------------------------------------------------------ mid M
+
+// measured crossover: at M = 192 and 256 the two row passes re-stream the
+// weights and the single-pass prefill kernel is faster (47 us against 52 / 63
+// at N = 11008, K = 4096)
+constexpr int MID_MAX_M = 128;
+
+// K splits of the mid-M path: enough 128-column x K-range workgroups for
+// about two per CU, at least one chunk each.
+__host__ __device__ inline int mid_splits(int N, int K) {
+    const int tiles = N / 128, kchunks = K / 128;
+    int s = (512 + tiles - 1) / tiles;
+    if (s > kchunks) s = kchunks;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+
+__host__ __device__ inline size_t mid_workspace_bytes(int M, int N, int K) {
+    return (size_t)mid_splits(N, K) * M * N * sizeof(float);
+}
+
+// Workgroup L: column tile L % tiles (consecutive ids, which the dispatcher
+// spreads over the XCDs, take neighbouring tiles), K split L / tiles over
+// chunks [ks * kc / S, (ks + 1) * kc / S).  part[ks][m][n] fp32.
+template <int G>
+__global__ __launch_bounds__(256, 2) void w4a16_mid_kernel(const uint16_t* __restrict__ A,
+                                                           const uint8_t* __restrict__ wf,
+                                                           const uint16_t* __restrict__ S,
+                                                           float* __restrict__ part, int M, int N, int K,
+                                                           int splits) {
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * XP_SLAB];
+    const int tiles = N / 128, kchunks = K / 128;
+    const int ct = blockIdx.x % tiles, ks = blockIdx.x / tiles;
+    const int c0 = (int)((long)ks * kchunks / splits), c1 = (int)((long)(ks + 1) * kchunks / splits);
+    const uint8_t* wfp[1] = {wf};
+    const uint16_t* sp[1] = {S};
+    const int ncol0 = ct * 128 + (threadIdx.x >> 6) * 32;
+    float* out = part + (size_t)ks * M * N;
+    for (int r0 = 0; r0 < M; r0 += 128) {
+        const int R = M - r0 < 128 ? M - r0 : 128;
+        // element offset of A row r of this pass (M * K < 2^32 is checked at launch)
+        auto row_off = [&](int r) -> uint32_t { return (uint32_t)(r0 + r) * (uint32_t)K; };
+        switch ((R + 31) / 32) {
+            case 1: expert_pass<G, 1, 1, 1>(sA, A, row_off, R, wfp, sp, N, kchunks, c0, c1, ncol0, r0, out); break;
+            case 2: expert_pass<G, 1, 2, 1>(sA, A, row_off, R, wfp, sp, N, kchunks, c0, c1, ncol0, r0, out); break;
+            case 3: expert_pass<G, 1, 3, 1>(sA, A, row_off, R, wfp, sp, N, kchunks, c0, c1, ncol0, r0, out); break;
+            default: expert_pass<G, 1, 4, 1>(sA, A, row_off, R, wfp, sp, N, kchunks, c0, c1, ncol0, r0, out); break;
+        }
+        __syncthreads();  // the next pass refills both LDS buffers
+    }
+}
+
+// Y[i] = fp16(sum over splits s = 0 .. S-1 of part[s][i]), s ascending; eight
+// outputs per lane per step, grid-stride.
+__global__ __launch_bounds__(256) void w4a16_splitk_reduce_kernel(const float* __restrict__ part,
+                                                                  uint16_t* __restrict__ Y, size_t n8,
+                                                                  size_t stride_s, int splits) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n8; c += stride) {
+        const float* p = part + c * 8;
+        floatx4 lo = *reinterpret_cast<const floatx4*>(p);
+        floatx4 hi = *reinterpret_cast<const floatx4*>(p + 4);
+        for (int s = 1; s < splits; ++s) {
+            lo += *reinterpret_cast<const floatx4*>(p + s * stride_s);
+            hi += *reinterpret_cast<const floatx4*>(p + s * stride_s + 4);
+        }
+        const uintx4 o = {(uint32_t)f2h(lo[0]) | ((uint32_t)f2h(lo[1]) << 16),
+                          (uint32_t)f2h(lo[2]) | ((uint32_t)f2h(lo[3]) << 16),
+                          (uint32_t)f2h(hi[0]) | ((uint32_t)f2h(hi[1]) << 16),
+                          (uint32_t)f2h(hi[2]) | ((uint32_t)f2h(hi[3]) << 16)};
+        *reinterpret_cast<uintx4*>(Y + c * 8) = o;
+    }
+}
+
+template <int G>
+int32_t launch_w4a16_mid(const uint16_t* A, const uint8_t* wf, const uint16_t* S, uint16_t* Y, int M,
+                         int N, int K, float* part, hipStream_t st) {
+    const int splits = mid_splits(N, K);
+    hipLaunchKernelGGL(w4a16_mid_kernel<G>, dim3((N / 128) * splits), dim3(256), 0, st, A, wf, S, part, M, N,
+                       K, splits);
+    const size_t n8 = (size_t)M * N / 8, want = (n8 + 255) / 256;
+    hipLaunchKernelGGL(w4a16_splitk_reduce_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
+                       part, Y, n8, (size_t)M * N, splits);
+    return qgh::launch_status();
+}
+
 template <int G>
 int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, uint16_t* Y, int M,
                      int N, int K, hipStream_t st) {
@@ -584,13 +677,19 @@ int32_t launch_w4a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, ui
 
 }  // namespace
 
-extern "C" size_t qgemm_w4a16_workspace_bytes(int32_t, int32_t, int32_t, int32_t) { return 0; }
+// the mid-M path's fp32 split partials; 0 for every other shape
+static bool mid_path(int M, int N, int K) {
+    return M > 16 && M <= MID_MAX_M && (size_t)M * K < ((size_t)1 << 32);
+}
+
+extern "C" size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G) {
+    if (M <= 0 || N <= 0 || K <= 0 || G <= 0 || N % 128 != 0 || K % 128 != 0 || K % G != 0) return 0;
+    return mid_path(M, N, K) ? mid_workspace_bytes(M, N, K) : 0;
+}
 
 extern "C" int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales,
                                uint16_t* Y, int32_t M, int32_t N, int32_t K, int32_t G,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (M < 0 || N < 0 || K < 0 || G <= 0) return QGEMM_BAD_SHAPE;
     if (K % G != 0) return QGEMM_BAD_SHAPE;
     if (M == 0) return QGEMM_OK;
@@ -601,6 +700,15 @@ extern "C" int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const u
         !qgh::aligned(Y, 16))
         return QGEMM_MISALIGNED;
     hipStream_t st = (hipStream_t)stream;
+    if (mid_path(M, N, K) && workspace && qgh::aligned(workspace, 16) &&
+        workspace_bytes >= mid_workspace_bytes(M, N, K)) {
+        float* part = static_cast<float*>(workspace);
+        switch (G) {
+            case 32: return launch_w4a16_mid<32>(A, w_frag, scales, Y, M, N, K, part, st);
+            case 64: return launch_w4a16_mid<64>(A, w_frag, scales, Y, M, N, K, part, st);
+            default: return launch_w4a16_mid<128>(A, w_frag, scales, Y, M, N, K, part, st);
+        }
+    }
     switch (G) {
         case 32: return launch_w4a16<32>(A, w_frag, scales, Y, M, N, K, st);
         case 64: return launch_w4a16<64>(A, w_frag, scales, Y, M, N, K, st);

@@ -89,7 +89,10 @@ QGEMM_API size_t qgemm_w4a16_packed_bytes(int32_t K, int32_t N);
 QGEMM_API int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag, int32_t K, int32_t N,
                             void* stream);
 
-/* Workspace bytes qgemm_w4a16 needs for this shape (currently always 0). */
+/* Workspace bytes qgemm_w4a16 uses for this shape: for 16 < M <= 128 (and
+   M*K < 2^32) the fp32 partial sums of its split-K path,
+   S * M * N * 4 bytes with S = min(ceil(512 / (N/128)), K/128, 16); 0 for
+   every other shape and for invalid arguments. */
 QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
 
 /* Y = A x dequant(w_frag, scales).
@@ -97,9 +100,14 @@ QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, in
    w_frag: prepacked weights from qgemm_w4a16_prepack(K, N).
    scales: fp16 [K/G][N].
    Y:      fp16 [M][N] output; must not overlap the inputs.
-   M == 0 is a successful no-op.  M <= 16 runs the memory-bound decode
-   kernel, larger M the MFMA prefill kernel; both compute the same function
-   (fp32 accumulation, one rounding to fp16 at the end). */
+   workspace: device memory of workspace_bytes bytes (16-byte aligned), or
+   NULL / 0.  M == 0 is a successful no-op.  M <= 16 runs the memory-bound
+   decode kernel; 16 < M <= 128 with at least qgemm_w4a16_workspace_bytes()
+   of workspace runs the split-K kernel (fp32 partials in the workspace, then
+   a reduction adding the K splits in a fixed order); other M, or a smaller
+   workspace, run the MFMA prefill kernels.  All compute the same function
+   (fp32 accumulation, one rounding to fp16 at the end) and are
+   deterministic.  Calls sharing one workspace must not overlap. */
 QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales, uint16_t* Y,
                     int32_t M, int32_t N, int32_t K, int32_t G, void* workspace,
                     size_t workspace_bytes, void* stream);

@@ -61,6 +61,13 @@ def test_size_queries(L):
     assert L.qgemm_w4a16_packed_bytes(4000, 11008) == 0
     assert L.qgemm_w4a16_packed_bytes(4096, 100) == 0
     assert L.qgemm_w4a16_workspace_bytes(1, 11008, 4096, 128) == 0
+    assert L.qgemm_w4a16_workspace_bytes(16, 11008, 4096, 128) == 0
+    assert L.qgemm_w4a16_workspace_bytes(129, 11008, 4096, 128) == 0
+    # mid M: S * M * N * 4 with S = min(ceil(512 / (N/128)), K/128, 16), by the header's rule
+    for M, N, K in [(17, 11008, 4096), (64, 11008, 4096), (64, 4096, 4096), (128, 256, 256), (100, 128, 512)]:
+        S = min(-(-512 // (N // 128)), K // 128, 16)
+        assert L.qgemm_w4a16_workspace_bytes(M, N, K, 128) == S * M * N * 4, (M, N, K)
+    assert L.qgemm_w4a16_workspace_bytes(64, 11008, 4000, 128) == 0   # invalid K
     ws = L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2)
     P_ = 512
     # down-projection K splits, by the rule the header states

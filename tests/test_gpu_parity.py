@@ -118,6 +118,34 @@ def test_w4a16_prefill_small(qg, M, G):
 # M > 512 takes the 128x256 DMA kernel when N % 256 == 0: ragged M, every
 # group size, one chunk and a count that leaves a partial six-trip pass;
 # N = 384 checks that such M falls back to the 128x128 kernel
+# mid M (16 < M <= 128): the split-K path (workspace from the library's
+# query) and, with an empty workspace, the single-pass prefill kernel
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M,K,N", [(17, 1152, 256), (64, 512, 384), (100, 896, 256), (128, 384, 512),
+                                   (33, 256, 128)])
+def test_w4a16_mid_m_split_k(qg, M, K, N, G):
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 470 + M + K + G)
+    assert qg.qgemm_w4a16_workspace_bytes(M, N, K, G) > 0
+    ref = oracle.w4a16(A, Wb, S, G)
+    assert_fp16_close(run_w4a16(qg, A, Wb, S, G), ref, f"split-K M={M} K={K} N={N} G={G}")
+    Wf = prepack(qg, Wb, K, N)
+    Y0 = qg.qgemm_w4a16(dev(A), Wf, dev(S), G, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    assert_fp16_close(host(Y0), ref, f"no workspace M={M}")
+
+
+def test_w4a16_mid_m_full_shape_sampled(qg):
+    # M = 64 on the decode weights (K = 4096, N = 11008): 86 column tiles x 6 K splits
+    M, K, N, G = 64, 4096, 11008, 128
+    Wb, S = qi.w4a16_weights(K, N, G, 101)
+    A = qi.activations(M, K, 1064)
+    Wf = prepack(qg, Wb, K, N)
+    Y = host(qg.qgemm_w4a16(dev(A), Wf, dev(S), G))
+    ms, ns = qi.sample_positions(M, N, 3000, 12)
+    assert_fp16_close(Y[ms, ns], oracle.w4a16_at(A, Wb, S, G, ms, ns), "split-K M=64 cfg1 weights")
+    Y2 = host(qg.qgemm_w4a16(dev(A), Wf, dev(S), G))
+    assert np.array_equal(bits(Y2), bits(Y))
+
+
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("M,K,N", [(513, 128, 256), (640, 896, 512), (1100, 384, 256), (600, 256, 384)])
 def test_w4a16_prefill_large(qg, M, K, N, G):
