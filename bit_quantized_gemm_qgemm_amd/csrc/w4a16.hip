@@ -557,11 +557,12 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
 // at N = 11008, K = 4096)
 constexpr int MID_MAX_M = 128;
 
-// K splits of the mid-M path: enough 128-column x K-range workgroups for
-// about two per CU, at least one chunk each.
+// K splits of the mid-M path: as many 128-column x K-range workgroups as fit
+// in one round at two per CU (a 513th workgroup would double the time), at
+// least one chunk each.
 __host__ __device__ inline int mid_splits(int N, int K) {
     const int tiles = N / 128, kchunks = K / 128;
-    int s = (512 + tiles - 1) / tiles;
+    int s = 512 / tiles;
     if (s > kchunks) s = kchunks;
     if (s > 16) s = 16;
     return s < 1 ? 1 : s;

@@ -91,7 +91,7 @@ QGEMM_API int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag,
 
 /* Workspace bytes qgemm_w4a16 uses for this shape: for 16 < M <= 128 (and
    M*K < 2^32) the fp32 partial sums of its split-K path,
-   S * M * N * 4 bytes with S = min(ceil(512 / (N/128)), K/128, 16); 0 for
+   S * M * N * 4 bytes with S = max(1, min(floor(512 / (N/128)), K/128, 16)); 0 for
    every other shape and for invalid arguments. */
 QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
 

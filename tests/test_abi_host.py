@@ -63,9 +63,10 @@ def test_size_queries(L):
     assert L.qgemm_w4a16_workspace_bytes(1, 11008, 4096, 128) == 0
     assert L.qgemm_w4a16_workspace_bytes(16, 11008, 4096, 128) == 0
     assert L.qgemm_w4a16_workspace_bytes(129, 11008, 4096, 128) == 0
-    # mid M: S * M * N * 4 with S = min(ceil(512 / (N/128)), K/128, 16), by the header's rule
-    for M, N, K in [(17, 11008, 4096), (64, 11008, 4096), (64, 4096, 4096), (128, 256, 256), (100, 128, 512)]:
-        S = min(-(-512 // (N // 128)), K // 128, 16)
+    # mid M: S * M * N * 4 with S = max(1, min(floor(512 / (N/128)), K/128, 16)), by the header's rule
+    for M, N, K in [(17, 11008, 4096), (64, 11008, 4096), (64, 4096, 4096), (128, 256, 256), (100, 128, 512),
+                    (64, 131072, 4096)]:
+        S = max(1, min(512 // (N // 128), K // 128, 16))
         assert L.qgemm_w4a16_workspace_bytes(M, N, K, 128) == S * M * N * 4, (M, N, K)
     assert L.qgemm_w4a16_workspace_bytes(64, 11008, 4000, 128) == 0   # invalid K
     ws = L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2)
