@@ -7,7 +7,8 @@ its Python binding never import it, and it imports nothing from them.
 Thin numpy front end over ``liboracle.so`` (built from ``qgemm_oracle.c``).
 Every function takes and returns numpy arrays in the natural formats:
 fp16 data as ``np.float16`` (bit patterns passed through unchanged), int4
-weights as natural packed bytes ``uint8 [K][N/2]`` (low nibble = even column).
+weights as natural packed bytes ``uint8 [K][N/2]`` (low nibble = even column),
+int8 weights as ``int8 [K][N]``.
 """
 import ctypes
 import os
@@ -54,6 +55,10 @@ def _declare(lib):
         "qo_w4a16_at": (None, [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32]),
         "qo_frag_nibble_index": (_I64, [_I32, _I32, _I32]),
         "qo_w4a16_prepack": (None, [_P, _P, _I32, _I32]),
+        "qo_w8a16": (None, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32]),
+        "qo_w8a16_at": (None, [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32]),
+        "qo_frag8_byte_index": (_I64, [_I32, _I32, _I32]),
+        "qo_w8a16_prepack": (None, [_P, _P, _I32, _I32]),
         "qo_quant_sym_int8": (None, [_P, _P, _P, _I64, _I32]),
         "qo_dequant_sym_int8": (None, [_P, _P, _P, _I64, _I32]),
         "qo_w8a8_acc": (None, [_P, _P, _P, _I32, _I32, _I32]),
@@ -164,6 +169,53 @@ def w4a16_prepack(W, K, N):
     assert W.size == K * N // 2 and K % 128 == 0 and N % 128 == 0
     F = np.empty(K * N // 2, np.uint8)
     _load().qo_w4a16_prepack(_ptr(W), _ptr(F), K, N)
+    return F
+
+
+# ---------------------------------------------------------------- W8A16
+
+def w8a16(A, W, S, G, want_f64=False):
+    """Y = fp16(A @ (W * S)) with fp64 sums; A fp16 [M,K], W int8 [K,N], S fp16 [K/G,N]
+    (G == K: one scale per column)."""
+    A = _c(A, np.float16)
+    W = _c(W, np.int8)
+    S = _c(S, np.float16)
+    M, K = A.shape
+    N = W.shape[1]
+    assert W.shape == (K, N) and K % G == 0 and S.shape == (K // G, N)
+    Y = np.empty((M, N), np.float16)
+    Y64 = np.empty((M, N), np.float64) if want_f64 else None
+    _load().qo_w8a16(_ptr(A), _ptr(W), _ptr(S), _ptr(Y), _ptr(Y64), M, N, K, G)
+    return (Y, Y64) if want_f64 else Y
+
+
+def w8a16_at(A, W, S, G, ms, ns, want_f64=False):
+    A = _c(A, np.float16)
+    W = _c(W, np.int8)
+    S = _c(S, np.float16)
+    M, K = A.shape
+    N = W.shape[1]
+    assert W.shape == (K, N) and K % G == 0 and S.shape == (K // G, N)
+    ms = _c(np.asarray(ms, np.int32), np.int32)
+    ns = _c(np.asarray(ns, np.int32), np.int32)
+    assert ms.shape == ns.shape
+    assert ms.size == 0 or (ms.min() >= 0 and ms.max() < M and ns.min() >= 0 and ns.max() < N)
+    y = np.empty(ms.shape, np.float16)
+    y64 = np.empty(ms.shape, np.float64) if want_f64 else None
+    _load().qo_w8a16_at(_ptr(A), _ptr(W), _ptr(S), _ptr(ms), _ptr(ns), ms.size, _ptr(y), _ptr(y64),
+                        N, K, G)
+    return (y, y64) if want_f64 else y
+
+
+def frag8_byte_index(K, k, n):
+    return _load().qo_frag8_byte_index(K, k, n)
+
+
+def w8a16_prepack(W, K, N):
+    W = _c(W, np.int8)
+    assert W.shape == (K, N) and K % 128 == 0 and N % 128 == 0
+    F = np.empty(K * N, np.uint8)
+    _load().qo_w8a16_prepack(_ptr(W), _ptr(F), K, N)
     return F
 
 

@@ -5,9 +5,11 @@
  * CPU-baseline leg of the benchmark may load or call this library.  The HIP
  * library never includes, links or calls it, and this file includes nothing
  * from the HIP side.  It reads only the *natural* weight format
- * (int4 [K][N/2], low nibble = even column), never the GPU fragment layout,
- * except in qo_w4a16_prepack, which writes that layout from its written
- * definition so the GPU prepack can be checked byte for byte.
+ * (int4 [K][N/2], low nibble = even column; int8 [K][N]), never the GPU
+ * fragment layouts,
+ * except in qo_w4a16_prepack and qo_w8a16_prepack, which write those
+ * layouts from their written definitions so the GPU prepacks can be checked
+ * byte for byte.
  *
  * Arithmetic rules:
  *   - fp16 <-> binary64 conversion is written here from IEEE 754 binary16
@@ -31,7 +33,8 @@
  *        (saturation to [-127, 127]).
  *   [P2] FP8 vs INT8 low-precision inference in TensorRT-LLM (itzkxy.com):
  *        FP8 E4M3 for GEMMs and the KV cache, per-tensor scaling factors
- *        derived from the activation A-max.
+ *        derived from the activation A-max; the INT8 configurations it
+ *        compares (weight-only int8 with fp16 activations among them).
  *   [P3] "Int4 Groupwise GEMM Plugin V2" (TensorRT-Edge-LLM C++ API docs):
  *        class summary (W4A16 group-wise GEMM; inputs: fp16 activations
  *        [b,seq,K], int4 weights, fp16 scales [ceil(K/G), N]; output fp16
@@ -209,6 +212,76 @@ QO_API void qo_w4a16_prepack(const uint8_t* W, uint8_t* F, int32_t K, int32_t N)
             const int64_t idx = qo_frag_nibble_index(K, k, n);
             F[idx / 2] |= (idx & 1) ? (uint8_t)(u << 4) : u;
         }
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A16 weight-only int8 GEMM  [P2 INT8 configurations: int8 weight-only    */
+/* quantization with fp16 activations]                                      */
+/*   Y[m][n] = fp16( sum_k A[m][k] * W[k][n] * S[k/G][n] ),  k ascending     */
+/* A fp16 [M][K]; W int8 [K][N] (two's complement, row-major); S fp16        */
+/* [K/G][N]; G == K is one scale per output column (per channel).  Y fp16    */
+/* [M][N]; Y64 (optional) receives the unrounded fp64 sums.                 */
+/* ------------------------------------------------------------------------ */
+
+static double qo_w8a16_dot(const uint16_t* A, const int8_t* W, const uint16_t* S, int32_t N,
+                           int32_t K, int32_t G, int32_t m, int32_t n) {
+    double s = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+        const double a = qo_f16_to_f64(A[(int64_t)m * K + k]);
+        const double w = (double)W[(int64_t)k * N + n] * qo_f16_to_f64(S[(int64_t)(k / G) * N + n]);
+        s += a * w;
+    }
+    return s;
+}
+
+QO_API void qo_w8a16(const uint16_t* A, const int8_t* W, const uint16_t* S, uint16_t* Y,
+                     double* Y64, int32_t M, int32_t N, int32_t K, int32_t G) {
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t n = 0; n < N; ++n) {
+            const double s = qo_w8a16_dot(A, W, S, N, K, G, m, n);
+            if (Y) Y[(int64_t)m * N + n] = qo_f64_to_f16(s);
+            if (Y64) Y64[(int64_t)m * N + n] = s;
+        }
+}
+
+QO_API void qo_w8a16_at(const uint16_t* A, const int8_t* W, const uint16_t* S,
+                        const int32_t* ms, const int32_t* ns, int64_t count, uint16_t* y,
+                        double* y64, int32_t N, int32_t K, int32_t G) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < count; ++i) {
+        const double s = qo_w8a16_dot(A, W, S, N, K, G, ms[i], ns[i]);
+        if (y) y[i] = qo_f64_to_f16(s);
+        if (y64) y64[i] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Int8 weight prepack: natural int8 [K][N] -> the library's int8 fragment   */
+/* layout, written from its definition:                                      */
+/*   weight block (16 columns x 128 k, 2048 bytes): strip s = n/16,          */
+/*     chunk c = k/128;                                                      */
+/*   tile (128 columns x 128 k, 16384 bytes) = 8 consecutive strips;         */
+/*   block offset = ((s/8) * (K/128) + c) * 16384 + (s%8) * 2048;            */
+/*   inside a block, with r = k%128, column cl = n%16:                       */
+/*     kk = r/32, q = (r%32)/8, j = r%8;                                     */
+/*     byte (kk/2)*1024 + (cl + 16*q)*16 + (kk%2)*8 + j;                     */
+/*     stored value v + 128 (offset binary).                                 */
+/* The k of each byte is that of the int4 layout's nibble with the same      */
+/* (block, cl, q, kk, j).  Requires K % 128 == 0 and N % 128 == 0.           */
+/* ------------------------------------------------------------------------ */
+
+QO_API int64_t qo_frag8_byte_index(int32_t K, int32_t k, int32_t n) {
+    const int32_t s = n / 16, cl = n % 16, c = k / 128, r = k % 128;
+    const int32_t kk = r / 32, q = (r % 32) / 8, j = r % 8;
+    const int64_t block = ((int64_t)(s / 8) * (K / 128) + c) * 16384 + (int64_t)(s % 8) * 2048;
+    return block + (int64_t)(kk / 2) * 1024 + (int64_t)(cl + 16 * q) * 16 + (kk % 2) * 8 + j;
+}
+
+QO_API void qo_w8a16_prepack(const int8_t* W, uint8_t* F, int32_t K, int32_t N) {
+    for (int32_t k = 0; k < K; ++k)
+        for (int32_t n = 0; n < N; ++n)
+            F[qo_frag8_byte_index(K, k, n)] = (uint8_t)((int)W[(int64_t)k * N + n] + 128);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -39,6 +39,16 @@ def w4a16_problem(M, K, N, G, seed):
     return A, W, S
 
 
+def w8a16_problem(M, K, N, G, seed):
+    """fp16 activations ~ N(0, 1); int8 weights [K][N] uniform over [-128, 127]
+    (random bytes); fp16 scales [K/G][N] U[0.0005, 0.002] (G == K: per column)."""
+    r = rng(seed)
+    A = r.standard_normal((M, K)).astype(np.float16)
+    W = r.integers(0, 256, size=(K, N), dtype=np.uint8).view(np.int8)
+    S = r.uniform(0.0005, 0.002, size=(K // G, N)).astype(np.float16)
+    return A, W, S
+
+
 def w8a8_problem(M, N, K, seed):
     """fp16 activations X [M,K] and weights Wf [N,K] ~ N(0,1); bias [N] ~ N(0, 0.1^2);
     the static output multiplier of the recipe, 127 / (4 sqrt(K)) in fp32."""
