@@ -18,8 +18,9 @@ cpu_baseline = the CPU oracle on the same step (all host threads the oracle
              uses), repeated for about 10 s
 rows       = every other hot-path row, each timed the same way on its own
              inputs (prefill GEMM, W8A8 GEMM + epilogue, per-token int8
-             quantization, KV-cache quant/dequant, INT4 MoE layer, and the
-             FP8 E4M3 path: per-tensor quantization, FP8 GEMM, FP8 KV cache)
+             quantization, KV-cache quant/dequant, INT4 MoE layer, the FP8
+             E4M3 path: per-tensor quantization, FP8 GEMM, FP8 KV cache, and
+             weight-only int8 (W8A16) decode and prefill)
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu]
 """
@@ -176,7 +177,7 @@ def main():
     achieved = b1 / (per_m[1]["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": read_traffic(), "kernel": "w4a16_decode_kernel<MT=1,NSW=1,KCW=4,G=128,BAL=false> (M=1)",
+                "traffic": read_traffic(), "kernel": "wq_decode_kernel<WB=4,MT=1,NSW=1,KCW=4,G=128,BAL=false> (M=1)",
                 "bytes_per_launch": b1}
 
     rows = {}
@@ -289,18 +290,27 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
     print(f"profiled {name} x{launches}", file=sys.stderr, flush=True)
 
 
+# sources of the decode kernel whose HBM counters profiles/decode_traffic.json holds
+DECODE_SOURCES = ("common.hpp", "wq_tile.hpp", "wq_pass.hpp", "wq_gemm.hpp", "w4a16.hip")
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def read_traffic():
     """HBM bytes per launch of the M=1 decode kernel from the committed counter
-    summary, if it was taken on the current kernel source; otherwise None."""
-    import hashlib
+    summary, if it was taken on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    src = os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", "csrc", "w4a16.hip")
     try:
         with open(path) as f:
             d = json.load(f)
-        with open(src, "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()[:16]
-        if d.get("source_sha256_16") != h:
+        if d.get("source_sha256_16") != decode_source_hash():
             return None
         return d.get("bytes_per_launch")
     except (OSError, ValueError):
@@ -457,6 +467,38 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
     rows["fp8_kv_dequant_32x2048x128"] = {"us": round(td * 1e6, 2), "GB/s": round(kb / td / 1e9, 1),
                                           "hbm_frac": round(kb / td / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] fp8 kv {rows['fp8_kv_quant_32x2048x128']} {rows['fp8_kv_dequant_32x2048x128']}")
+    del kvs, Qs, Ss, Q8, Sk, Xo
+
+    # W8A16 (int8 weights, fp16 activations, G = 128): decode M = 1, 8 on the
+    # K = 4096, N = 11008 weights (16 rotated sets of 45 MB) and prefill
+    # M = 2048, K = N = 4096 (12 rotated (A, W) sets)
+    K, N, G = DEC_K, DEC_N, DEC_G
+    sets = []
+    for r in range(ROT):
+        _, W, S = qi.w8a16_problem(1, K, N, G, 107 + 1000 * r)
+        sets.append((qg.qgemm_w8a16_prepack(to_dev(W), K, N), to_dev(S)))
+    for M in (1, 8):
+        Ad = to_dev(qi.activations(M, K, 1070 + M))
+        Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        g = graph_of([(lambda w=w: qg.qgemm_w8a16(Ad, w[0], w[1], G, Y=Y)) for w in sets])
+        t = time_graph(g, ROT, reps=20)
+        b = K * N + 2 * (K // G) * N + 2 * M * K + 2 * M * N
+        rows[f"w8a16_decode_M{M}_K{K}_N{N}"] = {"us": round(t * 1e6, 3), "GB/s": round(b / t / 1e9, 1),
+                                                "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] w8a16 decode M={M} {rows[f'w8a16_decode_M{M}_K{K}_N{N}']}")
+    del sets
+    M, K, N, G = 2048, 4096, 4096, 128
+    probs = []
+    for r in range(12):
+        A, W, S = qi.w8a16_problem(M, K, N, G, 108 + 1000 * r)
+        probs.append((to_dev(A), qg.qgemm_w8a16_prepack(to_dev(W), K, N), to_dev(S)))
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    g = graph_of([(lambda p=p: qg.qgemm_w8a16(p[0], p[1], p[2], G, Y=Y)) for p in probs])
+    t = time_graph(g, 12, reps=10)
+    fl = 2 * M * N * K
+    rows["w8a16_prefill_M2048_K4096_N4096"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(fl / t / 1e12, 1),
+                                               "mfma_frac": round(fl / t / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+    log(f"[bench] w8a16 prefill {rows['w8a16_prefill_M2048_K4096_N4096']}")
     return rows
 
 

@@ -73,6 +73,10 @@ def _declare(L):
         "qgemm_w4a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
         "qgemm_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
         "qgemm_w4a16": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+        "qgemm_w8a16_packed_bytes": (_SZ, [_I32, _I32]),
+        "qgemm_w8a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
+        "qgemm_w8a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+        "qgemm_w8a16": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
         "quant_sym_int8": (_I32, [_P, _P, _P, _I32, _I32, _P]),
         "dequant_sym_int8": (_I32, [_P, _P, _P, _I32, _I32, _P]),
         "qgemm_w8a8_epilogue": (_I32, [_P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_uint32, _P, _P,
@@ -92,7 +96,8 @@ def _declare(L):
 EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
            "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
-           "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8")
+           "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
+           "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16")
 
 
 def _ptr(t):
@@ -164,6 +169,49 @@ def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
             workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("qgemm_w4a16", lib().qgemm_w4a16(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
+                                             _ptr(workspace) if ws else None, ws, _stream()))
+    return Y
+
+
+# ---------------------------------------------------------------- W8A16
+
+def qgemm_w8a16_packed_bytes(K, N):
+    return lib().qgemm_w8a16_packed_bytes(K, N)
+
+
+def qgemm_w8a16_prepack(w_natural, K, N, w_frag=None):
+    """Natural int8 weights [K, N] -> int8 fragment-layout bytes uint8 [K*N]."""
+    _need(w_natural, torch.int8, "w_natural")
+    if w_frag is None:
+        w_frag = torch.empty(max(qgemm_w8a16_packed_bytes(K, N), 1), dtype=torch.uint8,
+                             device=w_natural.device)
+    _need(w_frag, torch.uint8, "w_frag")
+    _check("qgemm_w8a16_prepack",
+           lib().qgemm_w8a16_prepack(_ptr(w_natural), _ptr(w_frag), K, N, _stream()))
+    return w_frag
+
+
+def qgemm_w8a16_workspace_bytes(M, N, K, G):
+    return lib().qgemm_w8a16_workspace_bytes(M, N, K, G)
+
+
+def qgemm_w8a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
+    """Y[M, N] = A[M, K] (fp16) x (W * scales), W int8 from w_frag, scales fp16
+    [K/G, N] (G == K: [1, N], one per column).  Workspace as for qgemm_w4a16."""
+    _need(A, torch.float16, "A")
+    _need(w_frag, torch.uint8, "w_frag")
+    _need(scales, torch.float16, "scales")
+    M, K = A.shape
+    N = scales.shape[1] if N is None else N
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    _need(Y, torch.float16, "Y")
+    if workspace is None:
+        need = qgemm_w8a16_workspace_bytes(M, N, K, G)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("qgemm_w8a16", lib().qgemm_w8a16(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
                                              _ptr(workspace) if ws else None, ws, _stream()))
     return Y
 

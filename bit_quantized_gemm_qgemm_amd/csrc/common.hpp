@@ -57,29 +57,6 @@ __device__ __forceinline__ half8 raw8(uint32_t d) {
     return __builtin_bit_cast(half8, r);
 }
 
-// Exact fp16 weights v = (1024 + u) - 1032.
-__device__ __forceinline__ half8 dequant8(uint32_t d) {
-    const _Float16 c = (_Float16)-1032.0f;
-    return raw8(d) + half8{c, c, c, c, c, c, c, c};
-}
-
-// Same, multiplied by a per-column scale (fp16 rounding of q*s).
-__device__ __forceinline__ half8 dequant8_scaled(uint32_t d, _Float16 s) {
-    const half8 s8 = {s, s, s, s, s, s, s, s};
-    return dequant8(d) * s8;
-}
-
-// ---------------------------------------------------------------- fragment layout
-//
-// Weight block = 16 columns x 128 k = 1024 bytes; tile = 8 blocks (128 columns).
-// Block (strip s = n/16, chunk c = k/128) starts at
-//   ((s/8) * (K/128) + c) * 8192 + (s%8) * 1024.
-// Inside a block, lane position p = cl + 16*q (cl = column in strip, q = 0..3)
-// owns 16 bytes at p*16: word kk (0..3) holds k = c*128 + kk*32 + q*8 + j.
-__device__ __forceinline__ size_t frag_block_offset(int strip, int chunk, int kchunks) {
-    return ((size_t)(strip >> 3) * kchunks + chunk) * 8192u + (size_t)(strip & 7) * 1024u;
-}
-
 // Workgroups of a 1-D grid are dispatched round-robin over the eight XCDs
 // (workgroup b runs on XCD b % 8).  xcd_contiguous(b, n) is a bijection of
 // [0, n) that hands each XCD one contiguous run of work items, so items that

@@ -15,7 +15,7 @@
 //               o being the K-split partials added in split order.
 // Every reduction has a fixed order, so the layer is deterministic.
 #include "common.hpp"
-#include "w4_pass.hpp"
+#include "wq_pass.hpp"
 
 namespace {
 
@@ -203,12 +203,12 @@ __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
             else return (uint32_t)(slot0 + r) * (uint32_t)I;
         };
         switch ((R + 31) / 32) {
-            case 1: expert_pass<G, NB, 1, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
-            case 2: expert_pass<G, NB, 2, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
-            case 3: expert_pass<G, NB, 3, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 1: expert_pass<G, NB, 1, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 2: expert_pass<G, NB, 2, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 3: expert_pass<G, NB, 3, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
             default:
                 if constexpr (PASS == 128)
-                    expert_pass<G, NB, 4, MODE>(sA, abase, row_off, R, wf, S, N, kchunks, c0, c1, ncol0, slot0, out);
+                    expert_pass<G, NB, 4, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out);
                 break;
         }
         __syncthreads();  // the next pass refills both LDS buffers

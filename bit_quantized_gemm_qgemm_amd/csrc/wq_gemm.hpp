@@ -1,0 +1,486 @@
+// Weight-only GEMM kernels shared by the int4 (W4A16) and int8 (W8A16)
+// entry points: Y[M,N] = A[M,K] (fp16) x (q * s), q the WB-bit weights of a
+// fragment layout (wq_tile.hpp), s fp16 scales, fp32 accumulation, fp16
+// output.  Three regimes, chosen by M:
+//   decode  (M <= 16): HBM-bound weight stream.  Each wave owns up to NSW
+//       16-column strips and KCW 128-k chunks; it issues every weight, A and
+//       scale load of its slice before its first wait, stages A and scales in
+//       its own LDS slice (no workgroup barrier before the main loop) and runs
+//       v_mfma_f32_16x16x32_f16 on the raw fp16 values 1024 + u; per-group
+//       fp32 partials are corrected and scaled, and the K partials of the
+//       workgroup's waves are added in LDS in a fixed order.
+//   mid (16 < M <= 128, with a workspace): split-K.  A workgroup owns 128
+//       columns and a K range and runs all M rows through them (the
+//       B-stationary pass of the MoE GEMMs), writing fp32 partials; a second
+//       launch adds the splits in a fixed order and rounds to fp16.  A single
+//       pass over K with 128-column tiles would leave most CUs idle (86
+//       workgroups for N = 11008).
+//   prefill (other M > 16): 128x128 output tiles, four waves of 64x64, A
+//       tiles double-buffered through LDS via registers, B fragments read
+//       straight from the fragment layout into registers and dequantized with
+//       the group scale folded in, v_mfma_f32_32x32x16_f16.  The workgroup
+//       index runs column-major over tiles, so the workgroups resident on one
+//       XCD share weight columns in its L2.
+// Scales: row (k / G) of S at element offset (k / G) * ldS; ldS = 0 gives
+// every group row 0, i.e. one scale per column.
+#pragma once
+
+#include "wq_pass.hpp"
+
+namespace {
+
+using namespace qg;
+
+// ------------------------------------------------------------------ decode
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// v plus the value of lane l' of the same 16-lane row, l' given by a DPP
+// control (quad permutation or row mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                     0xf, 0xf, false));
+}
+
+// Sum of v over each aligned group of N adjacent lanes (N = 4, 8 or 16),
+// delivered to every lane of the group: lane ^ 1 and lane ^ 2 (quad
+// permutations) give quad sums, the half-row mirror (lane 7 - i within 8)
+// adds the other quad and the row mirror (lane 15 - i within 16) the other
+// half.  Register moves only, no LDS round trips.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    v = dpp_add<0xB1>(v);                          // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);                          // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
+    if constexpr (N >= 16) v = dpp_add<0x140>(v);  // row_mirror
+    return v;
+}
+
+// Decode kernel for WB-bit weights.  MT = rows of the MFMA A tile that may be
+// non-zero (M <= MT <= 16); each wave owns up to NSW 16-column strips and KCW
+// 128-k chunks (NSW * KCW * P 16-byte weight loads per lane, P = 1 for int4
+// and 2 for int8); WK = 32 / KCW waves cover
+// 4096 k, so a workgroup of WK waves holds its strips over a whole 4096-k
+// block and reduces its K partials in LDS in a fixed order.  With BAL the
+// grid is sized to the chip and each workgroup takes a contiguous range of
+// strips (NSW at most).
+//
+// Everything a wave needs is staged by that wave alone, in its own slice of
+// LDS, so there is no barrier before the main loop: it issues the loads of
+// its A slice (rows < M), of its group scales and then all eight weight
+// loads; while the weights stream in it writes A and the scales to LDS and
+// forms the per-(row, group) constant C = bias * sum_k a_k (bias = 1032 for
+// int4, 1152 for int8).  The MFMAs work on the raw fp16 values 1024 + u
+// (seven VALU ops per eight int4 weights, four per eight int8 weights); each
+// group's fp32 partial T becomes acc += s * (T - C).  One A fragment read from
+// LDS feeds the MFMAs of all NSW strips.
+template <int WB, int MT, int NSW, int KCW, int G, bool BAL>
+__global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ wf, const uint16_t* __restrict__ Sc,
+    int ldS, uint16_t* __restrict__ Y, int M, int N, int K) {
+    constexpr int P = WFormat<WB>::kPieces;
+    constexpr float BIAS = WFormat<WB>::kBias;
+    constexpr int WK = 32 / KCW;                 // waves per workgroup (one 4096-k block)
+    constexpr int KW = KCW * 128;                // k per wave
+    constexpr int LDA = KW + 8;                  // halfs per staged A row (+16 B pad)
+    constexpr int APIECES = MT * KW / 8;         // 16-byte A pieces per wave
+    constexpr int APL = APIECES < 64 ? 1 : APIECES / 64;  // per lane
+    constexpr int NG = 128 / G, KKPG = G / 32;   // groups per chunk, k-steps per group
+    constexpr int GW = KCW * NG;                 // groups per wave
+    constexpr int GP = G / 8;                    // A pieces per group and row
+    constexpr int SPL = GW * NSW * 2;            // 16-byte scale pieces per wave (<= 64)
+    static_assert(APIECES < 64 || APL * 64 == APIECES, "A staging must tile the wave's slice");
+    static_assert(SPL <= 64, "one scale piece per lane");
+    // C = bias * sum_k a_k per (row, group): by VALU during staging, except
+    // for 16-row tiles over several strips, where an extra MFMA per k-step
+    // against a constant bias operand (shared by the strips) is cheaper than
+    // sixteen rows of sums and shuffles (measured: M = 16 8.8 us instead of
+    // 9.6; for M <= 8 the VALU sums are faster)
+    constexpr bool CM = NSW >= 2 && MT >= 16;
+    struct WaveLds {
+        _Float16 a[MT * LDA];
+        float c[GW][16];
+        uint16_t s[GW][NSW * 16];
+    };
+    constexpr size_t RED = sizeof(floatx4) * WK * NSW * 64;  // K-partials for the reduction
+    constexpr size_t STAGE = sizeof(WaveLds) * WK;
+    __shared__ __attribute__((aligned(16))) char lds_raw[STAGE > RED ? STAGE : RED];
+    WaveLds* lds = reinterpret_cast<WaveLds*>(lds_raw);
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    WaveLds& L = lds[wave];
+    // BAL: the workgroups share the N / 16 strips in contiguous ranges of
+    // NSW - 1 or NSW strips (every CU busy when N / 16 is not a multiple of
+    // NSW x 256); a slot past the range repeats its last strip and is not stored
+    int strip0, nst;
+    if constexpr (BAL) {
+        const int wg = xcd_contiguous(blockIdx.x, gridDim.x), nstrips = N / 16;
+        strip0 = (int)((long)wg * nstrips / gridDim.x);
+        nst = (int)((long)(wg + 1) * nstrips / gridDim.x) - strip0;
+    } else {
+        strip0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSW;
+        nst = NSW;
+    }
+    const int cl = lane & 15, q = lane >> 4;
+    const int kchunks = K / 128;
+    const int arow = cl & (MT - 1);  // rows >= MT of the MFMA tile are never stored
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[NSW];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) acc[s] = zero;
+
+    for (int kb0 = 0; kb0 < K; kb0 += 4096) {
+        const int kw0 = kb0 + wave * KW;             // first k of this wave
+        const int kwl = K - kw0 < KW ? K - kw0 : KW;  // k of this wave in this block (may be <= 0)
+        // Loads, in the order they are needed: A, scales, weights.  Every load
+        // is unconditional (out-of-range requests are clamped to valid data
+        // that is never used): a load under a branch makes the compiler wait
+        // for all outstanding loads at the join, which would serialize the
+        // weight stream behind the staging.  Rows >= M repeat row M-1; they
+        // only feed accumulator rows that are never stored.
+        uintx4 ast[APL];
+#pragma unroll
+        for (int p = 0; p < APL; ++p) {
+            const int idx = lane + 64 * p;
+            const int row = idx / (KW / 8) < M ? idx / (KW / 8) : M - 1;
+            const int c8 = (idx < APIECES && (idx % (KW / 8)) * 8 < kwl) ? idx % (KW / 8) : 0;
+            ast[p] = *reinterpret_cast<const uintx4*>(A + (size_t)row * K + kw0 * (kwl > 0) + c8 * 8);
+        }
+        const int sp_g = lane / (NSW * 2), sp_r = lane % (NSW * 2);  // group, 8-column piece
+        const bool sp_ok = lane < SPL && sp_g * G < kwl && sp_r < 2 * nst;
+        const uintx4 sreg = *reinterpret_cast<const uintx4*>(
+            Sc + (sp_ok ? (size_t)(kw0 / G + sp_g) * ldS + strip0 * 16 + sp_r * 8 : 0));
+        uintx4 braw[KCW][NSW][P];
+#pragma unroll
+        for (int i = 0; i < KCW; ++i)
+#pragma unroll
+            for (int s = 0; s < NSW; ++s) {
+                const int c = i * 128 < kwl ? kw0 / 128 + i : 0;
+                const uint8_t* blk = wf + wblock_offset<WB>(strip0 + (s < nst ? s : nst - 1), c, kchunks);
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    braw[i][s][p] = ldg_nt(reinterpret_cast<const uintx4*>(blk + p * 1024 + lane * 16));
+            }
+        // keep every load above ahead of the first use of any of them
+        __builtin_amdgcn_sched_barrier(0);
+        // stage A and C; rows < MT only, pieces of a (row, group) sit in GP adjacent lanes
+#pragma unroll
+        for (int p = 0; p < APL; ++p) {
+            const int idx = lane + 64 * p, row = idx / (KW / 8), c8 = idx % (KW / 8);
+            // (Whole-vector bit casts only: a bit cast of one element of a
+            // u32x4 was miscompiled by this toolchain into element 0.)
+            const half8 h = __builtin_bit_cast(half8, ast[p]);
+            if constexpr (CM) {
+                if (idx < APIECES) *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
+            } else {
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) part += (float)h[j];
+                part = group_sum<GP>(part);
+                if (idx < APIECES) {
+                    *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
+                    if (c8 % GP == 0) L.c[c8 / GP][row] = part * BIAS;
+                }
+            }
+        }
+        if (lane < SPL) *reinterpret_cast<uintx4*>(&L.s[sp_g][sp_r * 8]) = sreg;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < KCW; ++i) {
+            if (i * 128 >= kwl) break;
+            const _Float16* ap = L.a + arow * LDA + i * 128 + q * 8;
+            half8 a[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const half8*>(ap + kk * 32);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int gl = i * NG + g;
+                floatx4 cc;
+                if constexpr (CM) {
+                    const _Float16 kb = (_Float16)BIAS;
+                    const half8 cb = {kb, kb, kb, kb, kb, kb, kb, kb};
+                    cc = zero;
+#pragma unroll
+                    for (int kk = g * KKPG; kk < (g + 1) * KKPG; ++kk) cc = mfma16(a[kk], cb, cc);
+                } else {
+                    cc = *reinterpret_cast<const floatx4*>(&L.c[gl][4 * q]);
+                }
+#pragma unroll
+                for (int s = 0; s < NSW; ++s) {
+                    floatx4 tmp = zero;
+#pragma unroll
+                    for (int kk = g * KKPG; kk < (g + 1) * KKPG; ++kk)
+                        tmp = mfma16(a[kk], raw_kstep<WB>(braw[i][s], kk), tmp);
+                    const float sv = h2f(L.s[gl][s * 16 + cl]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[s][j] = __builtin_fmaf(tmp[j] - cc[j], sv, acc[s][j]);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // K partials of the workgroup's strips, added in wave order
+    __syncthreads();
+    floatx4* red = reinterpret_cast<floatx4*>(lds_raw);
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) red[(wave * NSW + s) * 64 + lane] = acc[s];
+    __syncthreads();
+    // wave w < NSW finalizes strip w
+    if (wave < nst) {
+        floatx4 t = red[wave * 64 + lane];
+        for (int w = 1; w < WK; ++w) t += red[(w * NSW + wave) * 64 + lane];
+        const int n = (strip0 + wave) * 16 + cl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 4 * q + j;  // accumulator layout: rows 4*(l/16)+j, column l%16
+            if (row < M) Y[(size_t)row * N + n] = f2h(t[j]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ prefill
+
+constexpr int PF_BM = 128, PF_BN = 128, PF_LDA = 136;  // LDS row: 128 halfs + 8 pad
+
+template <int WB, int G>
+__global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ wf,
+                                                            const uint16_t* __restrict__ S, int ldS,
+                                                            uint16_t* __restrict__ Y, int M, int N,
+                                                            int K) {
+    typedef BChunk<2, G, WB> Chunk;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][PF_BM * PF_LDA];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    // tile (x, y) of workgroup id L: y = L % (row tiles), see the large kernel
+    const int mtiles = (M + PF_BM - 1) / PF_BM;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * PF_BM, n0 = (L / mtiles) * PF_BN;
+    const int kchunks = K / 128;
+    const int h = lane >> 5, c32 = lane & 31;
+    const int ncol0 = n0 + wn * 64;
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
+
+    // A staging: 128 rows x 256 bytes = 2048 pieces of 16 bytes, 8 per thread.
+    uintx4 areg[8];
+    auto load_a = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
+            const int gm = m0 + row;
+            // rows >= M repeat row M-1 (unconditional load; those rows are not stored)
+            areg[i] = *reinterpret_cast<const uintx4*>(A + (size_t)(gm < M ? gm : M - 1) * K + c * 128 + col * 8);
+        }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
+            *reinterpret_cast<uintx4*>(&sA[buf][row * PF_LDA + col * 8]) = areg[i];
+        }
+    };
+
+    auto compute = [&](const uint16_t* sa, const Chunk& b) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int kg = kgroup_of_step(s, h);
+            half8 a[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const half8*>(&sa[(wm * 64 + i * 32 + c32) * PF_LDA + kg * 8]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G, WB>(b, t, s);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
+        }
+    };
+
+    // Two B register sets used alternately (no copies), two chunks per trip
+    // and no branch inside a trip: a load under a branch, a load issued
+    // before a branch but used only after it, or a register copy of in-flight
+    // data makes the compiler wait for the prefetch before computing.  The
+    // scheduling barriers keep the prefetch loads ahead of the compute.  The
+    // last trip reloads its second chunk when the count is even; an odd count
+    // leaves one staged chunk for the tail.
+    Chunk b0, b1;
+    load_a(0);
+    load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, 0, ncol0, lane);
+    store_a(0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < kchunks; c += 2) {
+        load_a(c + 1);
+        load_b_chunk<2, G, WB>(b1, wf, S, ldS, kchunks, c + 1, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA[0], b0);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(1);
+        __syncthreads();
+        const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
+        load_a(c2);
+        load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, c2, ncol0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sA[1], b1);
+        __builtin_amdgcn_sched_barrier(0);
+        store_a(0);
+        __syncthreads();
+    }
+    if (c < kchunks) compute(sA[0], b0);
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = ncol0 + t * 32 + c32;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int row = m0 + wm * 64 + i * 32 + acc_row(j, lane);
+                if (row < M) Y[(size_t)row * N + col] = f2h(acc[i][t][j]);
+            }
+        }
+}
+
+// ------------------------------------------------------------------ mid M
+
+// measured crossover: at M = 192 and 256 the two row passes re-stream the
+// weights and the single-pass prefill kernel is faster (47 us against 52 / 63
+// at N = 11008, K = 4096)
+constexpr int MID_MAX_M = 128;
+
+// K splits of the mid-M path: as many 128-column x K-range workgroups as fit
+// in one round at two per CU (a 513th workgroup would double the time), at
+// least one chunk each.
+__host__ __device__ inline int mid_splits(int N, int K) {
+    const int tiles = N / 128, kchunks = K / 128;
+    int s = 512 / tiles;
+    if (s > kchunks) s = kchunks;
+    if (s > 16) s = 16;
+    return s < 1 ? 1 : s;
+}
+
+__host__ __device__ inline size_t mid_workspace_bytes(int M, int N, int K) {
+    return (size_t)mid_splits(N, K) * M * N * sizeof(float);
+}
+
+// Workgroup L: column tile L % tiles (consecutive ids, which the dispatcher
+// spreads over the XCDs, take neighbouring tiles), K split L / tiles over
+// chunks [ks * kc / S, (ks + 1) * kc / S).  part[ks][m][n] fp32.
+template <int WB, int G>
+__global__ __launch_bounds__(256, 2) void wq_mid_kernel(const uint16_t* __restrict__ A,
+                                                        const uint8_t* __restrict__ wf,
+                                                        const uint16_t* __restrict__ S, int ldS,
+                                                        float* __restrict__ part, int M, int N, int K,
+                                                        int splits) {
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * XP_SLAB];
+    const int tiles = N / 128, kchunks = K / 128;
+    const int ct = blockIdx.x % tiles, ks = blockIdx.x / tiles;
+    const int c0 = (int)((long)ks * kchunks / splits), c1 = (int)((long)(ks + 1) * kchunks / splits);
+    const uint8_t* wfp[1] = {wf};
+    const uint16_t* sp[1] = {S};
+    const int ncol0 = ct * 128 + (threadIdx.x >> 6) * 32;
+    float* out = part + (size_t)ks * M * N;
+    for (int r0 = 0; r0 < M; r0 += 128) {
+        const int R = M - r0 < 128 ? M - r0 : 128;
+        // element offset of A row r of this pass (M * K < 2^32 is checked at launch)
+        auto row_off = [&](int r) -> uint32_t { return (uint32_t)(r0 + r) * (uint32_t)K; };
+        switch ((R + 31) / 32) {
+            case 1: expert_pass<G, 1, 1, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            case 2: expert_pass<G, 1, 2, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            case 3: expert_pass<G, 1, 3, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            default: expert_pass<G, 1, 4, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+        }
+        __syncthreads();  // the next pass refills both LDS buffers
+    }
+}
+
+// Y[i] = fp16(sum over splits s = 0 .. S-1 of part[s][i]), s ascending; eight
+// outputs per lane per step, grid-stride.
+__global__ __launch_bounds__(256) void wq_splitk_reduce_kernel(const float* __restrict__ part,
+                                                               uint16_t* __restrict__ Y, size_t n8,
+                                                               size_t stride_s, int splits) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n8; c += stride) {
+        const float* p = part + c * 8;
+        floatx4 lo = *reinterpret_cast<const floatx4*>(p);
+        floatx4 hi = *reinterpret_cast<const floatx4*>(p + 4);
+        for (int s = 1; s < splits; ++s) {
+            lo += *reinterpret_cast<const floatx4*>(p + s * stride_s);
+            hi += *reinterpret_cast<const floatx4*>(p + s * stride_s + 4);
+        }
+        const uintx4 o = {(uint32_t)f2h(lo[0]) | ((uint32_t)f2h(lo[1]) << 16),
+                          (uint32_t)f2h(lo[2]) | ((uint32_t)f2h(lo[3]) << 16),
+                          (uint32_t)f2h(hi[0]) | ((uint32_t)f2h(hi[1]) << 16),
+                          (uint32_t)f2h(hi[2]) | ((uint32_t)f2h(hi[3]) << 16)};
+        *reinterpret_cast<uintx4*>(Y + c * 8) = o;
+    }
+}
+
+// One launch of the decode kernel for M <= 16.
+// (MT, NSW, KCW): rows of the MFMA tile, 16-column strips per wave, 128-k
+// chunks per wave; the workgroup is 32 / KCW waves over NSW strips.
+template <int WB, int G>
+void launch_wq_decode(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
+                      int N, int K, hipStream_t st) {
+    if (M == 1)
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
+                           S, ldS, Y, M, N, K);
+    else if (M == 2)
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
+                           S, ldS, Y, M, N, K);
+    else {
+        // at least one workgroup per CU where there are enough strips,
+        // each over a contiguous range of at most three strips
+        const int nstrips = N / 16;
+        int nwg = nstrips < 256 ? nstrips : 256;
+        if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
+        if (M <= 4)
+            hipLaunchKernelGGL((wq_decode_kernel<WB, 4, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf,
+                               S, ldS, Y, M, N, K);
+        else if (M <= 8)
+            hipLaunchKernelGGL((wq_decode_kernel<WB, 8, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf,
+                               S, ldS, Y, M, N, K);
+        else
+            hipLaunchKernelGGL((wq_decode_kernel<WB, 16, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A,
+                               wf, S, ldS, Y, M, N, K);
+    }
+}
+
+template <int WB, int G>
+void launch_wq_prefill(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
+                       int N, int K, hipStream_t st) {
+    dim3 grid((N / PF_BN) * ((M + PF_BM - 1) / PF_BM));
+    hipLaunchKernelGGL((wq_prefill_kernel<WB, G>), grid, dim3(256), 0, st, A, wf, S, ldS, Y, M, N, K);
+}
+
+template <int WB, int G>
+void launch_wq_mid(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
+                   int N, int K, float* part, hipStream_t st) {
+    const int splits = mid_splits(N, K);
+    hipLaunchKernelGGL((wq_mid_kernel<WB, G>), dim3((N / 128) * splits), dim3(256), 0, st, A, wf, S, ldS,
+                       part, M, N, K, splits);
+    const size_t n8 = (size_t)M * N / 8, want = (n8 + 255) / 256;
+    hipLaunchKernelGGL(wq_splitk_reduce_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
+                       part, Y, n8, (size_t)M * N, splits);
+}
+
+// Shapes the mid-M path takes (given enough workspace).
+inline bool mid_path(int M, int K) {
+    return M > 16 && M <= MID_MAX_M && (size_t)M * K < ((size_t)1 << 32);
+}
+
+}  // namespace

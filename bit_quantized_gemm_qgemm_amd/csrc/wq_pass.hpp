@@ -1,5 +1,6 @@
-// B-stationary W4A16 pass shared by the MoE grouped GEMMs and the mid-M
-// split-K GEMM: a workgroup of four waves owns 128 columns of NB weight
+// B-stationary weight-only pass (int4 or int8 weights, WB bits) shared by
+// the MoE grouped GEMMs and the mid-M split-K GEMMs: a workgroup of four
+// waves owns 128 columns of NB weight
 // matrices (wave w: columns 32w .. 32w + 31) and runs R <= 128 rows of A
 // through them over the 128-k chunks c0 .. c1 - 1, so each weight byte of
 // its range is read once.  A rows reach LDS by global -> LDS DMA, double-
@@ -8,7 +9,7 @@
 // for all NRB 32-row MFMA blocks (v_mfma_f32_32x32x16_f16).
 #pragma once
 
-#include "w4_tile.hpp"
+#include "wq_tile.hpp"
 
 namespace qg {
 
@@ -18,12 +19,14 @@ constexpr int XP_SLAB = 128 * 128;  // halfs per LDS A buffer: 128 rows of 128 k
 // MODE 1: out[slot][n] = the fp32 partial sum over the pass's chunk range
 // (the K splits of the MoE down projection and of the mid-M GEMM).
 // slot0 + row indexes the output row; row_off(r) is the element offset of
-// A row r of the pass from abase.
-template <int G, int NB, int NRB, int MODE, typename RowOff>
+// A row r of the pass from abase.  N is the row stride of out, ldS that of
+// the scales (0: one scale per column).
+template <int G, int NB, int NRB, int MODE, int WB, typename RowOff>
 __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowOff row_off, int R,
                                             const uint8_t* const* wf, const uint16_t* const* S,
-                                            int N, int kchunks, int c0, int c1, int ncol0,
+                                            int N, int ldS, int kchunks, int c0, int c1, int ncol0,
                                             int slot0, void* out) {
+    typedef BChunk<1, G, WB> Chunk;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, c32 = lane & 31;
     floatx16 acc[NB][NRB];
@@ -50,15 +53,15 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
             __builtin_amdgcn_global_load_lds(abase + src[j] + c * 128,
                                              sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, 16, 0, 0);
     };
-    auto load_b = [&](BChunk<1, G>* bs, int c) {
+    auto load_b = [&](Chunk* bs, int c) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) load_b_chunk<1, G>(bs[b], wf[b], S[b], N, kchunks, c, ncol0, lane);
+        for (int b = 0; b < NB; ++b) load_b_chunk<1, G, WB>(bs[b], wf[b], S[b], ldS, kchunks, c, ncol0, lane);
     };
     // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
     // are interleaved with the MFMAs of step s (one MFMA, then at most one
     // LDS read and a share of the dequant VALU ops), so the wave keeps the
     // MFMA unit busy while it prepares the next operands.
-    auto operands = [&](const uint16_t* sa, const BChunk<1, G>* bs, int s, half8 (&a)[NRB],
+    auto operands = [&](const uint16_t* sa, const Chunk* bs, int s, half8 (&a)[NRB],
                         half8 (&bf)[NB]) {
         const int kg = kgroup_of_step(s, h);
 #pragma unroll
@@ -67,11 +70,12 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
             a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G>(bs[b], 0, s);
+        for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G, WB>(bs[b], 0, s);
     };
     constexpr int NM = NB * NRB;                 // MFMAs per k-step
-    constexpr int VPER = (15 * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
-    auto compute = [&](const uint16_t* sa, const BChunk<1, G>* bs) {
+    constexpr int VB = WB == 4 ? 15 : 12;        // dequant VALU ops per B fragment
+    constexpr int VPER = (VB * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
+    auto compute = [&](const uint16_t* sa, const Chunk* bs) {
         half8 a[NRB], bf[NB];
         operands(sa, bs, 0, a, bf);
 #pragma unroll
@@ -105,7 +109,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     // issues the next DMA.  Two trips per loop pass keep the buffer indices
     // literals; the prefetch past the last chunk reloads the last chunk and
     // an odd chunk count leaves one chunk, already staged, for the tail.
-    BChunk<1, G> b0[NB], b1[NB];
+    Chunk b0[NB], b1[NB];
     const int last = c1 - 1;
     dma_a(c0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -113,7 +117,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    auto trip = [&](int c, int abuf, const BChunk<1, G>* bc, BChunk<1, G>* bn) __attribute__((always_inline)) {
+    auto trip = [&](int c, int abuf, const Chunk* bc, Chunk* bn) __attribute__((always_inline)) {
         const int cn = c + 1 < c1 ? c + 1 : last;
         dma_a(cn, abuf ^ 1);
         __builtin_amdgcn_sched_barrier(0);

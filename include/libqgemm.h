@@ -113,6 +113,52 @@ QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const ui
                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * W8A16 weight-only int8 GEMM  (FP8 vs INT8 low-precision inference in
+ * TensorRT-LLM, itzkxy.com: weight-only int8 with fp16 activations is one of
+ * the INT8 configurations compared; the page leaves the scale granularity
+ * open, and this version takes group-wise or per-column fp16 scales).
+ *
+ *   Y[m][n] = fp16( sum_k A[m][k] * W[k][n] * S[k/G][n] )
+ *
+ * Natural weight format: int8 [K][N] (two's complement, full range
+ * [-128, 127]).  G = K means one scale per column (S is fp16 [1][N]).
+ *
+ * Supported in this version: K % 128 == 0, N % 128 == 0, G in {32, 64, 128}
+ * or G == K; other shapes return QGEMM_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of the int8 fragment-layout buffer for a K x N matrix (= K*N); 0 if
+   the shape is unsupported. */
+QGEMM_API size_t qgemm_w8a16_packed_bytes(int32_t K, int32_t N);
+
+/* Repack natural int8 weights into the library's int8 fragment layout.
+   w_natural: int8 [K][N] (input, not modified).
+   w_frag:    uint8 [qgemm_w8a16_packed_bytes(K, N)] (output); must not
+              overlap w_natural.
+   Run once per weight matrix; the layout is only consumed by qgemm_w8a16. */
+QGEMM_API int32_t qgemm_w8a16_prepack(const int8_t* w_natural, uint8_t* w_frag, int32_t K, int32_t N,
+                                      void* stream);
+
+/* Workspace bytes qgemm_w8a16 uses for this shape: the same rule as
+   qgemm_w4a16_workspace_bytes (split-K partials for 16 < M <= 128, else 0;
+   0 for invalid arguments). */
+QGEMM_API size_t qgemm_w8a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
+
+/* Y = A x (W * S).
+   A:      fp16 [M][K] activations.
+   w_frag: prepacked weights from qgemm_w8a16_prepack(K, N).
+   scales: fp16 [K/G][N] ([1][N] for G == K).
+   Y:      fp16 [M][N] output; must not overlap the inputs.
+   workspace: as for qgemm_w4a16.  M <= 16 runs the memory-bound decode
+   kernel, 16 < M <= 128 with enough workspace the split-K kernel, every
+   other M the MFMA prefill kernel; all compute the same function (fp32
+   accumulation, one rounding to fp16) and are deterministic.  Calls sharing
+   one workspace must not overlap. */
+QGEMM_API int32_t qgemm_w8a16(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales, uint16_t* Y,
+                              int32_t M, int32_t N, int32_t K, int32_t G, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Symmetric int8 quantization, one scale per row  (INT8 cross-modal MHA
  * TensorRT plugin interview page, answer step 1: scale = 127 / max|x| per
  * output channel of the weights and per token of the activations, and

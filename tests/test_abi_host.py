@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
         "qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
         "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
         "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
-        "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8"])
+        "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
+        "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -93,6 +94,32 @@ def test_w4a16_validation(L):
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 256, 256, None, 0, None) == 5  # G = 256
     assert f(FAKE + 2, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 3
     assert f(FAKE, FAKE, FAKE, FAKE + 8, 4, 128, 128, 128, None, 0, None) == 3
+
+
+def test_w8a16_size_queries_and_validation(L):
+    assert L.qgemm_w8a16_packed_bytes(4096, 11008) == 4096 * 11008
+    assert L.qgemm_w8a16_packed_bytes(4000, 11008) == 0
+    for M, N, K, G in [(17, 11008, 4096, 128), (64, 11008, 4096, 4096), (128, 256, 256, 64)]:
+        S = max(1, min(512 // (N // 128), K // 128, 16))
+        assert L.qgemm_w8a16_workspace_bytes(M, N, K, G) == S * M * N * 4, (M, N, K, G)
+    assert L.qgemm_w8a16_workspace_bytes(8, 11008, 4096, 128) == 0
+    assert L.qgemm_w8a16_workspace_bytes(64, 11008, 4096, 256) == 0  # G neither <= 128 nor K
+    f = L.qgemm_w8a16
+    assert f(None, None, None, None, 0, 128, 128, 128, None, 0, None) == 0
+    assert f(None, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, -128, 128, 128, None, 0, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 384, 256, None, 0, None) == 2  # G does not divide K
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 256, None, 0, None) == 5  # G = 256 < K
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 200, 200, None, 0, None) == 5  # K % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 96, 128, 128, None, 0, None) == 5   # N % 128
+    assert f(FAKE, FAKE, FAKE + 2, FAKE, 4, 128, 128, 128, None, 0, None) == 3
+    p = L.qgemm_w8a16_prepack
+    assert p(None, FAKE, 128, 128, None) == 1
+    assert p(FAKE, FAKE, 128, 0, None) == 0
+    assert p(FAKE, FAKE, -128, 128, None) == 2
+    assert p(FAKE, FAKE, 128, 192, None) == 5
+    assert p(FAKE + 4, FAKE + 65536, 128, 128, None) == 3
+    assert p(FAKE, FAKE + 8192, 128, 128, None) == 2  # overlapping buffers
 
 
 def test_prepack_validation(L):

@@ -1,0 +1,163 @@
+"""GPU parity of the weight-only int8 GEMM (W8A16) against the CPU oracle.
+
+Bars: the int8 prepack is bit-exact; fp16 outputs within
+|y - y_ref| <= 1e-2 |y_ref| + 1e-3 max|y_ref| of the oracle's fp64 result;
+repeated calls are bit-identical.  Every regime (decode M <= 16, mid-M
+split-K, 128x128 prefill) runs with group sizes 32, 64, 128 and with one
+scale per column (G = K), on ragged M and K counts that leave partial
+tiles, and on the decode / prefill benchmark shapes (sampled outputs).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qgemm_inputs as qi
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qg():
+    import bit_quantized_gemm_qgemm_amd as qg
+    if not os.path.exists(qg.LIB_PATH):
+        from bit_quantized_gemm_qgemm_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qg.lib()
+    return qg
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits(a):
+    return np.asarray(a).view(np.uint16)
+
+
+def assert_fp16_close(y, ref, what=""):
+    y64 = y.astype(np.float64)
+    r64 = ref.astype(np.float64)
+    assert np.all(np.isfinite(y64)), f"{what}: non-finite outputs"
+    bound = 1e-2 * np.abs(r64) + 1e-3 * np.abs(r64).max()
+    err = np.abs(y64 - r64)
+    bad = err > bound
+    if bad.any():
+        i = np.argmax(err - bound)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst at flat "
+                             f"{i}: got {y64.ravel()[i]} want {r64.ravel()[i]} bound {bound.ravel()[i]}")
+
+
+def gsize(G, K):
+    return K if G == "K" else G
+
+
+def run(qg, A, W, S, G, workspace=None):
+    K, N = W.shape
+    Wf = qg.qgemm_w8a16_prepack(dev(W), K, N)
+    return host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G, workspace=workspace))
+
+
+@pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (512, 512), (4096, 11008)])
+def test_w8a16_prepack_bytes_match_oracle(qg, K, N):
+    W = qi.w8a16_problem(1, K, N, 128, 600 + K + N)[1]
+    got = host(qg.qgemm_w8a16_prepack(dev(W), K, N))
+    assert np.array_equal(got, oracle.w8a16_prepack(W, K, N))
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, "K"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16])
+def test_w8a16_decode_small(qg, M, G):
+    K, N = 512, 512
+    G = gsize(G, K)
+    A, W, S = qi.w8a16_problem(M, K, N, G, 610 + M + G)
+    assert_fp16_close(run(qg, A, W, S, G), oracle.w8a16(A, W, S, G), f"M={M} G={G}")
+
+
+@pytest.mark.parametrize("G", [64, "K"])
+@pytest.mark.parametrize("K", [128, 1152, 4224])
+def test_w8a16_decode_ragged_k(qg, K, G):
+    # K/128 chunks not a multiple of the waves per 4096-k block (1, 9, 33 chunks)
+    G = gsize(G, K)
+    for M in (1, 3, 9):
+        A, W, S = qi.w8a16_problem(M, K, 256, G, 620 + K + M)
+        assert_fp16_close(run(qg, A, W, S, G), oracle.w8a16(A, W, S, G), f"M={M} K={K} G={G}")
+
+
+def test_w8a16_extreme_weights(qg):
+    # every weight -128 or 127 (the ends of the offset-binary range) in a column pattern
+    M, K, N, G = 20, 256, 256, 64
+    A, _, S = qi.w8a16_problem(M, K, N, G, 630)
+    W = np.where((np.arange(K)[:, None] + np.arange(N)[None, :]) % 3 == 0, -128, 127).astype(np.int8)
+    ref = oracle.w8a16(A, W, S, G)
+    for Mx in (1, 4, 16, 20):
+        assert_fp16_close(run(qg, A[:Mx], W, S, G), ref[:Mx], f"extreme M={Mx}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_w8a16_decode_full_shape(qg, M):
+    K, N, G = 4096, 11008, 128
+    _, W, S = qi.w8a16_problem(1, K, N, G, 640)
+    A = qi.activations(M, K, 641 + M)
+    assert_fp16_close(run(qg, A, W, S, G), oracle.w8a16(A, W, S, G), f"M={M} K=4096 N=11008")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, "K"])
+@pytest.mark.parametrize("M,K,N", [(17, 1152, 256), (64, 512, 384), (100, 896, 256), (128, 384, 512),
+                                   (33, 256, 128)])
+def test_w8a16_mid_m_split_k(qg, M, K, N, G):
+    G = gsize(G, K)
+    A, W, S = qi.w8a16_problem(M, K, N, G, 650 + M + K + G)
+    assert qg.qgemm_w8a16_workspace_bytes(M, N, K, G) > 0
+    ref = oracle.w8a16(A, W, S, G)
+    assert_fp16_close(run(qg, A, W, S, G), ref, f"split-K M={M} K={K} N={N} G={G}")
+    empty = torch.empty(0, dtype=torch.uint8, device="cuda")
+    assert_fp16_close(run(qg, A, W, S, G, workspace=empty), ref, f"no workspace M={M} G={G}")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, "K"])
+@pytest.mark.parametrize("M,K,N", [(129, 512, 256), (300, 384, 384), (600, 256, 512), (1100, 128, 256)])
+def test_w8a16_prefill(qg, M, K, N, G):
+    G = gsize(G, K)
+    A, W, S = qi.w8a16_problem(M, K, N, G, 660 + M + K + G)
+    assert_fp16_close(run(qg, A, W, S, G), oracle.w8a16(A, W, S, G), f"M={M} K={K} N={N} G={G}")
+
+
+def test_w8a16_mid_m_full_shape_sampled(qg):
+    M, K, N = 64, 4096, 11008
+    G = K
+    _, W, S = qi.w8a16_problem(1, K, N, G, 670)
+    A = qi.activations(M, K, 671)
+    Wf = qg.qgemm_w8a16_prepack(dev(W), K, N)
+    Y = host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G))
+    ms, ns = qi.sample_positions(M, N, 3000, 13)
+    assert_fp16_close(Y[ms, ns], oracle.w8a16_at(A, W, S, G, ms, ns), "split-K M=64, per column")
+    assert np.array_equal(bits(host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G))), bits(Y))
+
+
+def test_w8a16_prefill_full_shape_sampled(qg):
+    M, K, N, G = 2048, 4096, 4096, 128
+    A, W, S = qi.w8a16_problem(M, K, N, G, 680)
+    Wf = qg.qgemm_w8a16_prepack(dev(W), K, N)
+    Y = host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G))
+    ms, ns = qi.sample_positions(M, N, 6000, 14)
+    assert_fp16_close(Y[ms, ns], oracle.w8a16_at(A, W, S, G, ms, ns), "M=2048 sampled")
+    rows = np.full(N, 777, np.int32), np.arange(N, dtype=np.int32)
+    assert_fp16_close(Y[777], oracle.w8a16_at(A, W, S, G, *rows), "M=2048 row")
+    assert np.array_equal(bits(host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G))), bits(Y))
+
+
+def test_w8a16_zero_m_is_noop(qg):
+    _, W, S = qi.w8a16_problem(1, 128, 128, 128, 690)
+    Y = torch.full((1, 128), 7.0, dtype=torch.float16, device="cuda")
+    A = torch.zeros((0, 128), dtype=torch.float16, device="cuda")
+    qg.qgemm_w8a16(A, qg.qgemm_w8a16_prepack(dev(W), 128, 128), dev(S), 128, Y=Y[:0])
+    assert float(host(Y).astype(np.float32).min()) == 7.0
