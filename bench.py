@@ -52,7 +52,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-rows", action="store_true", help="skip the other hot-path rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -102,9 +102,16 @@ def main():
                 f()
         return g
 
-    def time_graph(g, launches, reps, warmup=3):
-        for _ in range(warmup):
+    def time_graph(g, launches, reps, warm_s=0.05):
+        # untimed replays for at least warm_s seconds first: the shader clock
+        # takes tens of milliseconds of load to settle (an MFMA-bound GEMM ran
+        # 15 % slower in its first 50 ms than afterwards)
+        t0, n = time.perf_counter(), 0
+        while n < 3 or time.perf_counter() - t0 < warm_s:
             g.replay()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
