@@ -78,6 +78,8 @@ def _declare(lib):
         "qo_dequant_fp8": (None, [_P, _P, _P, _I64, _I32, _I32]),
         "qo_fp8_gemm": (None, [_P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32]),
         "qo_fp8_gemm_at": (None, [_P, _P, _P, _I32, _P, _I32, _I64, _P, _P, _P, _I32]),
+        "qo_mha_int8_probs": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _F32, _P, _P, _P]),
+        "qo_mha_int8_out": (None, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _F32, _F32, _U32, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -405,3 +407,53 @@ def moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=None, want_f64=False)
                    _ptr(Sd), _ptr(Y), _ptr(Y64), _ptr(ids), _ptr(w), T, H, I, E, topK, G,
                    _ptr(tok), 0 if tok is None else tok.size)
     return (Y, ids, w, Y64) if want_f64 else (Y, ids, w)
+
+
+# ---------------------------------------------------------------- INT8 attention chain
+
+def _heads(heads, B, H):
+    heads = np.arange(B * H, dtype=np.int32) if heads is None else np.asarray(heads, np.int32)
+    assert heads.ndim == 1 and (heads.size == 0 or (heads.min() >= 0 and heads.max() < B * H))
+    return _c(heads, np.int32)
+
+
+def mha_int8_probs(Q, K, alpha, heads=None):
+    """S int32, P int8 and R = 127 p (fp64), each [len(heads), Lq, Lk], for the listed heads
+    (b * H + h; default all) of Q [B, Lq, H, D], K [B, Lk, H, D] int8."""
+    Q = _c(Q, np.int8)
+    K = _c(K, np.int8)
+    B, Lq, H, D = Q.shape
+    Lk = K.shape[1]
+    assert K.shape == (B, Lk, H, D)
+    hs = _heads(heads, B, H)
+    S = np.empty((hs.size, Lq, Lk), np.int32)
+    P = np.empty((hs.size, Lq, Lk), np.int8)
+    R = np.empty((hs.size, Lq, Lk), np.float64)
+    _load().qo_mha_int8_probs(_ptr(Q), _ptr(K), _ptr(hs), hs.size, H, Lq, Lk, D, float(np.float32(alpha)),
+                              _ptr(S), _ptr(P), _ptr(R))
+    return S, P, R
+
+
+def mha_int8_out(P, V, bias, pv_scale, out_mult, flags, Lq, heads=None, O=None):
+    """O int8 [B, Lq, H, D] of the listed heads from their probabilities P [len(heads), Lq, Lk];
+    other heads of O (zeros when O is None) are left as they are."""
+    V = _c(V, np.int8)
+    B, Lk, H, D = V.shape
+    hs = _heads(heads, B, H)
+    P = _c(P, np.int8)
+    assert P.shape == (hs.size, Lq, Lk)
+    bias = _c(np.zeros(H * D, np.float16) if bias is None else bias, np.float16)
+    assert bias.size == H * D
+    if O is None:
+        O = np.zeros((B, Lq, H, D), np.int8)
+    O = _c(O, np.int8)
+    _load().qo_mha_int8_out(_ptr(P), _ptr(V), _ptr(bias), _ptr(hs), hs.size, H, Lq, Lk, D,
+                            float(np.float32(pv_scale)), float(np.float32(out_mult)), int(flags), _ptr(O))
+    return O
+
+
+def mha_int8(Q, K, V, bias, alpha, pv_scale, out_mult, flags, heads=None):
+    """The whole chain: (O, S, P, R) for the listed heads (O holds zeros for the others)."""
+    S, P, R = mha_int8_probs(Q, K, alpha, heads)
+    O = mha_int8_out(P, V, bias, pv_scale, out_mult, flags, Q.shape[1], heads)
+    return O, S, P, R

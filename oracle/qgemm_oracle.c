@@ -30,7 +30,8 @@
  *        (cms365.cn): knowledge points 1-2 (INT8 data path; per-channel and
  *        per-token symmetric quantization; rescale + bias + GELU, then
  *        requantize), answer step 1 (scale = 127 / max|x|), knowledge point 5
- *        (saturation to [-127, 127]).
+ *        (saturation to [-127, 127]), answer steps 2-3 (the attention chain:
+ *        QK^T, int8 softmax, P.V, requantization with bias).
  *   [P2] FP8 vs INT8 low-precision inference in TensorRT-LLM (itzkxy.com):
  *        FP8 E4M3 for GEMMs and the KV cache, per-tensor scaling factors
  *        derived from the activation A-max; the INT8 configurations it
@@ -664,4 +665,84 @@ QO_API void qo_fp8_gemm_at(const uint8_t* A, const uint8_t* W, const float* sa, 
         const double acc = qo_fp8_dot(A + (int64_t)m * K, W + (int64_t)n * K, K);
         Y[i] = qo_f64_to_f16(acc * (double)sa[sa_per_row ? m : 0] * (double)sw[sw_per_row ? n : 0]);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 multi-head attention chain  [P1 answer step 3 (enqueue core): int8   */
+/* QK^T GEMM to int32 logits; online softmax from fp32 to int8              */
+/* probabilities, the logits scaled by scale_q * scale_k; int8 P.V GEMM;    */
+/* rescale, bias and requantization to int8.  P1 answer step 2: output      */
+/* dimensions [batch, seq, heads, head_dim]; knowledge point 5: +-127]      */
+/*                                                                          */
+/* Q [B][Lq][H][D], K and V [B][Lk][H][D] int8; O [B][Lq][H][D] int8.        */
+/* For head (b, h), query i, key j, channel c:                              */
+/*   S_ij = sum_c Q[b,i,h,c] * K[b,j,h,c]                 exact integer      */
+/*   x_ij = fl32(fl32(S_ij) * alpha)                      one fp32 multiply  */
+/*   p_ij = exp(x_ij - max_j x) / sum_j exp(x_ij - max_j x)   in fp64        */
+/*   P_ij = rne(127 * p_ij), in [0, 127] (probabilities carry scale 1/127)   */
+/*   A_ic = sum_j P_ij * V[b,j,h,c]                       exact integer      */
+/*   t = fl32(A_ic); t = t * pv_scale; t = t + bias[h*D + c] if flagged;     */
+/*   O = clamp(rne(t * out_mult), -127, 127)              fp32 steps         */
+/* Heads are listed as b*H + h; per-head arrays are [nheads][Lq][Lk].        */
+/* ------------------------------------------------------------------------ */
+
+static int64_t qo_mha_at(int32_t b, int32_t t, int32_t h, int32_t L, int32_t H, int32_t D) {
+    return (((int64_t)b * L + t) * H + h) * D;
+}
+
+/* S (optional), P and R = 127 * p (optional) of the listed heads. */
+QO_API void qo_mha_int8_probs(const int8_t* Q, const int8_t* K, const int32_t* heads, int64_t nheads,
+                              int32_t H, int32_t Lq, int32_t Lk, int32_t D, float alpha, int32_t* S,
+                              int8_t* P, double* R) {
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t hh = 0; hh < nheads; ++hh)
+        for (int32_t i = 0; i < Lq; ++i) {
+            const int32_t b = heads[hh] / H, h = heads[hh] % H;
+            const int64_t row = (hh * Lq + i) * (int64_t)Lk;
+            double* x = (double*)malloc(sizeof(double) * (size_t)Lk);
+            double m = -INFINITY;
+            for (int32_t j = 0; j < Lk; ++j) {
+                const int8_t* q = Q + qo_mha_at(b, i, h, Lq, H, D);
+                const int8_t* k = K + qo_mha_at(b, j, h, Lk, H, D);
+                int64_t s = 0;
+                for (int32_t c = 0; c < D; ++c) s += (int64_t)q[c] * (int64_t)k[c];
+                if (S) S[row + j] = (int32_t)s;
+                const float xs = (float)s;
+                const float xf = xs * alpha;
+                x[j] = (double)xf;
+                if (x[j] > m) m = x[j];
+            }
+            double sum = 0.0;
+            for (int32_t j = 0; j < Lk; ++j) sum += exp(x[j] - m);
+            for (int32_t j = 0; j < Lk; ++j) {
+                const double r = 127.0 * (exp(x[j] - m) / sum);
+                P[row + j] = (int8_t)nearbyint(r);
+                if (R) R[row + j] = r;
+            }
+            free(x);
+        }
+}
+
+/* O of the listed heads from their probabilities P ([nheads][Lq][Lk]); the
+   other heads' outputs are left untouched. */
+QO_API void qo_mha_int8_out(const int8_t* P, const int8_t* V, const uint16_t* bias, const int32_t* heads,
+                            int64_t nheads, int32_t H, int32_t Lq, int32_t Lk, int32_t D, float pv_scale,
+                            float out_mult, uint32_t flags, int8_t* O) {
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t hh = 0; hh < nheads; ++hh)
+        for (int32_t i = 0; i < Lq; ++i) {
+            const int32_t b = heads[hh] / H, h = heads[hh] % H;
+            const int8_t* p = P + (hh * Lq + i) * (int64_t)Lk;
+            for (int32_t c = 0; c < D; ++c) {
+                int64_t acc = 0;
+                for (int32_t j = 0; j < Lk; ++j) acc += (int64_t)p[j] * (int64_t)V[qo_mha_at(b, j, h, Lk, H, D) + c];
+                float t = (float)acc;
+                t = t * pv_scale;
+                if (flags & QO_EPI_BIAS) t = t + qo_f16_to_f32(bias[h * D + c]);
+                float v = nearbyintf(t * out_mult);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                O[qo_mha_at(b, i, h, Lq, H, D) + c] = (int8_t)v;
+            }
+        }
 }

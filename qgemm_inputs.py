@@ -49,6 +49,22 @@ def w8a16_problem(M, K, N, G, seed):
     return A, W, S
 
 
+def mha_problem(B, Lq, Lk, H, D, seed):
+    """INT8 attention inputs: Q [B, Lq, H, D], K and V [B, Lk, H, D] int8 drawn as N(0, 32^2)
+    rounded and clipped to [-127, 127] (the codes N(0, 1) data gets with amax = 4 sigma); fp16
+    bias [H * D] ~ N(0, 0.02^2); and the recipe's fp32 factors: alpha = (4/127)^2 / sqrt(D)
+    (logits of unit spread), pv_scale = (1/127) (4/127), out_mult = 127 / 0.3."""
+    r = rng(seed)
+    Q = np.clip(np.rint(r.normal(0.0, 32.0, (B, Lq, H, D))), -127, 127).astype(np.int8)
+    K = np.clip(np.rint(r.normal(0.0, 32.0, (B, Lk, H, D))), -127, 127).astype(np.int8)
+    V = np.clip(np.rint(r.normal(0.0, 32.0, (B, Lk, H, D))), -127, 127).astype(np.int8)
+    bias = r.normal(0.0, 0.02, H * D).astype(np.float16)
+    alpha = np.float32((4.0 / 127.0) ** 2 / math.sqrt(D))
+    pv_scale = np.float32((1.0 / 127.0) * (4.0 / 127.0))
+    out_mult = np.float32(127.0 / 0.3)
+    return Q, K, V, bias, alpha, pv_scale, out_mult
+
+
 def w8a8_problem(M, N, K, seed):
     """fp16 activations X [M,K] and weights Wf [N,K] ~ N(0,1); bias [N] ~ N(0, 0.1^2);
     the static output multiplier of the recipe, 127 / (4 sqrt(K)) in fp32."""
