@@ -19,8 +19,9 @@ cpu_baseline = the CPU oracle on the same step (all host threads the oracle
 rows       = every other hot-path row, each timed the same way on its own
              inputs (prefill GEMM, W8A8 GEMM + epilogue, per-token int8
              quantization, KV-cache quant/dequant, INT4 MoE layer, the FP8
-             E4M3 path: per-tensor quantization, FP8 GEMM, FP8 KV cache, and
-             weight-only int8 (W8A16) decode and prefill)
+             E4M3 path: per-tensor quantization, FP8 GEMM, FP8 KV cache,
+             weight-only int8 (W8A16) decode and prefill, and the INT8
+             attention chain)
 
 Usage: python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu]
 """
@@ -41,6 +42,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense E4M3 MFMA, AMD's published MI355X figure
 
 DEC_K, DEC_N, DEC_G = 4096, 11008, 128
 DEC_MS = (1, 4, 8)
+MHA_SHAPE = (8, 512, 32, 128)  # batch, tokens (queries = keys), heads, head_dim
 ROT = 16
 
 
@@ -58,7 +60,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile", default=None,
                     choices=["decode1", "decode4", "decode8", "prefill", "w8a8", "quant_act",
-                             "kvquant", "kvdequant", "moe", "copy"],
+                             "kvquant", "kvdequant", "moe", "mha", "copy"],
                     help="launch one workload's kernels --launches times (eagerly) and exit; "
                          "for rocprofv3 runs")
     ap.add_argument("--launches", type=int, default=20)
@@ -285,6 +287,14 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
         torch.cuda.synchronize()
         for _ in range(launches):
             qg.moe_w4a16(*args, topK, G)
+    elif name == "mha":
+        B, L, H, D = MHA_SHAPE
+        Q, K, V, bias, alpha, pv, om = qi.mha_problem(B, L, L, H, D, 109)
+        Qd, Kd, Vd, bd = (to_dev(a) for a in (Q, K, V, bias))
+        O = torch.empty((B, L, H, D), dtype=torch.int8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            qg.mha_int8(Qd, Kd, Vd, alpha, pv, om, bias=bd, O=O)
     elif name == "copy":
         # an elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB),
         # to calibrate the HBM byte counters
@@ -506,6 +516,23 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
     rows["w8a16_prefill_M2048_K4096_N4096"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(fl / t / 1e12, 1),
                                                "mfma_frac": round(fl / t / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
     log(f"[bench] w8a16 prefill {rows['w8a16_prefill_M2048_K4096_N4096']}")
+    del probs
+
+    # INT8 attention chain: 8 sequences x 512 tokens, 32 heads of 128 (the W8A8
+    # token batch), 4 rotated input sets; algorithmic work 4 B H L^2 D int-ops
+    # (Q K^T and P V; the kernel computes Q K^T twice)
+    B, L, H, D = MHA_SHAPE
+    sets = []
+    for r in range(4):
+        Q, K, V, bias, alpha, pv, om = qi.mha_problem(B, L, L, H, D, 109 + 1000 * r)
+        sets.append(tuple(to_dev(a) for a in (Q, K, V, bias)))
+    O = torch.empty((B, L, H, D), dtype=torch.int8, device=dev)
+    g = graph_of([(lambda s=s: qg.mha_int8(s[0], s[1], s[2], alpha, pv, om, bias=s[3], O=O)) for s in sets])
+    t = time_graph(g, 4, reps=10)
+    ops = 4 * B * H * L * L * D
+    rows[f"mha_int8_B{B}_L{L}_H{H}_D{D}"] = {"us": round(t * 1e6, 2), "TOPS": round(ops / t / 1e12, 1),
+                                            "mfma_frac": round(ops / t / 1e12 / I8_MFMA_PEAK_TOPS, 4)}
+    log(f"[bench] mha {rows[f'mha_int8_B{B}_L{L}_H{H}_D{D}']}")
     return rows
 
 

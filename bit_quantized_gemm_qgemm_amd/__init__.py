@@ -73,6 +73,7 @@ def _declare(L):
         "qgemm_w4a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
         "qgemm_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
         "qgemm_w4a16": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+        "mha_int8": (_I32, [_P] * 7 + [_I32] * 5 + [ctypes.c_float] * 3 + [ctypes.c_uint32, _P]),
         "qgemm_w8a16_packed_bytes": (_SZ, [_I32, _I32]),
         "qgemm_w8a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
         "qgemm_w8a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
@@ -97,7 +98,7 @@ EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
            "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
            "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
-           "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16")
+           "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8")
 
 
 def _ptr(t):
@@ -362,3 +363,31 @@ def qgemm_fp8(A, W, a_scale, w_scale, Y=None):
                                          w_per_row, _ptr(Y), M, N, K, _stream()))
     return Y
 
+
+
+# ---------------------------------------------------------------- INT8 attention chain
+
+def mha_int8(Q, K, V, alpha, pv_scale, out_mult, bias=None, O=None, s_out=None, p_out=None):
+    """O [B, Lq, H, D] int8 = requant(P V) with P = int8 softmax of Q K^T * alpha;
+    Q [B, Lq, H, D], K and V [B, Lk, H, D] int8; bias fp16 [H * D] (applied when given).
+    Optional s_out int32 / p_out int8 [B, H, Lq, Lk] receive the logits and the codes."""
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.int8, n)
+    B, Lq, H, D = Q.shape
+    Lk = K.shape[1]
+    if tuple(K.shape) != (B, Lk, H, D) or tuple(V.shape) != (B, Lk, H, D):
+        raise ValueError("mha_int8: K and V must be [B, Lk, H, D] matching Q [B, Lq, H, D]")
+    if bias is not None:
+        _need(bias, torch.float16, "bias")
+    if O is None:
+        O = torch.empty((B, Lq, H, D), dtype=torch.int8, device=Q.device)
+    _need(O, torch.int8, "O")
+    if s_out is not None:
+        _need(s_out, torch.int32, "s_out")
+    if p_out is not None:
+        _need(p_out, torch.int8, "p_out")
+    flags = EPI_BIAS if bias is not None else 0
+    _check("mha_int8", lib().mha_int8(_ptr(Q), _ptr(K), _ptr(V), _ptr(bias), _ptr(O), _ptr(s_out), _ptr(p_out),
+                                      B, H, Lq, Lk, D, float(alpha), float(pv_scale), float(out_mult), flags,
+                                      _stream()))
+    return O

@@ -312,6 +312,44 @@ QGEMM_API int32_t qgemm_fp8(const uint8_t* A, const uint8_t* W, const float* a_s
                             int32_t a_per_row, const float* w_scale, int32_t w_per_row, uint16_t* Y,
                             int32_t M, int32_t N, int32_t K, void* stream);
 
+/* ------------------------------------------------------------------------
+ * INT8 multi-head attention chain  (INT8 cross-modal MHA TensorRT plugin
+ * interview page, answer step 3, enqueue core: int8 QK^T GEMM to int32
+ * logits; online softmax from fp32 to int8 probabilities with the factor
+ * scale_q * scale_k; int8 P.V GEMM; requantization with the output scale and
+ * an fp16 bias.  Answer step 2: output [batch, seq, heads, head_dim].
+ * Knowledge point 5: int8 codes within [-127, 127]).
+ *
+ * For batch b, head h, query i, key j, channel c (D = head_dim):
+ *   S_ij = sum_c Q[b][i][h][c] * K[b][j][h][c]                (int32, exact)
+ *   x_ij = fl32(fl32(S_ij) * alpha)
+ *   P_ij = rne(127 * softmax_j(x)_ij)  in [0, 127]    (probability scale 1/127)
+ *   A_ic = sum_j P_ij * V[b][j][h][c]                         (int32, exact)
+ *   O[b][i][h][c] = clamp(rne(fl32(fl32(fl32(A_ic) * pv_scale) + bias[h*D + c])
+ *                              * out_mult), -127, 127)
+ * (the bias term only with QGEMM_EPI_BIAS).  alpha is the logit factor the
+ * caller forms from its per-tensor dequant scales, scale_q * scale_k, with
+ * any 1/sqrt(D) folded in; pv_scale = (1/127) * scale_v.
+ *
+ * The softmax runs in fp32 (exp2 of the max-shifted logits, an online sum
+ * over key blocks, then code = rne(e * fl32(127 / sum))), so a probability
+ * code may differ by one from the exactly rounded 127 * p where that value
+ * lies within the fp32 error of a rounding boundary; everything else is
+ * integer or a fixed fp32 sequence.
+ *
+ *   Q: int8 [B][Lq][H][D]; K, V: int8 [B][Lk][H][D]; O: int8 [B][Lq][H][D].
+ *   bias: fp16 [H*D] (read only with QGEMM_EPI_BIAS).
+ *   s_out: optional int32 [B][H][Lq][Lk] logits S; p_out: optional int8
+ *   [B][H][Lq][Lk] probability codes P (NULL skips them; for tests).
+ *   Supported: D in {64, 128}, 1 <= Lk <= 133143, B and H <= 65535, flags in
+ *   {0, QGEMM_EPI_BIAS}.  B, H or Lq == 0 is a successful no-op; Lk == 0 is
+ *   QGEMM_BAD_SHAPE.
+ * ---------------------------------------------------------------------- */
+QGEMM_API int32_t mha_int8(const int8_t* Q, const int8_t* K, const int8_t* V, const uint16_t* bias, int8_t* O,
+                           int32_t* s_out, int8_t* p_out, int32_t B, int32_t H, int32_t Lq, int32_t Lk,
+                           int32_t D, float alpha, float pv_scale, float out_mult, uint32_t flags,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
         "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
         "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
         "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
-        "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16"])
+        "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -120,6 +120,23 @@ def test_w8a16_size_queries_and_validation(L):
     assert p(FAKE, FAKE, 128, 192, None) == 5
     assert p(FAKE + 4, FAKE + 65536, 128, 128, None) == 3
     assert p(FAKE, FAKE + 8192, 128, 128, None) == 2  # overlapping buffers
+
+
+def test_mha_validation(L):
+    f = L.mha_int8
+    args = lambda B, H, Lq, Lk, D, flags=0, q=FAKE, k=FAKE, v=FAKE, bias=FAKE, o=FAKE: (
+        q, k, v, bias, o, None, None, B, H, Lq, Lk, D, 1.0, 1.0, 1.0, flags, None)
+    assert f(*args(1, 1, 0, 16, 64)) == 0                      # Lq == 0: no-op
+    assert f(*args(0, 1, 8, 16, 64, q=None)) == 0              # B == 0: no-op before pointer checks
+    assert f(*args(1, 1, 8, 16, 64, q=None)) == 1
+    assert f(*args(1, 1, 8, 16, 64, flags=1, bias=None)) == 1  # bias flagged but missing
+    assert f(*args(1, 1, -8, 16, 64)) == 2
+    assert f(*args(1, 1, 8, 0, 64)) == 2                       # softmax over no keys
+    assert f(*args(1, 1, 8, 16, 96)) == 5                      # head_dim
+    assert f(*args(1, 1, 8, 16, 64, flags=2)) == 5             # no GELU in this chain
+    assert f(*args(1, 1, 8, 133144, 64)) == 5                  # P V would overflow int32
+    assert f(*args(1, 1, 8, 16, 64, k=FAKE + 8)) == 3
+    assert f(*args(1, 1, 8, 16, 64, flags=1, bias=FAKE + 2)) == 3
 
 
 def test_prepack_validation(L):
