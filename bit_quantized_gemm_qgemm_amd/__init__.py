@@ -30,6 +30,13 @@ EPI_GELU = 2
 FP8_PER_TENSOR = 0
 FP8_PER_ROW = 1
 
+TACTIC_DEFAULT = 0
+QGEMM_W4A16_TACTIC_DECODE_NARROW = 1
+QGEMM_W4A16_TACTIC_DECODE_BALANCED = 2
+QGEMM_W4A16_TACTIC_SPLITK = 3
+QGEMM_W4A16_TACTIC_PREFILL = 4
+QGEMM_W4A16_TACTIC_PREFILL_LARGE = 5
+
 _lib = None
 
 
@@ -74,6 +81,10 @@ def _declare(L):
         "qgemm_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
         "qgemm_w4a16": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
         "mha_int8": (_I32, [_P] * 7 + [_I32] * 5 + [ctypes.c_float] * 3 + [ctypes.c_uint32, _P]),
+        "qgemm_w4a16_tactics": (_I32, [_I32, _I32, _I32, _I32, _P, _I32]),
+        "qgemm_w4a16_tactic_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+        "qgemm_w4a16_tactic": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+        "qgemm_w4a16_autotune": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _I32, _P, _P, _P]),
         "qgemm_w8a16_packed_bytes": (_SZ, [_I32, _I32]),
         "qgemm_w8a16_prepack": (_I32, [_P, _P, _I32, _I32, _P]),
         "qgemm_w8a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
@@ -98,7 +109,9 @@ EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
            "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
            "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
-           "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8")
+           "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
+           "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
+           "qgemm_w4a16_autotune")
 
 
 def _ptr(t):
@@ -152,10 +165,12 @@ def qgemm_w4a16_workspace_bytes(M, N, K, G):
     return lib().qgemm_w4a16_workspace_bytes(M, N, K, G)
 
 
-def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
+def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None, tactic=0):
     """Y[M, N] = A[M, K] (fp16) x dequant(w_frag, scales [K/G, N] fp16).  Without a
-    workspace the one the library asks for (mid M) is allocated here; an empty
-    tensor selects the kernels that need none."""
+    workspace the one the library asks for (for the tactic) is allocated here; an
+    empty tensor selects the kernels that need none.  tactic: 0 = the library's
+    choice, an id from qgemm_w4a16_tactics, or "auto" = the fastest id found by
+    qgemm_w4a16_autotune for this shape (tuned on first use, then remembered)."""
     _need(A, torch.float16, "A")
     _need(w_frag, torch.uint8, "w_frag")
     _need(scales, torch.float16, "scales")
@@ -164,14 +179,51 @@ def qgemm_w4a16(A, w_frag, scales, G, N=None, Y=None, workspace=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
     _need(Y, torch.float16, "Y")
+    if tactic == "auto":
+        tactic = _TUNED.get((M, N, K, G))
+        if tactic is None:
+            tactic = qgemm_w4a16_autotune(A, w_frag, scales, G, N=N)[0] if M else 0
     if workspace is None:
-        need = qgemm_w4a16_workspace_bytes(M, N, K, G)
+        need = qgemm_w4a16_tactic_workspace_bytes(M, N, K, G, tactic)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("qgemm_w4a16", lib().qgemm_w4a16(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
-                                             _ptr(workspace) if ws else None, ws, _stream()))
+    _check("qgemm_w4a16", lib().qgemm_w4a16_tactic(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G,
+                                                    int(tactic), _ptr(workspace) if ws else None, ws, _stream()))
     return Y
+
+
+_TUNED = {}
+
+
+def qgemm_w4a16_tactics(M, N, K, G):
+    """Ids of the W4A16 kernels valid for the shape (ascending)."""
+    n = lib().qgemm_w4a16_tactics(M, N, K, G, None, 0)
+    buf = (ctypes.c_int32 * max(n, 1))()
+    lib().qgemm_w4a16_tactics(M, N, K, G, buf, n)
+    return list(buf[:n])
+
+
+def qgemm_w4a16_tactic_workspace_bytes(M, N, K, G, tactic):
+    return lib().qgemm_w4a16_tactic_workspace_bytes(M, N, K, G, int(tactic))
+
+
+def qgemm_w4a16_autotune(A, w_frag, scales, G, N=None, reps=20):
+    """Times every valid tactic on these operands (the library's autotune call)
+    and remembers the fastest for the shape; returns (tactic, us per launch)."""
+    _need(A, torch.float16, "A")
+    M, K = A.shape
+    N = scales.shape[1] if N is None else N
+    Y = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    need = qgemm_w4a16_tactic_workspace_bytes(M, N, K, G, QGEMM_W4A16_TACTIC_SPLITK)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=A.device)
+    best = ctypes.c_int32(0)
+    us = ctypes.c_float(0.0)
+    _check("qgemm_w4a16_autotune",
+           lib().qgemm_w4a16_autotune(_ptr(A), _ptr(w_frag), _ptr(scales), _ptr(Y), M, N, K, G, _ptr(ws),
+                                      ws.numel(), int(reps), ctypes.byref(best), ctypes.byref(us), _stream()))
+    _TUNED[(M, N, K, G)] = best.value
+    return best.value, us.value
 
 
 # ---------------------------------------------------------------- W8A16

@@ -430,34 +430,47 @@ __global__ __launch_bounds__(256) void wq_splitk_reduce_kernel(const float* __re
     }
 }
 
-// One launch of the decode kernel for M <= 16.
-// (MT, NSW, KCW): rows of the MFMA tile, 16-column strips per wave, 128-k
-// chunks per wave; the workgroup is 32 / KCW waves over NSW strips.
+// Decode launches.  (MT, NSW, KCW): rows of the MFMA tile, 16-column strips
+// per wave, 128-k chunks per wave; the workgroup is 32 / KCW waves over NSW
+// strips.  Narrow (M <= 2): one strip per workgroup of eight waves, 4 chunks
+// per wave.  Balanced (M <= 16): at least one workgroup per CU where there
+// are enough strips, each over a contiguous range of at most three strips.
 template <int WB, int G>
-void launch_wq_decode(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
-                      int N, int K, hipStream_t st) {
+void launch_wq_decode_narrow(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
+                             int M, int N, int K, hipStream_t st) {
     if (M == 1)
         hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
-    else if (M == 2)
+    else
         hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
-    else {
-        // at least one workgroup per CU where there are enough strips,
-        // each over a contiguous range of at most three strips
-        const int nstrips = N / 16;
-        int nwg = nstrips < 256 ? nstrips : 256;
-        if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
-        if (M <= 4)
-            hipLaunchKernelGGL((wq_decode_kernel<WB, 4, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf,
-                               S, ldS, Y, M, N, K);
-        else if (M <= 8)
-            hipLaunchKernelGGL((wq_decode_kernel<WB, 8, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf,
-                               S, ldS, Y, M, N, K);
-        else
-            hipLaunchKernelGGL((wq_decode_kernel<WB, 16, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A,
-                               wf, S, ldS, Y, M, N, K);
-    }
+}
+
+template <int WB, int G>
+void launch_wq_decode_balanced(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
+                               int M, int N, int K, hipStream_t st) {
+    const int nstrips = N / 16;
+    int nwg = nstrips < 256 ? nstrips : 256;
+    if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
+    if (M <= 4)
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 4, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf, S,
+                           ldS, Y, M, N, K);
+    else if (M <= 8)
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 8, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf, S,
+                           ldS, Y, M, N, K);
+    else
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 16, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf, S,
+                           ldS, Y, M, N, K);
+}
+
+// One launch of the decode kernel for M <= 16 (the shapes measured fastest).
+template <int WB, int G>
+void launch_wq_decode(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
+                      int N, int K, hipStream_t st) {
+    if (M <= 2)
+        launch_wq_decode_narrow<WB, G>(A, wf, S, ldS, Y, M, N, K, st);
+    else
+        launch_wq_decode_balanced<WB, G>(A, wf, S, ldS, Y, M, N, K, st);
 }
 
 template <int WB, int G>

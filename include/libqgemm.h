@@ -113,6 +113,61 @@ QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const ui
                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * W4A16 tactics  (Int4 Groupwise GEMM Plugin V2 page: getNbTactics /
+ * getValidTactics list the valid kernel variants for a shape as positive ids,
+ * setTactic selects one, 0 being the default; configurePlugin's token count
+ * steers the choice; the timing cache lets each shape be autotuned once).
+ *
+ * Ids of this library's W4A16 kernels (all compute qgemm_w4a16's function
+ * with fp32 accumulation; results of different tactics agree within the
+ * fp16 tolerance, not bit for bit; each tactic alone is deterministic):
+ *   1 decode, one 16-column strip per workgroup      valid for M <= 2
+ *   2 decode, balanced ranges of up to 3 strips      valid for M <= 16
+ *   3 split-K with fp32 partials + ordered reduction valid for M <= 512 and
+ *     M*K < 2^32; needs qgemm_w4a16_tactic_workspace_bytes() of workspace
+ *   4 prefill, 128x128 tiles                         valid for every M
+ *   5 prefill, 128x256 tiles (LDS DMA)               valid for N % 256 == 0
+ * The library keeps no tactic state: a caller that autotunes keeps the
+ * result per shape.
+ * ---------------------------------------------------------------------- */
+#define QGEMM_TACTIC_DEFAULT 0
+#define QGEMM_W4A16_TACTIC_DECODE_NARROW 1
+#define QGEMM_W4A16_TACTIC_DECODE_BALANCED 2
+#define QGEMM_W4A16_TACTIC_SPLITK 3
+#define QGEMM_W4A16_TACTIC_PREFILL 4
+#define QGEMM_W4A16_TACTIC_PREFILL_LARGE 5
+
+/* Number of tactics valid for the shape (0 if qgemm_w4a16 does not support
+   the shape or M <= 0); the first min(count, capacity) ids, ascending, are
+   written to tactics (may be NULL). */
+QGEMM_API int32_t qgemm_w4a16_tactics(int32_t M, int32_t N, int32_t K, int32_t G, int32_t* tactics,
+                                      int32_t capacity);
+
+/* Workspace bytes a tactic needs (tactic 0: qgemm_w4a16_workspace_bytes;
+   0 for tactics that need none and for invalid arguments). */
+QGEMM_API size_t qgemm_w4a16_tactic_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G, int32_t tactic);
+
+/* qgemm_w4a16 with the kernel chosen by the caller: tactic 0 is exactly
+   qgemm_w4a16; a tactic not valid for the shape returns QGEMM_UNSUPPORTED;
+   tactic 3 without enough workspace returns QGEMM_WORKSPACE_TOO_SMALL.
+   Arguments and errors otherwise as qgemm_w4a16. */
+QGEMM_API int32_t qgemm_w4a16_tactic(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales, uint16_t* Y,
+                                     int32_t M, int32_t N, int32_t K, int32_t G, int32_t tactic, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Times every valid tactic (tactic 3 only if the workspace suffices) on the
+   given operands: two untimed launches, then `reps` launches between two HIP
+   events on `stream`; writes the fastest id to *best_tactic and its mean
+   microseconds per launch to *best_us (may be NULL).  Blocks the host until
+   the timed launches finish; Y is overwritten; creates and destroys two HIP
+   events, allocates no device memory.  M == 0 or reps <= 0 return
+   QGEMM_BAD_SHAPE; other argument errors as qgemm_w4a16. */
+QGEMM_API int32_t qgemm_w4a16_autotune(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales,
+                                       uint16_t* Y, int32_t M, int32_t N, int32_t K, int32_t G, void* workspace,
+                                       size_t workspace_bytes, int32_t reps, int32_t* best_tactic, float* best_us,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------
  * W8A16 weight-only int8 GEMM  (FP8 vs INT8 low-precision inference in
  * TensorRT-LLM, itzkxy.com: weight-only int8 with fp16 activations is one of
  * the INT8 configurations compared; the page leaves the scale granularity

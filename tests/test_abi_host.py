@@ -40,7 +40,9 @@ def test_header_declares_the_boundary():
         "qgemm_w4a16_prepack", "qgemm_w4a16_workspace_bytes", "qgemm_w4a16", "quant_sym_int8",
         "dequant_sym_int8", "qgemm_w8a8_epilogue", "moe_w4a16_workspace_bytes", "moe_w4a16",
         "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
-        "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8"])
+        "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
+        "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
+        "qgemm_w4a16_autotune"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -137,6 +139,48 @@ def test_mha_validation(L):
     assert f(*args(1, 1, 8, 133144, 64)) == 5                  # P V would overflow int32
     assert f(*args(1, 1, 8, 16, 64, k=FAKE + 8)) == 3
     assert f(*args(1, 1, 8, 16, 64, flags=1, bias=FAKE + 2)) == 3
+
+
+def test_w4a16_tactic_lists(L):
+    import ctypes
+    def tactics(M, N, K, G=128):
+        buf = (ctypes.c_int32 * 8)()
+        n = L.qgemm_w4a16_tactics(M, N, K, G, buf, 8)
+        return list(buf[:n])
+    # by the validity rules the header states
+    assert tactics(1, 11008, 4096) == [1, 2, 3, 4, 5]  # 11008 = 43 * 256
+    assert tactics(1, 11136, 4096) == [1, 2, 3, 4]     # 11136 = 87 * 128
+    assert tactics(2, 4096, 4096) == [1, 2, 3, 4, 5]
+    assert tactics(16, 4096, 4096) == [2, 3, 4, 5]
+    assert tactics(64, 11008, 4096) == [3, 4, 5]
+    assert tactics(512, 4096, 4096) == [3, 4, 5]
+    assert tactics(513, 4096, 4096) == [4, 5]
+    assert tactics(2048, 384, 4096) == [4]
+    assert tactics(0, 4096, 4096) == [] and tactics(8, 4096, 4000) == [] and tactics(8, 4096, 4096, 256) == []
+    assert L.qgemm_w4a16_tactics(1, 4096, 4096, 128, None, 0) == 5
+    buf = (ctypes.c_int32 * 2)()
+    assert L.qgemm_w4a16_tactics(1, 4096, 4096, 128, buf, 2) == 5 and list(buf) == [1, 2]
+    S = max(1, min(512 // (11008 // 128), 4096 // 128, 16))
+    assert L.qgemm_w4a16_tactic_workspace_bytes(8, 11008, 4096, 128, 3) == S * 8 * 11008 * 4
+    assert L.qgemm_w4a16_tactic_workspace_bytes(8, 11008, 4096, 128, 0) == 0
+    assert L.qgemm_w4a16_tactic_workspace_bytes(64, 11008, 4096, 128, 0) == S * 64 * 11008 * 4
+    assert L.qgemm_w4a16_tactic_workspace_bytes(64, 11008, 4096, 128, 4) == 0
+    assert L.qgemm_w4a16_tactic_workspace_bytes(600, 11008, 4096, 128, 3) == 0  # not valid there
+    f = L.qgemm_w4a16_tactic
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 128, 1, None, 0, None) == 5   # narrow decode: M <= 2
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 128, 9, None, 0, None) == 5   # unknown id
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 384, 4096, 128, 5, None, 0, None) == 5    # N % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 128, 3, None, 0, None) == 4   # no workspace
+    assert f(FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 128, 3, FAKE + 8, 1 << 30, None) == 3
+    assert f(None, None, None, None, 0, 4096, 4096, 128, 4, None, 0, None) == 0     # M == 0
+    assert f(None, FAKE, FAKE, FAKE, 4, 4096, 4096, 128, 4, None, 0, None) == 1
+    a = L.qgemm_w4a16_autotune
+    best = ctypes.c_int32(-1)
+    assert a(FAKE, FAKE, FAKE, FAKE, 4, 4096, 4096, 128, None, 0, 10, None, None, None) == 1
+    assert a(FAKE, FAKE, FAKE, FAKE, 4, 4096, 4096, 128, None, 0, 0, ctypes.byref(best), None, None) == 2
+    assert a(FAKE, FAKE, FAKE, FAKE, 0, 4096, 4096, 128, None, 0, 5, ctypes.byref(best), None, None) == 2
+    assert a(FAKE, FAKE, FAKE, FAKE, 4, 100, 4096, 128, None, 0, 5, ctypes.byref(best), None, None) == 5
+    assert best.value == -1
 
 
 def test_prepack_validation(L):

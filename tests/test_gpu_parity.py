@@ -115,9 +115,8 @@ def test_w4a16_prefill_small(qg, M, G):
     assert_fp16_close(run_w4a16(qg, A, Wb, S, G), oracle.w4a16(A, Wb, S, G), f"M={M} G={G}")
 
 
-# M > 512 takes the 128x256 DMA kernel when N % 256 == 0: ragged M, every
-# group size, one chunk and a count that leaves a partial six-trip pass;
-# N = 384 checks that such M falls back to the 128x128 kernel
+# the 128x256 DMA kernel: ragged M, every group size, one chunk and a count
+# that leaves a partial six-trip pass; N = 384 runs the 128x128 kernel
 # mid M (16 < M <= 128): the split-K path (workspace from the library's
 # query) and, with an empty workspace, the single-pass prefill kernel
 @pytest.mark.parametrize("G", [32, 64, 128])
@@ -149,8 +148,14 @@ def test_w4a16_mid_m_full_shape_sampled(qg):
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("M,K,N", [(513, 128, 256), (640, 896, 512), (1100, 384, 256), (600, 256, 384)])
 def test_w4a16_prefill_large(qg, M, K, N, G):
+    # the 128x256 kernel by its tactic id where N % 256 == 0 (the default call picks it only
+    # with enough tiles), and the default call
     A, Wb, S = qi.w4a16_problem(M, K, N, G, 450 + M + K + G)
-    assert_fp16_close(run_w4a16(qg, A, Wb, S, G), oracle.w4a16(A, Wb, S, G), f"M={M} K={K} N={N} G={G}")
+    ref = oracle.w4a16(A, Wb, S, G)
+    assert_fp16_close(run_w4a16(qg, A, Wb, S, G), ref, f"M={M} K={K} N={N} G={G}")
+    if N % 256 == 0:
+        Y = qg.qgemm_w4a16(dev(A), prepack(qg, Wb, K, N), dev(S), G, tactic=qg.QGEMM_W4A16_TACTIC_PREFILL_LARGE)
+        assert_fp16_close(host(Y), ref, f"128x256 tiles M={M} K={K} N={N} G={G}")
 
 
 def test_w4a16_prefill_cfg2_sampled(qg):
