@@ -269,6 +269,30 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
         if (c + 1 < kchunks) trip(c + 1, 1);
     }
 
+    // ---- epilogue.  The codes of the 256x256 tile go through LDS so that Y
+    // is written in whole 16-byte row pieces: a lane holds four consecutive
+    // rows of one column per register group; a 4x4 byte transpose inside each
+    // lane quad (two DPP moves, two byte permutes) gives each lane four
+    // consecutive columns of one row, stored as one dword into a row-major
+    // LDS tile (pitch 288 bytes: the 32 dwords of a half-wave fall in 32
+    // distinct banks).  The operand stages are free: the last trip ended with
+    // every wave's DMA drained and a barrier.
+    if (acc_out) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int row = m0 + wm * 128 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+                    if (row < M) acc_out[(size_t)row * N + n0 + wn * 64 + t * 32 + c32] = acc[i][t][j];
+                }
+    }
+    constexpr int EPW = 72;  // LDS tile pitch in dwords (256 bytes + 32)
+    uint32_t* stile = reinterpret_cast<uint32_t*>(lds);
+    const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;  // stage 1: pairs of lanes
+    const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;  // stage 2: pairs of pairs
+    const int q = lane & 3;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int col = n0 + wn * 64 + t * 32 + c32;
@@ -277,15 +301,30 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-                if (row < M) {
-                    const int32_t a = acc[i][t][j];
-                    if (acc_out) acc_out[(size_t)row * N + col] = a;
-                    Y[(size_t)row * N + col] = requant(a, sa[row], swv, bv, out_mult, flags);
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                uint32_t d = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + r0 + r < M ? m0 + r0 + r : M - 1;  // rows >= M are not stored
+                    const int8_t c = requant(acc[i][t][4 * g + r], sa[row], swv, bv, out_mult, flags);
+                    d |= (uint32_t)(uint8_t)c << (8 * r);
                 }
+                const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0xB1, 0xf, 0xf, false);
+                const uint32_t d1 = __builtin_amdgcn_perm(x, d, sel1);
+                const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d1, 0x4E, 0xf, 0xf, false);
+                stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = __builtin_amdgcn_perm(y, d1, sel2);
             }
         }
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int idx = tid + 512 * p, row = idx >> 4, piece = idx & 15;
+        if (m0 + row < M)
+            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 16) =
+                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
     }
 }
 
