@@ -131,6 +131,38 @@ __device__ __forceinline__ float absmax8(uintx4 v) {
     return m;
 }
 
+// ---- accumulator tiles to row-major pieces (GEMM epilogues)
+//
+// In a 32x32 MFMA accumulator a lane quad (lanes 4k .. 4k+3, lane q holding
+// column 4k + q) holds, per group of four registers, four consecutive rows
+// r = 0..3.  A 4x4 transpose inside the quad (DPP quad permutations and byte
+// permutes) gives lane q row q of the quad's four columns, so a lane can
+// store four adjacent outputs of one row at once.
+
+// 8-bit values: d holds row r in byte r; the result holds column c in byte c.
+__device__ __forceinline__ uint32_t quad_rows_u8(uint32_t d, int lane) {
+    const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;  // with lane ^ 1
+    const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;  // with lane ^ 2
+    const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0xB1, 0xf, 0xf, false);
+    const uint32_t d1 = __builtin_amdgcn_perm(x, d, sel1);
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d1, 0x4E, 0xf, 0xf, false);
+    return __builtin_amdgcn_perm(y, d1, sel2);
+}
+
+// 16-bit values: d0 holds rows 0 (low half) and 1, d1 rows 2 and 3; on
+// return e0 holds columns 0 and 1, e1 columns 2 and 3, of row q.
+__device__ __forceinline__ void quad_rows_u16(uint32_t d0, uint32_t d1, int lane, uint32_t& e0, uint32_t& e1) {
+    const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;  // with lane ^ 1
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d0, 0xB1, 0xf, 0xf, false);
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d1, 0xB1, 0xf, 0xf, false);
+    const uint32_t s0 = __builtin_amdgcn_perm(p0, d0, sel);
+    const uint32_t s1 = __builtin_amdgcn_perm(p1, d1, sel);
+    const uint32_t u0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0x4E, 0xf, 0xf, false);
+    const uint32_t u1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0x4E, 0xf, 0xf, false);
+    e0 = (lane & 2) ? u1 : s0;
+    e1 = (lane & 2) ? s1 : u0;
+}
+
 }  // namespace qg
 
 // Host-side helpers shared by the entry points.

@@ -174,7 +174,8 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
                                                           const float* __restrict__ sw, int sw_per_row,
                                                           uint16_t* __restrict__ Y, int M, int N, int K) {
     constexpr int SL = FB * 128;  // bytes per operand buffer (256 rows x 128 k)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * SL];  // A0, A1, W0, W1
+    // A0, A1, W0, W1; after the k loop the fp16 output tile (256 rows x 576 bytes)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * SL + 16384];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     // tile (x, y) of workgroup L: y = L % (row tiles), so the workgroups on
@@ -275,18 +276,52 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
         if (c + 1 < kchunks) trip(c + 1, 1);
     }
 
+    // ---- epilogue: Y = fp16(fl(fl(acc * sa) * sw)) through an LDS tile, so
+    // that rows are written in 16-byte pieces: a quad transpose gives each
+    // lane four adjacent columns of one row (8 bytes), stored into a
+    // row-major tile of pitch 576 bytes.  The operand buffers are free: the
+    // last trip ended with every wave's DMA drained and a barrier.
+    constexpr int EPW = 144;  // tile pitch in dwords (512 bytes + 64)
+    uint32_t* stile = reinterpret_cast<uint32_t*>(lds);
+    const int q = lane & 3;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int col = n0 + wn * 64 + t * 32 + c32;
-        if (col >= N) continue;
-        const float swv = sw[sw_per_row ? col : 0];
+        const float swv = sw[sw_per_row ? (col < N ? col : N - 1) : 0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-                if (row < M) Y[(size_t)row * N + col] = f2h((acc[i][t][j] * sa[sa_per_row ? row : 0]) * swv);
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                uint32_t v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + r0 + r < M ? m0 + r0 + r : M - 1;  // rows >= M are not stored
+                    v[r] = f2h_of_product(acc[i][t][4 * g + r] * sa[sa_per_row ? row : 0], swv);
+                }
+                uint32_t e0, e1;
+                quad_rows_u16(v[0] | (v[1] << 16), v[2] | (v[3] << 16), lane, e0, e1);
+                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wn * 32 + t * 16 + 2 * (c32 >> 2)]) =
+                    uintx2{e0, e1};
             }
+        }
+    }
+    __syncthreads();
+    // 256 rows x 32 pieces of 8 outputs; a piece past N (or any piece when
+    // rows are not 16-byte aligned, N % 8 != 0) is written output by output
+    const bool vec = (N & 7) == 0;
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int idx = tid + 512 * p, row = idx >> 5, piece = idx & 31;
+        const int colg = n0 + piece * 8;
+        if (m0 + row >= M || colg >= N) continue;
+        const uint32_t* src = &stile[row * EPW + piece * 4];
+        uint16_t* dst = Y + (size_t)(m0 + row) * N + colg;
+        if (vec && colg + 8 <= N) {
+            *reinterpret_cast<uintx4*>(dst) = *reinterpret_cast<const uintx4*>(src);
+        } else {
+            for (int e = 0; e < 8 && colg + e < N; ++e) dst[e] = (uint16_t)(src[e >> 1] >> (16 * (e & 1)));
         }
     }
 }

@@ -204,19 +204,40 @@ __global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint1
         if (c + 4 < kchunks) trip(c + 4, 0, 1);
         if (c + 5 < kchunks) trip(c + 5, 1, 2);
     }
-    wait_vmcnt<0>();  // the last trip's (unused) prefetches
-
+    // ---- epilogue: Y through an LDS tile in 16-byte row pieces.  A quad
+    // transpose gives each lane four adjacent columns of one row (8 bytes of
+    // fp16), stored into a row-major tile of pitch 576 bytes; then every
+    // thread writes whole 16-byte pieces.  Each wave first drains its last
+    // (unused) prefetches, and the barrier makes sure no DMA still writes LDS.
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int EPW = 144;  // tile pitch in dwords (512 bytes + 64)
+    uint32_t* stile = reinterpret_cast<uint32_t*>(sA);
+    const int q = lane & 3;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int col = n0 + wave * 64 + t * 32 + c32;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = m0 + i * 32 + acc_row(j, lane);
-                if (row < M) Y[(size_t)row * N + col] = f2h(acc[i][t][j]);
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                const uint32_t v0 = f2h(acc[i][t][4 * g]), v1 = f2h(acc[i][t][4 * g + 1]);
+                const uint32_t v2 = f2h(acc[i][t][4 * g + 2]), v3 = f2h(acc[i][t][4 * g + 3]);
+                uint32_t e0, e1;
+                quad_rows_u16(v0 | (v1 << 16), v2 | (v3 << 16), lane, e0, e1);
+                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wave * 32 + t * 16 + 2 * (c32 >> 2)]) =
+                    uintx2{e0, e1};
             }
-        }
+    __syncthreads();
+    // 128 rows x 32 pieces of 8 outputs (N % 256 == 0: every piece is whole and aligned)
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int idx = tid + 256 * p, row = idx >> 5, piece = idx & 31;
+        if (m0 + row < M)
+            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8) =
+                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
+    }
 }
 
 // Tactics (ids in the header): the kernels and launch shapes above, one id

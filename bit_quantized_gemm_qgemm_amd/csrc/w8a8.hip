@@ -299,8 +299,6 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
     }
     constexpr int EPW = 72;  // LDS tile pitch in dwords (256 bytes + 32)
     uint32_t* stile = reinterpret_cast<uint32_t*>(lds);
-    const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;  // stage 1: pairs of lanes
-    const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;  // stage 2: pairs of pairs
     const int q = lane & 3;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -319,10 +317,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
                     const int8_t c = requant(acc[i][t][4 * g + r], sa[row], swv, bv, out_mult, flags);
                     d |= (uint32_t)(uint8_t)c << (8 * r);
                 }
-                const uint32_t x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0xB1, 0xf, 0xf, false);
-                const uint32_t d1 = __builtin_amdgcn_perm(x, d, sel1);
-                const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d1, 0x4E, 0xf, 0xf, false);
-                stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = __builtin_amdgcn_perm(y, d1, sel2);
+                stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = quad_rows_u8(d, lane);
             }
         }
     }
