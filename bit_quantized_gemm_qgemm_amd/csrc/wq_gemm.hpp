@@ -342,17 +342,37 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
     }
     if (c < kchunks) compute(sA[0], b0);
 
+    // Epilogue through an LDS tile (128 rows x 320 bytes) so that Y is
+    // written in 16-byte row pieces: a quad transpose gives each lane four
+    // adjacent columns of one row.  The barrier waits for every wave's last
+    // reads of the A buffers.
+    __syncthreads();
+    constexpr int EPW = 80;  // tile pitch in dwords (256 bytes + 64)
+    uint32_t* stile = reinterpret_cast<uint32_t*>(&sA[0][0]);
+    const int q = lane & 3;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int col = ncol0 + t * 32 + c32;
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = m0 + wm * 64 + i * 32 + acc_row(j, lane);
-                if (row < M) Y[(size_t)row * N + col] = f2h(acc[i][t][j]);
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = wm * 64 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                const uint32_t v0 = f2h(acc[i][t][4 * g]), v1 = f2h(acc[i][t][4 * g + 1]);
+                const uint32_t v2 = f2h(acc[i][t][4 * g + 2]), v3 = f2h(acc[i][t][4 * g + 3]);
+                uint32_t e0, e1;
+                quad_rows_u16(v0 | (v1 << 16), v2 | (v3 << 16), lane, e0, e1);
+                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wn * 32 + t * 16 + 2 * (c32 >> 2)]) =
+                    uintx2{e0, e1};
             }
-        }
+    __syncthreads();
+    // 128 rows x 16 pieces of 8 outputs (N % 128 == 0: whole, aligned pieces)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int idx = tid + 256 * p, row = idx >> 4, piece = idx & 15;
+        if (m0 + row < M)
+            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8) =
+                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
+    }
 }
 
 // ------------------------------------------------------------------ mid M
