@@ -16,7 +16,8 @@
 // (keys as rows, so a lane holds 16 keys of one query) and keeps the online
 // row maximum (of the integer logits) and exp-sum; pass 2 recomputes each
 // block's S^T, turns it into int8 codes P = rne(exp(x - m) * fl(127 / l)) in
-// the same registers, and feeds them, packed, as the B operand of
+// the same registers (v_cvt_pk_u8_f32 rounds and packs), and feeds them as
+// the B operand of
 // O^T = V^T P^T: the k order of that
 // MFMA is the accumulator's row order (keys 8 (j / 4) + 4 (lane / 32) + j % 4
 // for register j), so V is written to LDS transposed in that key order.
@@ -220,14 +221,14 @@ __global__ __launch_bounds__(64 * NW, 2) void mha_int8_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)acc[j], a2, -m2));
-            // e <= 1 and cq <= 127: the rounded code is an integer in [0, 127], which the
-            // byte conversion packs exactly
-            const float c = valid(masked, kb, j) ? __builtin_rintf(e * cq) : 0.f;
+            // e <= 1 and cq <= 127, so e * cq lies in [0, 127]; the byte conversion rounds
+            // it to nearest, ties to even (checked on gfx950 for every float in [0, 128])
+            const float c = valid(masked, kb, j) ? e * cq : 0.f;
             pk[j >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, j & 3, pk[j >> 2]);
             if constexpr (DBG) {
                 const int key = kb * KB + key_of(j, lane);
                 if (p_out && q < Lq && key < Lk)
-                    p_out[(((size_t)b * H + h) * Lq + q) * Lk + key] = (int8_t)(int)c;
+                    p_out[(((size_t)b * H + h) * Lq + q) * Lk + key] = (int8_t)((pk[j >> 2] >> (8 * (j & 3))) & 0xffu);
             }
         }
         const intx4 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
