@@ -4,13 +4,11 @@
 // Int4 Groupwise GEMM Plugin V2 page (class summary: inputs, output and the
 // fragment-layout weights; configurePlugin: the token count M steers the
 // kernel choice; getValidTactics / setTactic: listed kernel variants).
-// Four kernels: the decode (M <= 16), mid-M split-K (16 < M <= 128, with
-// workspace) and 128x128 prefill kernels shared with the int8 path
-// (wq_gemm.hpp), and the large prefill kernel below (chosen by default when
-// it has enough tiles to fill the chip): 256x128 tiles, four waves of 128x64;
-// A tiles go global -> LDS by direct DMA with an XOR swizzle, B fragment
-// blocks and scale rows likewise.  Each launch shape is also a tactic a
-// caller can list, select or autotune.
+// Four kernels, all shared with the int8 path (wq_gemm.hpp): decode
+// (M <= 16), mid-M split-K (16 < M <= 128, with workspace), 128x128 prefill,
+// and 128x256 prefill (chosen by default when it has enough tiles to fill
+// the chip; A tiles and B fragment blocks reach LDS by direct DMA).  Each
+// launch shape is also a tactic a caller can list, select or autotune.
 #include "common.hpp"
 #include "wq_gemm.hpp"
 
@@ -20,225 +18,6 @@ using namespace qg;
 
 // ------------------------------------------------------------------ large prefill
 
-// Large-M prefill: 128x256 output tiles, four waves side by side, each
-// 128 rows x 64 columns (4 x 2 v_mfma_f32_32x32x16_f16 tiles, accumulators in
-// the unified VGPR/AGPR file); one workgroup per CU at M = 2048.  A tile that
-// is wide in N suits W4A16: per 128-k chunk a workgroup streams 32 KB of fp16
-// A and 16 KB of int4 B (a 256 x 128 tile would need 64 KB + 8 KB for the
-// same MFMA work), and each wave owns its columns, so every B element is
-// dequantized once per workgroup.
-//
-// Every load in the main loop is a global -> LDS DMA (no VGPR destinations,
-// no VALU): A (two buffers) and B (fragment blocks plus scale rows, three
-// stages, so B is fetched two chunks ahead).  A wave's A-DMA instruction
-// fills 1 KB of LDS in lane order (four 256-byte rows); the lane that fills
-// position pos of row r fetches piece pos ^ (r & 15) of that row, so the MFMA
-// fragment reads, 16 rows at one k-group, hit 16 distinct 16-byte bank
-// groups.  The loop waits for the DMA it needs with an explicit counter wait
-// and a bare barrier: __syncthreads() would also wait for the B prefetch
-// still in flight.
-constexpr int PL_BM = 128, PL_BN = 256;
-
-template <int G>
-__global__ __launch_bounds__(256, 1) void w4a16_prefill_large_kernel(const uint16_t* __restrict__ A,
-                                                                      const uint8_t* __restrict__ wf,
-                                                                      const uint16_t* __restrict__ S,
-                                                                      uint16_t* __restrict__ Y, int M,
-                                                                      int N, int K) {
-    constexpr int NG = 128 / G;
-    constexpr int SLAB = PL_BM * 128;        // halfs per A buffer (32 KB)
-    constexpr int BST = 16384 + 512 * NG;    // bytes per B stage: two fragment blocks + NG scale rows
-    constexpr int BDMA = 4 + 2 * NG;         // DMA instructions per wave for one B stage
-    // One LDS array for A and B: the compiler tells DMA targets from the
-    // buffers being read by their offsets within one array, but not across
-    // two arrays (it would then wait for every DMA before each LDS read).
-    // (Sized for the largest stage, G = 32: an array whose size depends on
-    // the template parameter, passed to the DMA builtin, made the host
-    // compiler drop the kernel's launch stub without a diagnostic.)
-    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * PL_BM * 128 + 3 * (16384 + 512 * 4) / 2];
-    uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + 2 * SLAB);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile (x, y) of
-    // id L has y = L % (row tiles), so the workgroups on one XCD share their
-    // A row tiles in that XCD's L2 and stream distinct B tiles.
-    const int mtiles = (M + PL_BM - 1) / PL_BM;
-    const int L = blockIdx.x;
-    const int m0 = (L % mtiles) * PL_BM, n0 = (L / mtiles) * PL_BN;
-    const int kchunks = K / 128, last = kchunks - 1;
-    const int h = lane >> 5, c32 = lane & 31;
-
-    floatx16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
-
-    // A: this lane's source for wave instruction j is row 4 * (8 * wave + j) + lane / 16,
-    // piece (lane % 16) ^ (row & 15).  Rows >= M repeat row M - 1 (never stored).
-    const int rsub = lane >> 4, pos = lane & 15;
-    auto dma_a = [&](int c, int buf) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = 4 * (8 * wave + j) + rsub;
-            const int gm = m0 + r < M ? m0 + r : M - 1;
-            const uint16_t* src = A + (size_t)gm * K + c * 128 + ((pos ^ (r & 15)) * 8);
-            __builtin_amdgcn_global_load_lds(src, sA + buf * SLAB + (8 * wave + j) * 512, 16, 0, 0);
-        }
-    };
-    // B: the tile's 256 columns are strips n0/16 .. n0/16 + 15, two 8 KB
-    // fragment blocks per chunk (stored one after the other in a stage);
-    // wave w copies strips 4w .. 4w + 3.  Each wave also copies every scale
-    // row of the chunk (512 bytes each; the four copies write identical
-    // bytes), which keeps the per-wave DMA count equal.
-    const uint8_t* wtile = wf + (size_t)(n0 >> 7) * kchunks * 8192;
-    const size_t sb_stride = (size_t)kchunks * 8192;  // between the two fragment blocks
-    auto dma_b = [&](int c, int stage) {
-        uint8_t* dst = sB + stage * BST;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int strip = 4 * wave + j;
-            __builtin_amdgcn_global_load_lds(wtile + (strip >> 3) * sb_stride + (size_t)c * 8192 +
-                                                 (strip & 7) * 1024 + lane * 16,
-                                             dst + strip * 1024, 16, 0, 0);
-        }
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                __builtin_amdgcn_global_load_lds(S + (size_t)(c * NG + g) * N + n0 + 128 * hh + 2 * lane,
-                                                 dst + 16384 + g * 512 + hh * 256, 4, 0, 0);
-    };
-    // this lane's B fragment pieces inside a stage: tile t, k-group parity h,
-    // pieces q = h and q = h + 2 of the strip holding column 64 wave + 32 t + c32
-    auto read_b = [&](const uint8_t* sb, BChunk<2, G>& b) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int colt = wave * 64 + t * 32 + c32;  // column inside the tile
-            const uint8_t* blk = sb + (colt >> 4) * 1024 + (colt & 15) * 16;
-            b.raw[t][0] = *reinterpret_cast<const uintx4*>(blk + 16 * 16 * h);
-            b.raw[t][1] = *reinterpret_cast<const uintx4*>(blk + 16 * 16 * (h + 2));
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-                b.sc[t][g] = reinterpret_cast<const uint16_t*>(sb + 16384)[g * 256 + colt];
-        }
-    };
-    // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
-    // are interleaved with the eight MFMAs of step s (one MFMA, then at most
-    // one LDS read and four VALU ops), so the in-order wave keeps the MFMA
-    // unit busy while it prepares the next operands.
-    auto operands = [&](const uint16_t* sa, const BChunk<2, G>& b, int s, half8 (&a)[4], half8 (&bf)[2]) {
-        const int kg = kgroup_of_step(s, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = i * 32 + c32;
-            a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G>(b, t, s);
-    };
-    // issue(): this trip's DMAs, placed after the LDS reads of step 0 so that
-    // their issue overlaps the read latency
-    auto compute = [&](const uint16_t* sa, const BChunk<2, G>& b, auto issue) {
-        half8 a[4], bf[2];
-        operands(sa, b, 0, a, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        issue();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            half8 an[4], bn[2];
-            if (s < 7) operands(sa, b, s + 1, an, bn);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
-            if (s < 7) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = an[i];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) bf[t] = bn[t];
-        }
-    };
-
-    dma_a(0, 0);
-    dma_b(0, 0);
-    dma_b(last < 1 ? last : 1, 1);
-    wait_vmcnt<0>();
-    __syncthreads();
-    // One trip = one chunk.  Every LDS offset a DMA writes is a compile-time
-    // constant in each trip (A buffer c % 2, B stage c % 3, so six trips per
-    // loop pass): with a run-time buffer or stage index the compiler cannot
-    // tell the DMA target from the buffer being read and waits for the DMA
-    // before every LDS read.
-    // (buf and stage are literals at every call; after inlining they fold)
-    auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
-        const int s2 = (stage + 2) % 3;  // stage of chunk c + 2
-        // B of chunk c goes to registers before this trip's DMAs are issued
-        // (LDS reads of a B stage after them would wait for those DMAs)
-        BChunk<2, G> b;
-        read_b(sB + stage * BST, b);
-        compute(sA + buf * SLAB, b, [&]() {
-            dma_a(c + 1 < last ? c + 1 : last, buf ^ 1);
-            dma_b(c + 2 < last ? c + 2 : last, s2);
-        });
-        // chunk c + 1's A (and, issued before it, its B) has landed; chunk
-        // c + 2's B may still be in flight
-        wait_vmcnt<BDMA>();
-        wait_lgkmcnt0();  // this wave's LDS reads of the buffers refilled next are done
-        __builtin_amdgcn_s_barrier();
-    };
-    for (int c = 0; c < kchunks; c += 6) {
-        trip(c, 0, 0);
-        if (c + 1 < kchunks) trip(c + 1, 1, 1);
-        if (c + 2 < kchunks) trip(c + 2, 0, 2);
-        if (c + 3 < kchunks) trip(c + 3, 1, 0);
-        if (c + 4 < kchunks) trip(c + 4, 0, 1);
-        if (c + 5 < kchunks) trip(c + 5, 1, 2);
-    }
-    // ---- epilogue: Y through an LDS tile in 16-byte row pieces.  A quad
-    // transpose gives each lane four adjacent columns of one row (8 bytes of
-    // fp16), stored into a row-major tile of pitch 576 bytes; then every
-    // thread writes whole 16-byte pieces.  Each wave first drains its last
-    // (unused) prefetches, and the barrier makes sure no DMA still writes LDS.
-    wait_vmcnt<0>();
-    __syncthreads();
-    constexpr int EPW = 144;  // tile pitch in dwords (512 bytes + 64)
-    uint32_t* stile = reinterpret_cast<uint32_t*>(sA);
-    const int q = lane & 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r0 = i * 32 + 8 * g + 4 * h;  // tile row of register 4g
-                const uint32_t v0 = f2h(acc[i][t][4 * g]), v1 = f2h(acc[i][t][4 * g + 1]);
-                const uint32_t v2 = f2h(acc[i][t][4 * g + 2]), v3 = f2h(acc[i][t][4 * g + 3]);
-                uint32_t e0, e1;
-                quad_rows_u16(v0 | (v1 << 16), v2 | (v3 << 16), lane, e0, e1);
-                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wave * 32 + t * 16 + 2 * (c32 >> 2)]) =
-                    uintx2{e0, e1};
-            }
-    __syncthreads();
-    // 128 rows x 32 pieces of 8 outputs (N % 256 == 0: every piece is whole and aligned)
-    const int tid = threadIdx.x;
-#pragma unroll 4
-    for (int p = 0; p < 16; ++p) {
-        const int idx = tid + 256 * p, row = idx >> 5, piece = idx & 31;
-        if (m0 + row < M)
-            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8) =
-                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
-    }
-}
 
 // Tactics (ids in the header): the kernels and launch shapes above, one id
 // each.  validity follows from what each kernel assumes of the shape.
@@ -280,7 +59,7 @@ void launch_w4a16(int tactic, const uint16_t* A, const uint8_t* wf, const uint16
         case QGEMM_W4A16_TACTIC_PREFILL: launch_wq_prefill<4, G>(A, wf, S, N, Y, M, N, K, st); break;
         default: {
             dim3 grid((N / PL_BN) * ((M + PL_BM - 1) / PL_BM));
-            hipLaunchKernelGGL(w4a16_prefill_large_kernel<G>, grid, dim3(256), 0, st, A, wf, S, Y, M, N, K);
+            hipLaunchKernelGGL((wq_prefill_large_kernel<4, G>), grid, dim3(256), 0, st, A, wf, S, N, Y, M, N, K);
         }
     }
 }

@@ -8,7 +8,8 @@
 // int8 fragment layout (2 KB blocks of 16 columns x 128 k, stored v + 128):
 // decode for M <= 16 (twice the weight bytes of W4A16 per column, so the
 // kernel is HBM-bound on a 2x larger stream), mid-M split-K with a
-// workspace, and the 128x128 MFMA prefill kernel for every other M.
+// workspace, and the 128x128 or (with enough tiles) 128x256 MFMA prefill
+// kernels for every other M.
 #include "common.hpp"
 #include "wq_gemm.hpp"
 
@@ -61,12 +62,17 @@ __global__ __launch_bounds__(256) void prepack8_kernel(const int8_t* __restrict_
 template <int G>
 int32_t launch_w8a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
                      int N, int K, float* part, hipStream_t st) {
-    if (M <= 16)
+    if (M <= 16) {
         launch_wq_decode<8, G>(A, wf, S, ldS, Y, M, N, K, st);
-    else if (part)
+    } else if (part) {
         launch_wq_mid<8, G>(A, wf, S, ldS, Y, M, N, K, part, st);
-    else
+    } else if (N % PL_BN != 0 || (long)(N / PL_BN) * ((M + PL_BM - 1) / PL_BM) < 160) {
         launch_wq_prefill<8, G>(A, wf, S, ldS, Y, M, N, K, st);
+    } else {
+        // the 128x256 kernel once it has enough tiles for the chip (the W4A16 rule)
+        dim3 grid((N / PL_BN) * ((M + PL_BM - 1) / PL_BM));
+        hipLaunchKernelGGL((wq_prefill_large_kernel<8, G>), grid, dim3(256), 0, st, A, wf, S, ldS, Y, M, N, K);
+    }
     return qgh::launch_status();
 }
 

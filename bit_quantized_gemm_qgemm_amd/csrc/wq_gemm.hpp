@@ -375,6 +375,262 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
     }
 }
 
+// Large-M prefill: 128x256 output tiles, four waves side by side, each
+// 128 rows x 64 columns (4 x 2 v_mfma_f32_32x32x16_f16 tiles, accumulators in
+// the unified VGPR/AGPR file); one workgroup per CU at M = 2048.  A tile that
+// is wide in N suits weight-only GEMMs: per 128-k chunk a workgroup streams
+// 32 KB of fp16 A and 16 KB (int4) or 32 KB (int8) of B (a 256 x 128 tile
+// would need 64 KB + 8 or 16 KB for the same MFMA work), and each wave owns
+// its columns, so every B element is dequantized once per workgroup.
+//
+// Every load in the main loop is a global -> LDS DMA (no VGPR destinations,
+// no VALU): A (two buffers) and B (fragment blocks plus scale rows; three
+// stages for int4, so B is fetched two chunks ahead, two for int8, whose
+// stages are twice as large).  A wave's A-DMA instruction
+// fills 1 KB of LDS in lane order (four 256-byte rows); the lane that fills
+// position pos of row r fetches piece pos ^ (r & 15) of that row, so the MFMA
+// fragment reads, 16 rows at one k-group, hit 16 distinct 16-byte bank
+// groups.  The loop waits for the DMA it needs with an explicit counter wait
+// and a bare barrier: __syncthreads() would also wait for the B prefetch
+// still in flight.
+constexpr int PL_BM = 128, PL_BN = 256;
+
+template <int WB, int G>
+__global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t* __restrict__ A,
+                                                                   const uint8_t* __restrict__ wf,
+                                                                   const uint16_t* __restrict__ S, int ldS,
+                                                                   uint16_t* __restrict__ Y, int M, int N,
+                                                                   int K) {
+    constexpr int NG = 128 / G;
+    constexpr int KBLK = WFormat<WB>::kBlock;  // bytes per 16-column x 128-k block
+    constexpr int P = WFormat<WB>::kPieces;
+    constexpr int NBST = WB == 4 ? 3 : 2;      // B stages
+    constexpr int SLAB = PL_BM * 128;          // halfs per A buffer (32 KB)
+    constexpr int BST = 16 * KBLK + 512 * NG;  // bytes per B stage: 16 fragment blocks + NG scale rows
+    constexpr int BDMA = 4 * P + 2 * NG;       // DMA instructions per wave for one B stage
+    // One LDS array for A and B: the compiler tells DMA targets from the
+    // buffers being read by their offsets within one array, but not across
+    // two arrays (it would then wait for every DMA before each LDS read).
+    // (One size for every instantiation, the largest: int8 B stages with
+    // G = 32.  An array whose size depends on the template parameters, passed
+    // to the DMA builtin, made the host compiler drop the kernel's launch
+    // stub without a diagnostic.)
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * PL_BM * 128 + 2 * (32768 + 512 * 4) / 2];
+    static_assert(2 * PL_BM * 128 * 2 + NBST * BST <= (int)sizeof(sA), "B stages fit the LDS array");
+    uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + 2 * SLAB);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile (x, y) of
+    // id L has y = L % (row tiles), so the workgroups on one XCD share their
+    // A row tiles in that XCD's L2 and stream distinct B tiles.
+    const int mtiles = (M + PL_BM - 1) / PL_BM;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * PL_BM, n0 = (L / mtiles) * PL_BN;
+    const int kchunks = K / 128, last = kchunks - 1;
+    const int h = lane >> 5, c32 = lane & 31;
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
+
+    // A: this lane's source for wave instruction j is row 4 * (8 * wave + j) + lane / 16,
+    // piece (lane % 16) ^ (row & 15).  Rows >= M repeat row M - 1 (never stored).
+    const int rsub = lane >> 4, pos = lane & 15;
+    auto dma_a = [&](int c, int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 4 * (8 * wave + j) + rsub;
+            const int gm = m0 + r < M ? m0 + r : M - 1;
+            const uint16_t* src = A + (size_t)gm * K + c * 128 + ((pos ^ (r & 15)) * 8);
+            __builtin_amdgcn_global_load_lds(src, sA + buf * SLAB + (8 * wave + j) * 512, 16, 0, 0);
+        }
+    };
+    // B: the tile's 256 columns are strips n0/16 .. n0/16 + 15, two 8-block
+    // fragment tiles per chunk (stored one after the other in a stage);
+    // wave w copies strips 4w .. 4w + 3, 1 KB per DMA instruction.  Each
+    // wave also copies every scale row of the chunk (512 bytes each; the four
+    // copies write identical bytes), which keeps the per-wave DMA count equal.
+    const uint8_t* wtile = wf + (size_t)(n0 >> 7) * kchunks * (8 * KBLK);
+    const size_t sb_stride = (size_t)kchunks * (8 * KBLK);  // between the two fragment tiles
+    auto dma_b = [&](int c, int stage) {
+        uint8_t* dst = sB + stage * BST;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int strip = 4 * wave + j;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                __builtin_amdgcn_global_load_lds(wtile + (strip >> 3) * sb_stride + (size_t)c * (8 * KBLK) +
+                                                     (strip & 7) * KBLK + p * 1024 + lane * 16,
+                                                 dst + strip * KBLK + p * 1024, 16, 0, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                __builtin_amdgcn_global_load_lds(S + (size_t)(c * NG + g) * ldS + n0 + 128 * hh + 2 * lane,
+                                                 dst + 16 * KBLK + g * 512 + hh * 256, 4, 0, 0);
+    };
+    // this lane's B fragment pieces inside a stage: tile t, k-group parity h,
+    // pieces q = h and q = h + 2 of the strip holding column 64 wave + 32 t + c32
+    typedef BChunk<2, G, WB> Chunk;
+    auto read_b = [&](const uint8_t* sb, Chunk& b) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int colt = wave * 64 + t * 32 + c32;  // column inside the tile
+            const uint8_t* blk = sb + (colt >> 4) * KBLK + (colt & 15) * 16;
+#pragma unroll
+            for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    b.raw[t][qi * P + p] = *reinterpret_cast<const uintx4*>(blk + p * 1024 + 16 * 16 * (h + 2 * qi));
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                b.sc[t][g] = reinterpret_cast<const uint16_t*>(sb + 16 * KBLK)[g * 256 + colt];
+        }
+    };
+    // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
+    // are interleaved with the eight MFMAs of step s (one MFMA, then at most
+    // one LDS read and four VALU ops), so the in-order wave keeps the MFMA
+    // unit busy while it prepares the next operands.
+    auto operands = [&](const uint16_t* sa, const Chunk& b, int s, half8 (&a)[4], half8 (&bf)[2]) {
+        const int kg = kgroup_of_step(s, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = i * 32 + c32;
+            a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G, WB>(b, t, s);
+    };
+    // issue(): this trip's DMAs, placed after the LDS reads of step 0 so that
+    // their issue overlaps the read latency
+    auto compute = [&](const uint16_t* sa, const Chunk& b, auto issue) {
+        half8 a[4], bf[2];
+        operands(sa, b, 0, a, bf);
+        __builtin_amdgcn_sched_barrier(0);
+        issue();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            half8 an[4], bn[2];
+            if (s < 7) operands(sa, b, s + 1, an, bn);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
+            if (s < 7) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = an[i];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bf[t] = bn[t];
+        }
+    };
+
+    if constexpr (NBST == 3) {
+        dma_a(0, 0);
+        dma_b(0, 0);
+        dma_b(last < 1 ? last : 1, 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        // One trip = one chunk.  Every LDS offset a DMA writes is a compile-time
+        // constant in each trip (A buffer c % 2, B stage c % 3, so six trips per
+        // loop pass): with a run-time buffer or stage index the compiler cannot
+        // tell the DMA target from the buffer being read and waits for the DMA
+        // before every LDS read.
+        // (buf and stage are literals at every call; after inlining they fold)
+        auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
+            const int s2 = (stage + 2) % 3;  // stage of chunk c + 2
+            // B of chunk c goes to registers before this trip's DMAs are issued
+            // (LDS reads of a B stage after them would wait for those DMAs)
+            Chunk b;
+            read_b(sB + stage * BST, b);
+            compute(sA + buf * SLAB, b, [&]() {
+                dma_a(c + 1 < last ? c + 1 : last, buf ^ 1);
+                dma_b(c + 2 < last ? c + 2 : last, s2);
+            });
+            // chunk c + 1's A (and, issued before it, its B) has landed; chunk
+            // c + 2's B may still be in flight
+            wait_vmcnt<BDMA>();
+            wait_lgkmcnt0();  // this wave's LDS reads of the buffers refilled next are done
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int c = 0; c < kchunks; c += 6) {
+            trip(c, 0, 0);
+            if (c + 1 < kchunks) trip(c + 1, 1, 1);
+            if (c + 2 < kchunks) trip(c + 2, 0, 2);
+            if (c + 3 < kchunks) trip(c + 3, 1, 0);
+            if (c + 4 < kchunks) trip(c + 4, 0, 1);
+            if (c + 5 < kchunks) trip(c + 5, 1, 2);
+        }
+    } else {
+        // two B stages: chunk c + 1's A and B are fetched during chunk c
+        dma_a(0, 0);
+        dma_b(0, 0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        auto trip = [&](int c, int buf) __attribute__((always_inline)) {
+            Chunk b;
+            read_b(sB + buf * BST, b);
+            compute(sA + buf * SLAB, b, [&]() {
+                const int cn = c + 1 < last ? c + 1 : last;
+                dma_a(cn, buf ^ 1);
+                dma_b(cn, buf ^ 1);
+            });
+            wait_vmcnt<0>();
+            wait_lgkmcnt0();
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int c = 0; c < kchunks; c += 2) {
+            trip(c, 0);
+            if (c + 1 < kchunks) trip(c + 1, 1);
+        }
+    }
+    // ---- epilogue: Y through an LDS tile in 16-byte row pieces.  A quad
+    // transpose gives each lane four adjacent columns of one row (8 bytes of
+    // fp16), stored into a row-major tile of pitch 576 bytes; then every
+    // thread writes whole 16-byte pieces.  Each wave first drains its last
+    // (unused) prefetches, and the barrier makes sure no DMA still writes LDS.
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int EPW = 144;  // tile pitch in dwords (512 bytes + 64)
+    uint32_t* stile = reinterpret_cast<uint32_t*>(sA);
+    const int q = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                const uint32_t v0 = f2h(acc[i][t][4 * g]), v1 = f2h(acc[i][t][4 * g + 1]);
+                const uint32_t v2 = f2h(acc[i][t][4 * g + 2]), v3 = f2h(acc[i][t][4 * g + 3]);
+                uint32_t e0, e1;
+                quad_rows_u16(v0 | (v1 << 16), v2 | (v3 << 16), lane, e0, e1);
+                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wave * 32 + t * 16 + 2 * (c32 >> 2)]) =
+                    uintx2{e0, e1};
+            }
+    __syncthreads();
+    // 128 rows x 32 pieces of 8 outputs (N % 256 == 0: every piece is whole and aligned)
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int idx = tid + 256 * p, row = idx >> 5, piece = idx & 31;
+        if (m0 + row < M)
+            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8) =
+                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
+    }
+}
+
 // ------------------------------------------------------------------ mid M
 
 // measured crossover: at M = 192 and 256 the two row passes re-stream the

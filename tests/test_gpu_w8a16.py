@@ -131,6 +131,16 @@ def test_w8a16_prefill(qg, M, K, N, G):
     assert_fp16_close(run(qg, A, W, S, G), oracle.w8a16(A, W, S, G), f"M={M} K={K} N={N} G={G}")
 
 
+@pytest.mark.parametrize("M,K,N,G", [(1200, 384, 4096, 64), (1300, 256, 4096, "K"), (1280, 128, 4096, 32)])
+def test_w8a16_prefill_128x256(qg, M, K, N, G):
+    # at least 160 tiles of 128 x 256: the LDS-DMA kernel with two int8 B stages (ragged M, an odd
+    # chunk count, one chunk, every group form)
+    G = gsize(G, K)
+    A, W, S = qi.w8a16_problem(M, K, N, G, 690 + M + K + G)
+    ref = oracle.w8a16(A, W, S, G)
+    assert_fp16_close(run(qg, A, W, S, G), ref, f"M={M} K={K} N={N} G={G}")
+
+
 def test_w8a16_mid_m_full_shape_sampled(qg):
     M, K, N = 64, 4096, 11008
     G = K
