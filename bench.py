@@ -70,8 +70,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding note in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(each operation would shard by columns, heads or experts); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

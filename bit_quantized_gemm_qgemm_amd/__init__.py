@@ -5,8 +5,7 @@ and takes torch tensors that live on the GPU; the work itself runs in the
 library's kernels on ``torch.cuda.current_stream()``.  Outputs may be passed
 in (no allocation then) or are allocated here with ``torch.empty``.  A non-zero
 status raises ``QGemmError``.  There is no fallback: without the built
-library (``python -m bit_quantized_gemm_qgemm_amd.build`` or
-``__graft_entry__.build()``) every call raises.
+library (``python -m bit_quantized_gemm_qgemm_amd.build``) every call raises.
 """
 import ctypes
 import os
