@@ -41,19 +41,28 @@ __device__ __forceinline__ uint16_t f2h_of_product(float a, float s) {
 //
 // Fragment-layout word: eight offset-binary nibbles u = v + 8 holding the
 // weights v_0..v_7 of eight consecutive k of one column, at nibble positions
-// [v0 v2 v4 v6 v1 v3 v5 v7] (bits 0-3 hold v0).  Masking the low and the
-// high nibble of every byte and splicing each with the byte 0x64 (v_perm_b32)
-// gives fp16 values 1024 + u, exactly, in the order v0..v7:
-//   lo = d & 0x0f0f0f0f holds (v0, v4, v1, v5), hi = (d >> 4) & 0x0f0f0f0f
-//   holds (v2, v6, v3, v7); selector 0x00060004 takes bytes 0 and 2 of the
-//   first operand, 0x00070005 bytes 1 and 3, each under an 0x64.
-// Seven VALU ops per eight weights, all visible to the compiler (inline asm
-// is avoided here: LLVM does not track MFMA hazards across it).
+// [v0 v2 v4 v6 v1 v3 v5 v7] (bits 0-3 hold v0), so that each fp16 pair of the
+// result comes from one nibble of each 16-bit half of a word.  Masking two
+// such nibbles and or-ing in a constant exponent gives the pair exactly: a
+// nibble in bits 0-3 of a half under exponent 0x6400 (1024, unit spacing) is
+// 1024 + u; a nibble in bits 4-7 under 0x5400 (64, spacing 1/16) is 64 + u.
+// Elements 0, 1, 4, 5 of the result are therefore 1024 + u and elements
+// 2, 3, 6, 7 are 64 + u:
+//   (v0, v1) = d & 0x000f000f | 0x64006400,  (v2, v3) = d & 0x00f000f0 | 0x54005400,
+//   and the same two with d >> 8 give (v4, v5) and (v6, v7).
+// Five VALU ops per eight weights: each mask-and-or is one v_bitop3_b32
+// (truth table 0xEA = (a & b) | c; written as & and | the compiler emits two
+// ops, since gfx9 three-operand encodings take no literal constants).  All
+// visible to the compiler (inline asm is avoided here: LLVM does not track
+// MFMA hazards across it).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+    return __builtin_amdgcn_bitop3_b32(a, mask, bits, 0xEA);
+}
 __device__ __forceinline__ half8 raw8(uint32_t d) {
-    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu, e = 0x64646464u;
+    const uint32_t d8 = d >> 8;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 r = {__builtin_amdgcn_perm(lo, e, 0x00060004u), __builtin_amdgcn_perm(hi, e, 0x00060004u),
-                     __builtin_amdgcn_perm(lo, e, 0x00070005u), __builtin_amdgcn_perm(hi, e, 0x00070005u)};
+    const u32x4 r = {and_or(d, 0x000f000fu, 0x64006400u), and_or(d, 0x00f000f0u, 0x54005400u),
+                     and_or(d8, 0x000f000fu, 0x64006400u), and_or(d8, 0x00f000f0u, 0x54005400u)};
     return __builtin_bit_cast(half8, r);
 }
 
@@ -80,6 +89,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Wait until this wave's LDS (and scalar memory) operations are done.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Buffer resource over `bytes` bytes from `base` (raw dword access, no
+// stride): a wave-uniform base for buffer loads, so a DMA's address is a
+// scalar descriptor plus a per-lane 32-bit offset and a scalar offset, with
+// no per-copy vector address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer -> LDS DMA: lane l's BYTES (4 or 16) from voff + soff go to
+// lds + BYTES * l (lds wave-uniform).  Counted by vmcnt like any load.
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_lds(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff,
+                                                uint32_t soff) {
+    static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte copies");
+    // (the size must be a literal for the builtin, also in a template)
+    auto* l = (__attribute__((address_space(3))) void*)lds;
+    if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, soff, 0, 0);
+}
 
 template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) {

@@ -73,17 +73,18 @@ __device__ __forceinline__ float group_sum(float v) {
 // LDS, so there is no barrier before the main loop: it issues the loads of
 // its A slice (rows < M), of its group scales and then all eight weight
 // loads; while the weights stream in it writes A and the scales to LDS and
-// forms the per-(row, group) constant C = bias * sum_k a_k (bias = 1032 for
-// int4, 1152 for int8).  The MFMAs work on the raw fp16 values 1024 + u
-// (seven VALU ops per eight int4 weights, four per eight int8 weights); each
-// group's fp32 partial T becomes acc += s * (T - C).  One A fragment read from
+// forms the per-(row, group) constant C = sum_k bias_k * a_k (bias_k = raw
+// value - weight at k: 1032 or 72 by position for int4, 1152 for int8).  The
+// MFMAs work on the raw fp16 values (five VALU ops per eight int4 weights,
+// four per eight int8 weights); each group's fp32 partial T becomes
+// acc += s * (T - C).  One A fragment read from
 // LDS feeds the MFMAs of all NSW strips.
 template <int WB, int MT, int NSW, int KCW, int G, bool BAL>
 __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ wf, const uint16_t* __restrict__ Sc,
     int ldS, uint16_t* __restrict__ Y, int M, int N, int K) {
     constexpr int P = WFormat<WB>::kPieces;
-    constexpr float BIAS = WFormat<WB>::kBias;
+    constexpr float B0 = WFormat<WB>::kBias0, B1 = WFormat<WB>::kBias1;
     constexpr int WK = 32 / KCW;                 // waves per workgroup (one 4096-k block)
     constexpr int KW = KCW * 128;                // k per wave
     constexpr int LDA = KW + 8;                  // halfs per staged A row (+16 B pad)
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     constexpr int SPL = GW * NSW * 2;            // 16-byte scale pieces per wave (<= 64)
     static_assert(APIECES < 64 || APL * 64 == APIECES, "A staging must tile the wave's slice");
     static_assert(SPL <= 64, "one scale piece per lane");
-    // C = bias * sum_k a_k per (row, group): by VALU during staging, except
+    // C = sum_k bias_k a_k per (row, group): by VALU during staging, except
     // for 16-row tiles over several strips, where an extra MFMA per k-step
     // against a constant bias operand (shared by the strips) is cheaper than
     // sixteen rows of sums and shuffles (measured: M = 16 8.8 us instead of
@@ -177,13 +178,21 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
             if constexpr (CM) {
                 if (idx < APIECES) *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
             } else {
-                float part = 0.f;
+                float part;
+                if constexpr (B0 == B1) {
+                    part = 0.f;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) part += (float)h[j];
-                part = group_sum<GP>(part);
+                    for (int j = 0; j < 8; ++j) part += (float)h[j];
+                    part = group_sum<GP>(part) * B0;
+                } else {
+                    // elements j % 4 < 2 against bias B0, the others against B1
+                    const float p0 = ((float)h[0] + (float)h[1]) + ((float)h[4] + (float)h[5]);
+                    const float p1 = ((float)h[2] + (float)h[3]) + ((float)h[6] + (float)h[7]);
+                    part = group_sum<GP>(p0 * B0 + p1 * B1);
+                }
                 if (idx < APIECES) {
                     *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
-                    if (c8 % GP == 0) L.c[c8 / GP][row] = part * BIAS;
+                    if (c8 % GP == 0) L.c[c8 / GP][row] = part;
                 }
             }
         }
@@ -201,8 +210,8 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
                 const int gl = i * NG + g;
                 floatx4 cc;
                 if constexpr (CM) {
-                    const _Float16 kb = (_Float16)BIAS;
-                    const half8 cb = {kb, kb, kb, kb, kb, kb, kb, kb};
+                    const _Float16 k0 = (_Float16)B0, k1 = (_Float16)B1;
+                    const half8 cb = {k0, k0, k1, k1, k0, k0, k1, k1};
                     cc = zero;
 #pragma unroll
                     for (int kk = g * KKPG; kk < (g + 1) * KKPG; ++kk) cc = mfma16(a[kk], cb, cc);
@@ -383,10 +392,10 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
 // would need 64 KB + 8 or 16 KB for the same MFMA work), and each wave owns
 // its columns, so every B element is dequantized once per workgroup.
 //
-// Every load in the main loop is a global -> LDS DMA (no VGPR destinations,
-// no VALU): A (two buffers) and B (fragment blocks plus scale rows; three
-// stages for int4, so B is fetched two chunks ahead, two for int8, whose
-// stages are twice as large).  A wave's A-DMA instruction
+// Every load in the main loop is a buffer -> LDS DMA (no VGPR destinations,
+// no VALU): A and B (fragment blocks plus scale rows) in three buffers each
+// for int4, so both are fetched two chunks ahead, and two each for int8,
+// whose B stages are twice as large.  A wave's A-DMA instruction
 // fills 1 KB of LDS in lane order (four 256-byte rows); the lane that fills
 // position pos of row r fetches piece pos ^ (r & 15) of that row, so the MFMA
 // fragment reads, 16 rows at one k-group, hit 16 distinct 16-byte bank
@@ -405,6 +414,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     constexpr int KBLK = WFormat<WB>::kBlock;  // bytes per 16-column x 128-k block
     constexpr int P = WFormat<WB>::kPieces;
     constexpr int NBST = WB == 4 ? 3 : 2;      // B stages
+    constexpr int NABUF = WB == 4 ? 3 : 2;     // A buffers
     constexpr int SLAB = PL_BM * 128;          // halfs per A buffer (32 KB)
     constexpr int BST = 16 * KBLK + 512 * NG;  // bytes per B stage: 16 fragment blocks + NG scale rows
     constexpr int BDMA = 4 * P + 2 * NG;       // DMA instructions per wave for one B stage
@@ -415,10 +425,12 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     // G = 32.  An array whose size depends on the template parameters, passed
     // to the DMA builtin, made the host compiler drop the kernel's launch
     // stub without a diagnostic.)
-    __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * PL_BM * 128 + 2 * (32768 + 512 * 4) / 2];
-    static_assert(2 * PL_BM * 128 * 2 + NBST * BST <= (int)sizeof(sA), "B stages fit the LDS array");
-    uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + 2 * SLAB);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[(3 * PL_BM * 128 * 2 + 3 * (16384 + 512 * 4)) / 2];
+    static_assert(NABUF * PL_BM * 128 * 2 + NBST * BST <= (int)sizeof(sA), "A buffers and B stages fit the LDS array");
+    uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + NABUF * SLAB);
+    // (the wave index as a scalar: every DMA's LDS destination and source
+    // base are then scalar arithmetic)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile (x, y) of
     // id L has y = L % (row tiles), so the workgroups on one XCD share their
     // A row tiles in that XCD's L2 and stream distinct B tiles.
@@ -438,23 +450,36 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
 
     // A: this lane's source for wave instruction j is row 4 * (8 * wave + j) + lane / 16,
     // piece (lane % 16) ^ (row & 15).  Rows >= M repeat row M - 1 (never stored).
+    // Every DMA is a buffer load: a wave-uniform descriptor (A rows from m0,
+    // the weight tile, the scale columns from n0), a loop-invariant 32-bit
+    // byte offset per lane and a scalar offset per copy, so issuing a copy
+    // takes no vector instructions.  Offsets stay below 2^31: the A tile
+    // spans 128 rows of K halfs, the weight tile two 128-column strips of K.
     const int rsub = lane >> 4, pos = lane & 15;
+    uint32_t aoff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 4 * (8 * wave + j) + rsub;
+        const int gr = m0 + r < M ? r : M - 1 - m0;
+        aoff[j] = ((uint32_t)gr * (uint32_t)K + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
+    }
+    const int arows = M - m0 < PL_BM ? M - m0 : PL_BM;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (size_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
     auto dma_a = [&](int c, int buf) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = 4 * (8 * wave + j) + rsub;
-            const int gm = m0 + r < M ? m0 + r : M - 1;
-            const uint16_t* src = A + (size_t)gm * K + c * 128 + ((pos ^ (r & 15)) * 8);
-            __builtin_amdgcn_global_load_lds(src, sA + buf * SLAB + (8 * wave + j) * 512, 16, 0, 0);
-        }
+        for (int j = 0; j < 8; ++j) buffer_load_lds<16>(ra, sA + buf * SLAB + (8 * wave + j) * 512, aoff[j], c * 256);
     };
     // B: the tile's 256 columns are strips n0/16 .. n0/16 + 15, two 8-block
     // fragment tiles per chunk (stored one after the other in a stage);
     // wave w copies strips 4w .. 4w + 3, 1 KB per DMA instruction.  Each
     // wave also copies every scale row of the chunk (512 bytes each; the four
     // copies write identical bytes), which keeps the per-wave DMA count equal.
-    const uint8_t* wtile = wf + (size_t)(n0 >> 7) * kchunks * (8 * KBLK);
-    const size_t sb_stride = (size_t)kchunks * (8 * KBLK);  // between the two fragment tiles
+    const uint32_t sb_stride = (uint32_t)kchunks * (8 * KBLK);  // between the two fragment tiles
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(wf + (size_t)(n0 >> 7) * sb_stride, 2u * sb_stride);
+    const uint32_t srows = ldS == 0 ? 1u : (uint32_t)(K / G);
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(S + n0, ((srows - 1u) * (uint32_t)ldS + (uint32_t)PL_BN) * 2u);
+    const uint32_t boff = (uint32_t)lane * 16u, soff = (uint32_t)lane * 4u;
     auto dma_b = [&](int c, int stage) {
         uint8_t* dst = sB + stage * BST;
 #pragma unroll
@@ -462,16 +487,15 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
             const int strip = 4 * wave + j;
 #pragma unroll
             for (int p = 0; p < P; ++p)
-                __builtin_amdgcn_global_load_lds(wtile + (strip >> 3) * sb_stride + (size_t)c * (8 * KBLK) +
-                                                     (strip & 7) * KBLK + p * 1024 + lane * 16,
-                                                 dst + strip * KBLK + p * 1024, 16, 0, 0);
+                buffer_load_lds<16>(rb, dst + strip * KBLK + p * 1024, boff,
+                                    (uint32_t)c * (8 * KBLK) + (strip >> 3) * sb_stride + (strip & 7) * KBLK + p * 1024);
         }
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                __builtin_amdgcn_global_load_lds(S + (size_t)(c * NG + g) * ldS + n0 + 128 * hh + 2 * lane,
-                                                 dst + 16 * KBLK + g * 512 + hh * 256, 4, 0, 0);
+                buffer_load_lds<4>(rs, dst + 16 * KBLK + g * 512 + hh * 256, soff,
+                                   ((uint32_t)(c * NG + g) * (uint32_t)ldS + 128u * hh) * 2u);
     };
     // this lane's B fragment pieces inside a stage: tile t, k-group parity h,
     // pieces q = h and q = h + 2 of the strip holding column 64 wave + 32 t + c32
@@ -494,76 +518,124 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
     // are interleaved with the eight MFMAs of step s (one MFMA, then at most
     // one LDS read and four VALU ops), so the in-order wave keeps the MFMA
-    // unit busy while it prepares the next operands.
-    auto operands = [&](const uint16_t* sa, const Chunk& b, int s, half8 (&a)[4], half8 (&bf)[2]) {
+    // unit busy while it prepares the next operands.  The pipeline runs
+    // across chunks too: the chunk boundary (counter wait and barrier) comes
+    // before the last k-step, whose MFMAs then cover the next chunk's B
+    // register reads, its first operands and the DMA issue.
+    auto a_frags = [&](const uint16_t* sa, int s, half8 (&a)[4]) {
         const int kg = kgroup_of_step(s, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = i * 32 + c32;
             a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
         }
+    };
+    auto operands = [&](const uint16_t* sa, const Chunk& b, int s, half8 (&a)[4], half8 (&bf)[2]) {
+        a_frags(sa, s, a);
 #pragma unroll
         for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G, WB>(b, t, s);
     };
-    // issue(): this trip's DMAs, placed after the LDS reads of step 0 so that
-    // their issue overlaps the read latency
-    auto compute = [&](const uint16_t* sa, const Chunk& b, auto issue) {
-        half8 a[4], bf[2];
-        operands(sa, b, 0, a, bf);
-        __builtin_amdgcn_sched_barrier(0);
-        issue();
-        __builtin_amdgcn_sched_barrier(0);
+    auto mfmas = [&](const half8 (&a)[4], const half8 (&bf)[2]) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
+    };
+    // Pipeline state between trips: chunk c's B registers and the operands of
+    // its first k-step.
+    Chunk b;
+    half8 a[4], bf[2];
+    // One trip = k-steps 0..6 of chunk c, the boundary, then k-step 7 with
+    // chunk c + 1's set-up and the DMAs of chunk c + 2 (A, into the buffer
+    // chunk c was read from) and chunk c + NBST (B, into chunk c's stage,
+    // whose registers were read one trip earlier).  Every LDS offset a DMA
+    // writes is a compile-time constant in each trip (buf and stage are
+    // literals at every call; after inlining they fold): with a run-time
+    // index the compiler cannot tell the DMA target from the buffer being
+    // read and waits for the DMA before every LDS read.  The DMA indexes
+    // clamp to the last chunk: the copies past the end are never read.
+    auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
+        const uint16_t* sa = sA + buf * SLAB;
+#pragma unroll
+        for (int s = 0; s < 7; ++s) {
             half8 an[4], bn[2];
-            if (s < 7) operands(sa, b, s + 1, an, bn);
+            operands(sa, b, s + 1, an, bn);
+            mfmas(a, bf);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
-            if (s < 7) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-                }
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i] = an[i];
 #pragma unroll
             for (int t = 0; t < 2; ++t) bf[t] = bn[t];
         }
+        // chunk c + 1's A and B have landed (with three B stages, chunk
+        // c + 2's B, issued last, may still be in flight); every wave's reads
+        // of chunk c's A buffer and of the B stage refilled below are done
+        wait_vmcnt<NABUF == 3 ? 8 + BDMA : (NBST == 3 ? BDMA : 0)>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int nbuf = buf + 1 < NABUF ? buf + 1 : 0, nstage = stage + 1 < NBST ? stage + 1 : 0;
+        // first half: the LDS reads, then the A DMAs, under four MFMAs
+        read_b(sB + nstage * BST, b);
+        half8 an[4], bn[2];
+        a_frags(sA + nbuf * SLAB, 0, an);
+        dma_a(c + NABUF < last ? c + NABUF : last, buf);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[0][t] = mfma32(a[0], bf[t], acc[0][t]);
+            acc[1][t] = mfma32(a[1], bf[t], acc[1][t]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < 2) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // LDS reads
+            else __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);   // DMA issue
+        }
+        // (a barrier to the scheduler: every A DMA is issued before the B DMAs,
+        // which the counter wait above relies on)
+        __builtin_amdgcn_sched_barrier(0);
+        // second half: the B DMAs and the dequant of chunk c + 1's first step
+        dma_b(c + NBST < last ? c + NBST : last, stage);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bn[t] = b_frag<2, G, WB>(b, t, 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[2][t] = mfma32(a[2], bf[t], acc[2][t]);
+            acc[3][t] = mfma32(a[3], bf[t], acc[3][t]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < 2) __builtin_amdgcn_sched_group_barrier(0x010, 4, 0);  // DMA issue
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = an[i];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bf[t] = bn[t];
     };
 
-    if constexpr (NBST == 3) {
-        dma_a(0, 0);
-        dma_b(0, 0);
-        dma_b(last < 1 ? last : 1, 1);
-        wait_vmcnt<0>();
-        __syncthreads();
-        // One trip = one chunk.  Every LDS offset a DMA writes is a compile-time
-        // constant in each trip (A buffer c % 2, B stage c % 3, so six trips per
-        // loop pass): with a run-time buffer or stage index the compiler cannot
-        // tell the DMA target from the buffer being read and waits for the DMA
-        // before every LDS read.
-        // (buf and stage are literals at every call; after inlining they fold)
-        auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
-            const int s2 = (stage + 2) % 3;  // stage of chunk c + 2
-            // B of chunk c goes to registers before this trip's DMAs are issued
-            // (LDS reads of a B stage after them would wait for those DMAs)
-            Chunk b;
-            read_b(sB + stage * BST, b);
-            compute(sA + buf * SLAB, b, [&]() {
-                dma_a(c + 1 < last ? c + 1 : last, buf ^ 1);
-                dma_b(c + 2 < last ? c + 2 : last, s2);
-            });
-            // chunk c + 1's A (and, issued before it, its B) has landed; chunk
-            // c + 2's B may still be in flight
-            wait_vmcnt<BDMA>();
-            wait_lgkmcnt0();  // this wave's LDS reads of the buffers refilled next are done
-            __builtin_amdgcn_s_barrier();
-        };
+#pragma unroll
+    for (int ab = 0; ab < NABUF; ++ab) dma_a(ab < last ? ab : last, ab);
+#pragma unroll
+    for (int st = 0; st < NBST; ++st) dma_b(st < last ? st : last, st);
+    wait_vmcnt<0>();
+    __syncthreads();
+    read_b(sB, b);
+    operands(sA, b, 0, a, bf);
+    if constexpr (NABUF == 3) {
+        for (int c = 0; c < kchunks; c += 3) {
+            trip(c, 0, 0);
+            if (c + 1 < kchunks) trip(c + 1, 1, 1);
+            if (c + 2 < kchunks) trip(c + 2, 2, 2);
+        }
+    } else if constexpr (NBST == 3) {
         for (int c = 0; c < kchunks; c += 6) {
             trip(c, 0, 0);
             if (c + 1 < kchunks) trip(c + 1, 1, 1);
@@ -573,26 +645,9 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
             if (c + 5 < kchunks) trip(c + 5, 1, 2);
         }
     } else {
-        // two B stages: chunk c + 1's A and B are fetched during chunk c
-        dma_a(0, 0);
-        dma_b(0, 0);
-        wait_vmcnt<0>();
-        __syncthreads();
-        auto trip = [&](int c, int buf) __attribute__((always_inline)) {
-            Chunk b;
-            read_b(sB + buf * BST, b);
-            compute(sA + buf * SLAB, b, [&]() {
-                const int cn = c + 1 < last ? c + 1 : last;
-                dma_a(cn, buf ^ 1);
-                dma_b(cn, buf ^ 1);
-            });
-            wait_vmcnt<0>();
-            wait_lgkmcnt0();
-            __builtin_amdgcn_s_barrier();
-        };
         for (int c = 0; c < kchunks; c += 2) {
-            trip(c, 0);
-            if (c + 1 < kchunks) trip(c + 1, 1);
+            trip(c, 0, 0);
+            if (c + 1 < kchunks) trip(c + 1, 1, 1);
         }
     }
     // ---- epilogue: Y through an LDS tile in 16-byte row pieces.  A quad

@@ -73,7 +73,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
         for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G, WB>(bs[b], 0, s);
     };
     constexpr int NM = NB * NRB;                 // MFMAs per k-step
-    constexpr int VB = WB == 4 ? 15 : 12;        // dequant VALU ops per B fragment
+    constexpr int VB = WB == 4 ? 13 : 12;        // dequant VALU ops per B fragment
     constexpr int VPER = (VB * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
     auto compute = [&](const uint16_t* sa, const Chunk* bs) {
         half8 a[NRB], bf[NB];

@@ -31,17 +31,21 @@ namespace qg {
 
 template <int WB>
 struct WFormat;
+// Raw fp16 value - weight of the raw operands (raw8 / raw8_u8): kBias0 for
+// elements j % 4 < 2 of a k-step's eight, kBias1 for j % 4 >= 2.
 template <>
 struct WFormat<4> {
     static constexpr int kBlock = 1024;   // bytes per 16-column x 128-k block
     static constexpr int kPieces = 1;     // 16-byte pieces per lane position
-    static constexpr float kBias = 1032.f;  // raw fp16 value - weight (1024 + offset 8)
+    static constexpr float kBias0 = 1032.f;  // 1024 + offset 8
+    static constexpr float kBias1 = 72.f;    // 64 + offset 8
 };
 template <>
 struct WFormat<8> {
     static constexpr int kBlock = 2048;
     static constexpr int kPieces = 2;
-    static constexpr float kBias = 1152.f;  // 1024 + offset 128
+    static constexpr float kBias0 = 1152.f;  // 1024 + offset 128
+    static constexpr float kBias1 = 1152.f;
 };
 
 // Byte offset of block (strip = n / 16, chunk = k / 128).
@@ -78,9 +82,9 @@ __device__ __forceinline__ half8 raw_kstep(const uintx4* p, int kk) {
 // multiply by the column's scale.
 template <int WB>
 __device__ __forceinline__ half8 dequant_scaled(half8 raw, _Float16 s) {
-    const _Float16 c = (_Float16)(-WFormat<WB>::kBias);
+    const _Float16 c0 = (_Float16)(-WFormat<WB>::kBias0), c1 = (_Float16)(-WFormat<WB>::kBias1);
     const half8 s8 = {s, s, s, s, s, s, s, s};
-    return (raw + half8{c, c, c, c, c, c, c, c}) * s8;
+    return (raw + half8{c0, c0, c1, c1, c0, c0, c1, c1}) * s8;
 }
 
 __device__ __forceinline__ int kgroup_of_step(int s, int h) { return 4 * (s & 3) + 2 * (s >> 2) + h; }
