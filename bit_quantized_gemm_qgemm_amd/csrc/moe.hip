@@ -299,7 +299,7 @@ extern "C" int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const ui
         return QGEMM_NULL_PTR;
     if (activation != 0 || E > 64 || H == 0 || I == 0 || H % 128 != 0 || I % 128 != 0 ||
         (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30 ||
-        (size_t)T * H >= (size_t)1 << 32 || (size_t)T * topK * I >= (size_t)1 << 32)
+        (size_t)T * H >= (size_t)1 << 31 || (size_t)T * topK * I >= (size_t)1 << 31)
         return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(X, 16) || !qgh::aligned(logits, 2) || !qgh::aligned(w_gate_frag, 16) ||
         !qgh::aligned(w_up_frag, 16) || !qgh::aligned(w_down_frag, 16) || !qgh::aligned(s_gate, 4) ||

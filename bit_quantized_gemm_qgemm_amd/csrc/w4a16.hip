@@ -25,7 +25,7 @@ bool tactic_valid(int tactic, int M, int N, int K) {
     switch (tactic) {
         case QGEMM_W4A16_TACTIC_DECODE_NARROW: return M <= 2;
         case QGEMM_W4A16_TACTIC_DECODE_BALANCED: return M <= 16;
-        case QGEMM_W4A16_TACTIC_SPLITK: return M <= 512 && (size_t)M * K < ((size_t)1 << 32);
+        case QGEMM_W4A16_TACTIC_SPLITK: return M <= 512 && (size_t)M * K < ((size_t)1 << 31);
         case QGEMM_W4A16_TACTIC_PREFILL: return true;
         case QGEMM_W4A16_TACTIC_PREFILL_LARGE: return N % PL_BN == 0;
         default: return false;

@@ -824,7 +824,7 @@ void launch_wq_mid(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int 
 
 // Shapes the mid-M path takes (given enough workspace).
 inline bool mid_path(int M, int K) {
-    return M > 16 && M <= MID_MAX_M && (size_t)M * K < ((size_t)1 << 32);
+    return M > 16 && M <= MID_MAX_M && (size_t)M * K < ((size_t)1 << 31);
 }
 
 }  // namespace

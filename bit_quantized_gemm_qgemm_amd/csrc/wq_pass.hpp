@@ -3,7 +3,7 @@
 // waves owns 128 columns of NB weight
 // matrices (wave w: columns 32w .. 32w + 31) and runs R <= 128 rows of A
 // through them over the 128-k chunks c0 .. c1 - 1, so each weight byte of
-// its range is read once.  A rows reach LDS by global -> LDS DMA, double-
+// its range is read once.  A rows reach LDS by buffer -> LDS DMA, double-
 // buffered and XOR-swizzled; B fragments come straight from the fragment
 // layout into registers one chunk ahead and are dequantized once per k-step
 // for all NRB 32-row MFMA blocks (v_mfma_f32_32x32x16_f16).
@@ -27,7 +27,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
                                             int N, int ldS, int kchunks, int c0, int c1, int ncol0,
                                             int slot0, void* out) {
     typedef BChunk<1, G, WB> Chunk;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int h = lane >> 5, c32 = lane & 31;
     floatx16 acc[NB][NRB];
 #pragma unroll
@@ -40,22 +40,38 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     // DMA: the workgroup's 8 NRB wave instructions each fill 1 KB of LDS =
     // rows 4g .. 4g+3 (g = 2 NRB wave + j); lane l fetches piece
     // (l % 16) ^ (row % 16) of row 4g + l / 16.  Rows >= R repeat row R - 1.
+    // Every load is a buffer load: a wave-uniform descriptor built per chunk
+    // from 64-bit base pointers (A at the chunk's first k, the chunk's
+    // fragment tile, its first scale row), a loop-invariant 32-bit byte
+    // offset per lane, so a load takes no vector address arithmetic.  The
+    // callers keep the A element offsets below 2^31 (byte offsets below
+    // 2^32); the descriptors do not bound.
     const int rsub = lane >> 4, pos = lane & 15;
-    uint32_t src[2 * NRB];  // element offsets from abase
+    uint32_t src[2 * NRB];  // byte offsets from the chunk's first k of abase
 #pragma unroll
     for (int j = 0; j < 2 * NRB; ++j) {
         const int r = 4 * (2 * NRB * wave + j) + rsub;
-        src[j] = row_off(r < R ? r : R - 1) + ((pos ^ (r & 15)) * 8);
+        src[j] = (row_off(r < R ? r : R - 1) + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
     }
     auto dma_a = [&](int c, int buf) {
+        const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(abase + (size_t)c * 128, 0xffffffffu);
 #pragma unroll
         for (int j = 0; j < 2 * NRB; ++j)
-            __builtin_amdgcn_global_load_lds(abase + src[j] + c * 128,
-                                             sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, 16, 0, 0);
+            buffer_load_lds<16>(ra, sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, src[j], 0);
     };
+    constexpr int KBLK = WFormat<WB>::kBlock;
+    constexpr int NGC = 128 / G;  // groups per chunk
+    const size_t wtile = (size_t)(ncol0 >> 7) * kchunks * (8 * KBLK);  // the wave's 128-column tile
+    const uint32_t boff = b_lane_offset<WB>((ncol0 & 127) + (lane & 31), lane);
+    const uint32_t soff = (uint32_t)(lane & 31) * 2u;
     auto load_b = [&](Chunk* bs, int c) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) load_b_chunk<1, G, WB>(bs[b], wf[b], S[b], ldS, kchunks, c, ncol0, lane);
+        for (int b = 0; b < NB; ++b) {
+            const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(wf[b] + wtile + (size_t)c * (8 * KBLK), 0xffffffffu);
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(S[b] + (size_t)c * NGC * ldS + ncol0, 0xffffffffu);
+            load_b_chunk_buf<G, WB>(bs[b], rb, rs, boff, soff, ldS);
+        }
     };
     // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
     // are interleaved with the MFMAs of step s (one MFMA, then at most one

@@ -135,6 +135,37 @@ __device__ __forceinline__ void load_b_chunk(BChunk<WTN, G, WB>& b, const uint8_
     }
 }
 
+// Byte offset, inside one 128-column fragment tile (column nt = 0..127 of
+// the tile), of the first piece this lane loads in a chunk (k-group parity
+// h = lane / 32); piece (qi, p) adds 512 qi + 1024 p.
+template <int WB>
+__device__ __forceinline__ uint32_t b_lane_offset(int nt, int lane) {
+    constexpr uint32_t B = WFormat<WB>::kBlock;
+    return ((uint32_t)nt >> 4) * B + (((uint32_t)nt & 15u) + 16u * ((uint32_t)lane >> 5)) * 16u;
+}
+
+// load_b_chunk for one 32-column tile by buffer loads: rb is a descriptor
+// from the chunk's fragment tile (8 blocks), rs one from the chunk's first
+// scale row at the tile's first column; boff = b_lane_offset of the lane's
+// column, soff = 2 * (its column - the first).  Group g's scale row is
+// g * ldS elements further (a scalar offset), so a load takes no vector
+// address arithmetic, and no offset exceeds one chunk of one tile.
+template <int G, int WB>
+__device__ __forceinline__ void load_b_chunk_buf(BChunk<1, G, WB>& b, __amdgpu_buffer_rsrc_t rb,
+                                                 __amdgpu_buffer_rsrc_t rs, uint32_t boff, uint32_t soff,
+                                                 int ldS) {
+    constexpr int P = WFormat<WB>::kPieces;
+    constexpr int NG = BChunk<1, G, WB>::NG;
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+            b.raw[0][qi * P + p] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff + 512u * qi + 1024u * p, 0, 2);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        b.sc[0][g] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, (uint32_t)g * (uint32_t)ldS * 2u, 0);
+}
+
 template <int WTN, int G, int WB = 4>
 __device__ __forceinline__ half8 b_frag(const BChunk<WTN, G, WB>& b, int t, int s) {
     constexpr int P = WFormat<WB>::kPieces;

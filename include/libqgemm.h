@@ -90,7 +90,7 @@ QGEMM_API int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag,
                             void* stream);
 
 /* Workspace bytes qgemm_w4a16 uses for this shape: for 16 < M <= 128 (and
-   M*K < 2^32) the fp32 partial sums of its split-K path,
+   M*K < 2^31) the fp32 partial sums of its split-K path,
    S * M * N * 4 bytes with S = max(1, min(floor(512 / (N/128)), K/128, 16)); 0 for
    every other shape and for invalid arguments. */
 QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
@@ -124,7 +124,7 @@ QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const ui
  *   1 decode, one 16-column strip per workgroup      valid for M <= 2
  *   2 decode, balanced ranges of up to 3 strips      valid for M <= 16
  *   3 split-K with fp32 partials + ordered reduction valid for M <= 512 and
- *     M*K < 2^32; needs qgemm_w4a16_tactic_workspace_bytes() of workspace
+ *     M*K < 2^31; needs qgemm_w4a16_tactic_workspace_bytes() of workspace
  *   4 prefill, 128x128 tiles                         valid for every M
  *   5 prefill, 128x256 tiles (LDS DMA)               valid for N % 256 == 0
  * The library keeps no tactic state: a caller that autotunes keeps the
@@ -312,7 +312,7 @@ QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int3
    Y: fp16 [T][H] (output); topk_ids: int32 [T][topK] (output);
    topk_w: fp32 [T][topK] (output).
    Supported: H % 128 == 0, I % 128 == 0, G in {32, 64, 128}, 1 <= topK <= E
-   <= 64, activation == 0, T*H < 2^32 and T*topK*I < 2^32.  T == 0 is a
+   <= 64, activation == 0, T*H < 2^31 and T*topK*I < 2^31.  T == 0 is a
    successful no-op. */
 QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
                   const uint8_t* w_up_frag, const uint8_t* w_down_frag, const uint16_t* s_gate,
