@@ -415,6 +415,8 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     constexpr int P = WFormat<WB>::kPieces;
     constexpr int NBST = WB == 4 ? 3 : 2;      // B stages
     constexpr int NABUF = WB == 4 ? 3 : 2;     // A buffers
+    // three buffers of each: a chunk's copies can be spread over the k-steps
+    constexpr bool SPREAD = NABUF == 3 && NBST == 3;
     constexpr int SLAB = PL_BM * 128;          // halfs per A buffer (32 KB)
     constexpr int BST = 16 * KBLK + 512 * NG;  // bytes per B stage: 16 fragment blocks + NG scale rows
     constexpr int BDMA = 4 * P + 2 * NG;       // DMA instructions per wave for one B stage
@@ -497,6 +499,22 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
                 buffer_load_lds<4>(rs, dst + 16 * KBLK + g * 512 + hh * 256, soff,
                                    ((uint32_t)(c * NG + g) * (uint32_t)ldS + 128u * hh) * 2u);
     };
+    // DMA instruction i of chunk c (i < 8: A; then the B blocks, then the
+    // scale rows), for issuing a chunk's copies a few at a time
+    constexpr int NDMA = 8 + BDMA;
+    auto dma_one = [&](int c, int buf, int stage, int i) __attribute__((always_inline)) {
+        if (i < 8) {
+            buffer_load_lds<16>(ra, sA + buf * SLAB + (8 * wave + i) * 512, aoff[i], c * 256);
+        } else if (i < 8 + 4 * P) {
+            const int strip = 4 * wave + (i - 8) / P, p = (i - 8) % P;
+            buffer_load_lds<16>(rb, sB + stage * BST + strip * KBLK + p * 1024, boff,
+                                (uint32_t)c * (8 * KBLK) + (strip >> 3) * sb_stride + (strip & 7) * KBLK + p * 1024);
+        } else {
+            const int g = (i - 8 - 4 * P) / 2, hh = (i - 8 - 4 * P) % 2;
+            buffer_load_lds<4>(rs, sB + stage * BST + 16 * KBLK + g * 512 + hh * 256, soff,
+                               ((uint32_t)(c * NG + g) * (uint32_t)ldS + 128u * hh) * 2u);
+        }
+    };
     // this lane's B fragment pieces inside a stage: tile t, k-group parity h,
     // pieces q = h and q = h + 2 of the strip holding column 64 wave + 32 t + c32
     typedef BChunk<2, G, WB> Chunk;
@@ -556,15 +574,27 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     // clamp to the last chunk: the copies past the end are never read.
     auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
         const uint16_t* sa = sA + buf * SLAB;
+        // SPREAD: chunk c + 2's copies go out two or three per k-step, into
+        // the buffer and stage chunk c - 1 used (free since the previous
+        // boundary); issued as one burst, the four waves' copies queue up in
+        // the address unit and each wave stalls at issue while the matrix
+        // unit runs dry
+        const int cd = c + 2 < last ? c + 2 : last;
+        const int dbuf = buf == 0 ? NABUF - 1 : buf - 1, dstage = stage == 0 ? NBST - 1 : stage - 1;
 #pragma unroll
         for (int s = 0; s < 7; ++s) {
             half8 an[4], bn[2];
             operands(sa, b, s + 1, an, bn);
+            if constexpr (SPREAD) {
+#pragma unroll
+                for (int i = s * NDMA / 7; i < (s + 1) * NDMA / 7; ++i) dma_one(cd, dbuf, dstage, i);
+            }
             mfmas(a, bf);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                 if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                if (SPREAD && (q == 1 || q == 3 || q == 5)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
             }
 #pragma unroll
@@ -572,10 +602,11 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
 #pragma unroll
             for (int t = 0; t < 2; ++t) bf[t] = bn[t];
         }
-        // chunk c + 1's A and B have landed (with three B stages, chunk
-        // c + 2's B, issued last, may still be in flight); every wave's reads
-        // of chunk c's A buffer and of the B stage refilled below are done
-        wait_vmcnt<NABUF == 3 ? 8 + BDMA : (NBST == 3 ? BDMA : 0)>();
+        // chunk c + 1's A and B have landed (the copies this trip issued, or
+        // with three B stages and no spreading chunk c + 2's B, may still be
+        // in flight); every wave's reads of chunk c's A buffer and of the B
+        // stage refilled below are done
+        wait_vmcnt<SPREAD ? NDMA : (NBST == 3 ? BDMA : 0)>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -584,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         read_b(sB + nstage * BST, b);
         half8 an[4], bn[2];
         a_frags(sA + nbuf * SLAB, 0, an);
-        dma_a(c + NABUF < last ? c + NABUF : last, buf);
+        if constexpr (!SPREAD) dma_a(c + NABUF < last ? c + NABUF : last, buf);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             acc[0][t] = mfma32(a[0], bf[t], acc[0][t]);
@@ -600,7 +631,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         // which the counter wait above relies on)
         __builtin_amdgcn_sched_barrier(0);
         // second half: the B DMAs and the dequant of chunk c + 1's first step
-        dma_b(c + NBST < last ? c + NBST : last, stage);
+        if constexpr (!SPREAD) dma_b(c + NBST < last ? c + NBST : last, stage);
 #pragma unroll
         for (int t = 0; t < 2; ++t) bn[t] = b_frag<2, G, WB>(b, t, 0);
 #pragma unroll
@@ -621,10 +652,12 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         for (int t = 0; t < 2; ++t) bf[t] = bn[t];
     };
 
+    // chunks 0 .. NABUF - 1 (SPREAD: 0 and 1; the first trip fetches chunk 2)
+    constexpr int PRE = SPREAD ? 2 : NABUF;
 #pragma unroll
-    for (int ab = 0; ab < NABUF; ++ab) dma_a(ab < last ? ab : last, ab);
+    for (int ab = 0; ab < PRE; ++ab) dma_a(ab < last ? ab : last, ab);
 #pragma unroll
-    for (int st = 0; st < NBST; ++st) dma_b(st < last ? st : last, st);
+    for (int st = 0; st < (SPREAD ? 2 : NBST); ++st) dma_b(st < last ? st : last, st);
     wait_vmcnt<0>();
     __syncthreads();
     read_b(sB, b);
