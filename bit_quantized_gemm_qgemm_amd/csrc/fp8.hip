@@ -181,6 +181,8 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
     constexpr int SL = FB * 128;  // bytes per operand buffer (256 rows x 128 k)
     // A0, A1, W0, W1; after the k loop the fp16 output tile (256 rows x 576 bytes)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * SL + 16384];
+    // (the wave index from threadIdx.x: its known range lets the compiler
+    // tell the copies' LDS targets from the buffer being read)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     // tile (x, y) of workgroup L: y = L % (row tiles), so the workgroups on
@@ -213,10 +215,13 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
         offa[j] = (uint32_t)(m0 + r < M ? m0 + r : M - 1) * (uint32_t)K + piece;
         offw[j] = (uint32_t)(n0 + r < N ? n0 + r : N - 1) * (uint32_t)K + piece;
     }
-    auto dma = [&](const uint8_t* base, const uint32_t (&off)[4], uint8_t* dst) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_global_load_lds(base + off[j], dst + (4 * wave + j) * 1024, 16, 0, 0);
+    // Buffer -> LDS copies (wave-uniform descriptors over A and W, the chunk's
+    // k offset as a scalar offset: no vector address arithmetic per copy).
+    // Copy i of a chunk: i < 4 A, else W.
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A, 0xffffffffu), rw = buffer_rsrc(W, 0xffffffffu);
+    auto dma_one = [&](int c, int buf, int i) __attribute__((always_inline)) {
+        if (i < 4) buffer_load_lds<16>(ra, lds + buf * SL + (4 * wave + i) * 1024, offa[i], (uint32_t)c * 128u);
+        else buffer_load_lds<16>(rw, lds + (2 + buf) * SL + (4 * wave + i - 4) * 1024, offw[i - 4], (uint32_t)c * 128u);
     };
     // operand of row r for 64-k step s: bytes k = 64 s + 32 h .. + 31 = pieces
     // 4 s + 2 h and 4 s + 2 h + 1 of the row
@@ -232,11 +237,15 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
 #pragma unroll
         for (int t = 0; t < 2; ++t) b[t] = frag(wb, wn * 64 + t * 32 + c32, s);
     };
-    // two 64-k steps per chunk; the operand reads of step 1 are interleaved
-    // with the MFMAs of step 0
-    auto compute = [&](const uint8_t* ab, const uint8_t* wb) {
+    // two 64-k steps per chunk; the operand reads of step 1 and the eight
+    // copies of the next chunk are interleaved with the MFMAs of step 0
+    // (issued as one burst, the copies of the eight waves queue at the address
+    // unit and the waves stall at issue)
+    auto compute = [&](const uint8_t* ab, const uint8_t* wb, int cn, int nbuf) {
         intx8 a[4], b[2], an[4], bn[2];
         operands(ab, wb, 0, a, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma_one(cn, nbuf, i);
         operands(ab, wb, 1, an, bn);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -246,11 +255,13 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -258,8 +269,8 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
             for (int t = 0; t < 2; ++t) acc[i][t] = mfma_fp8(an[i], bn[t], acc[i][t]);
     };
 
-    dma(A, offa, lds);
-    dma(W, offw, lds + 2 * SL);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_one(0, 0, i);
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
@@ -269,9 +280,7 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
     // DMA targets from the buffers being read)
     auto trip = [&](int c, int buf) __attribute__((always_inline)) {
         const int cn = c + 1 < last ? c + 1 : last;
-        dma(A + cn * 128, offa, lds + (buf ^ 1) * SL);
-        dma(W + cn * 128, offw, lds + (2 + (buf ^ 1)) * SL);
-        compute(lds + buf * SL, lds + (2 + buf) * SL);
+        compute(lds + buf * SL, lds + (2 + buf) * SL, cn, buf ^ 1);
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();

@@ -182,6 +182,8 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
     int8_t* __restrict__ Y, int32_t* __restrict__ acc_out, int M, int N, int K) {
     constexpr int SL = LB * 128;  // bytes per operand buffer
     __shared__ __attribute__((aligned(1024))) int8_t lds[4 * SL];  // A0, A1, W0, W1
+    // (the wave index from threadIdx.x: its known range lets the compiler
+    // tell the copies' LDS targets from the buffer being read)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     // tile (x, y) of workgroup L: y = L % (row tiles), so workgroups on one
@@ -213,10 +215,13 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
         offa[j] = (uint32_t)(m0 + r < M ? m0 + r : M - 1) * (uint32_t)K + piece;
         offw[j] = (uint32_t)(n0 + r) * (uint32_t)K + piece;
     }
-    auto dma = [&](const int8_t* base, const uint32_t (&off)[4], int8_t* dst) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_global_load_lds(base + off[j], dst + (4 * wave + j) * 1024, 16, 0, 0);
+    // Buffer -> LDS copies (wave-uniform descriptors over A and W, the chunk's
+    // k offset as a scalar offset: no vector address arithmetic per copy).
+    // Copy i of a chunk: i < 4 A, else W.
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A, 0xffffffffu), rw = buffer_rsrc(W, 0xffffffffu);
+    auto dma_one = [&](int c, int buf, int i) __attribute__((always_inline)) {
+        if (i < 4) buffer_load_lds<16>(ra, lds + buf * SL + (4 * wave + i) * 1024, offa[i], (uint32_t)c * 128u);
+        else buffer_load_lds<16>(rw, lds + (2 + buf) * SL + (4 * wave + i - 4) * 1024, offw[i - 4], (uint32_t)c * 128u);
     };
     auto operands = [&](const int8_t* ab, const int8_t* wb, int s, intx4 (&a)[4], intx4 (&b)[2]) {
         const int p = 2 * s + h;  // 16-byte piece of k = 32 s + 16 h .. + 15
@@ -231,12 +236,19 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
             b[t] = *reinterpret_cast<const intx4*>(wb + r * 128 + ((p ^ ((r >> 1) & 7)) * 16));
         }
     };
-    auto compute = [&](const int8_t* ab, const int8_t* wb) {
+    // The next chunk's eight copies go out three, three and two per k-step
+    // under the MFMAs of steps 0..2 (issued as one burst, the copies of the
+    // eight waves queue at the address unit and the waves stall at issue).
+    auto compute = [&](const int8_t* ab, const int8_t* wb, int cn, int nbuf) {
         intx4 a[4], b[2];
         operands(ab, wb, 0, a, b);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             intx4 an[4], bn[2];
+            if (s < 3) {
+#pragma unroll
+                for (int i = s * 8 / 3; i < (s + 1) * 8 / 3; ++i) dma_one(cn, nbuf, i);
+            }
             if (s < 3) operands(ab, wb, s + 1, an, bn);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -247,6 +259,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
                 for (int q = 0; q < 6; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    if (q < 3) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
                 }
             }
 #pragma unroll
@@ -256,8 +269,8 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
         }
     };
 
-    dma(A, offa, lds);
-    dma(W, offw, lds + 2 * SL);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_one(0, 0, i);
     wait_vmcnt<0>();
     __syncthreads();
     // one trip per chunk: DMA of chunk c + 1 into the idle buffers, MFMAs on
@@ -266,9 +279,7 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
     // DMA targets from the buffers being read)
     auto trip = [&](int c, int buf) __attribute__((always_inline)) {
         const int cn = c + 1 < last ? c + 1 : last;
-        dma(A + cn * 128, offa, lds + (buf ^ 1) * SL);
-        dma(W + cn * 128, offw, lds + (2 + (buf ^ 1)) * SL);
-        compute(lds + buf * SL, lds + (2 + buf) * SL);
+        compute(lds + buf * SL, lds + (2 + buf) * SL, cn, buf ^ 1);
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
