@@ -9,6 +9,8 @@
 // for all NRB 32-row MFMA blocks (v_mfma_f32_32x32x16_f16).
 #pragma once
 
+#include <type_traits>
+
 #include "wq_tile.hpp"
 
 namespace qg {
@@ -27,7 +29,9 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
                                             int N, int ldS, int kchunks, int c0, int c1, int ncol0,
                                             int slot0, void* out) {
     typedef BChunk<1, G, WB> Chunk;
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    // (the wave index from threadIdx.x: its known range lets the compiler
+    // tell the copies' LDS targets from the buffer being read)
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h = lane >> 5, c32 = lane & 31;
     floatx16 acc[NB][NRB];
 #pragma unroll
@@ -53,15 +57,20 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
         const int r = 4 * (2 * NRB * wave + j) + rsub;
         src[j] = (row_off(r < R ? r : R - 1) + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
     }
-    auto dma_a = [&](int c, int buf) {
+    auto dma_a_one = [&](int c, int buf, int j) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(abase + (size_t)c * 128, 0xffffffffu);
+        buffer_load_lds<16>(ra, sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, src[j], 0);
+    };
+    auto dma_a = [&](int c, int buf) {
 #pragma unroll
-        for (int j = 0; j < 2 * NRB; ++j)
-            buffer_load_lds<16>(ra, sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, src[j], 0);
+        for (int j = 0; j < 2 * NRB; ++j) dma_a_one(c, buf, j);
     };
     constexpr int KBLK = WFormat<WB>::kBlock;
     constexpr int NGC = 128 / G;  // groups per chunk
-    const size_t wtile = (size_t)(ncol0 >> 7) * kchunks * (8 * KBLK);  // the wave's 128-column tile
+    // (descriptor bases from the wave-uniform column as a scalar: a base the
+    // compiler takes for per-lane would turn every buffer load into a loop)
+    const int ncolu = __builtin_amdgcn_readfirstlane(ncol0);
+    const size_t wtile = (size_t)(ncolu >> 7) * kchunks * (8 * KBLK);  // the wave's 128-column tile
     const uint32_t boff = b_lane_offset<WB>((ncol0 & 127) + (lane & 31), lane);
     const uint32_t soff = (uint32_t)(lane & 31) * 2u;
     auto load_b = [&](Chunk* bs, int c) {
@@ -69,7 +78,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
         for (int b = 0; b < NB; ++b) {
             const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(wf[b] + wtile + (size_t)c * (8 * KBLK), 0xffffffffu);
             const __amdgpu_buffer_rsrc_t rs =
-                buffer_rsrc(S[b] + (size_t)c * NGC * ldS + ncol0, 0xffffffffu);
+                buffer_rsrc(S[b] + (size_t)c * NGC * ldS + ncolu, 0xffffffffu);
             load_b_chunk_buf<G, WB>(bs[b], rb, rs, boff, soff, ldS);
         }
     };
@@ -91,12 +100,24 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     constexpr int NM = NB * NRB;                 // MFMAs per k-step
     constexpr int VB = WB == 4 ? 13 : 12;        // dequant VALU ops per B fragment
     constexpr int VPER = (VB * NB + NM - 1) / NM;  // dequant VALU ops placed after each MFMA
-    auto compute = [&](const uint16_t* sa, const Chunk* bs) {
+    // With a next chunk (tag NEXT: std::true_type), its A copies go out under
+    // k-steps 0..3 instead of as one burst before the first step (the copies
+    // of the workgroup's waves would queue at the address unit while the
+    // waves stall at issue).  Each copy comes before the step's operand reads
+    // in program order: the compiler keeps copies behind earlier reads of LDS
+    // it cannot tell apart.  (The B register loads stay ahead of the steps:
+    // placed among them, the compiler waited for them at once.)
+    auto compute = [&](const uint16_t* sa, const Chunk* bs, auto next, int cn, int nbuf) {
+        constexpr bool NEXT = decltype(next)::value;
         half8 a[NRB], bf[NB];
         operands(sa, bs, 0, a, bf);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             half8 an[NRB], bn[NB];
+            if (NEXT && s < 4) {
+#pragma unroll
+                for (int j = s * 2 * NRB / 4; j < (s + 1) * 2 * NRB / 4; ++j) dma_a_one(cn, nbuf, j);
+            }
             if (s < 7) operands(sa, bs, s + 1, an, bn);
 #pragma unroll
             for (int i = 0; i < NRB; ++i)
@@ -106,6 +127,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
 #pragma unroll
                 for (int q = 0; q < NM; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (NEXT && q < 2 && s < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
                     if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
                     __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
                 }
@@ -135,11 +157,9 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     __builtin_amdgcn_s_barrier();
     auto trip = [&](int c, int abuf, const Chunk* bc, Chunk* bn) __attribute__((always_inline)) {
         const int cn = c + 1 < c1 ? c + 1 : last;
-        dma_a(cn, abuf ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
         load_b(bn, cn);
         __builtin_amdgcn_sched_barrier(0);
-        compute(sA + abuf * XP_SLAB, bc);
+        compute(sA + abuf * XP_SLAB, bc, std::true_type{}, cn, abuf ^ 1);
         wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
@@ -151,7 +171,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
         trip(c, 0, b0, b1);
         trip(c + 1, 1, b1, b0);
     }
-    if (c < c1) compute(sA, b0);
+    if (c < c1) compute(sA, b0, std::false_type{}, 0, 1);
 
     const int col = ncol0 + c32;
 #pragma unroll
