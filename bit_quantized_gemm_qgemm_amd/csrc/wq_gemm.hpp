@@ -415,8 +415,10 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     constexpr int P = WFormat<WB>::kPieces;
     constexpr int NBST = WB == 4 ? 3 : 2;      // B stages
     constexpr int NABUF = WB == 4 ? 3 : 2;     // A buffers
-    // three buffers of each: a chunk's copies can be spread over the k-steps
+    // three buffers of each: a chunk's copies can be spread over the k-steps;
+    // with two of each only the B copies can (BSPREAD), A waits for the boundary
     constexpr bool SPREAD = NABUF == 3 && NBST == 3;
+    constexpr bool BSPREAD = !SPREAD && NBST == 2;
     constexpr int SLAB = PL_BM * 128;          // halfs per A buffer (32 KB)
     constexpr int BST = 16 * KBLK + 512 * NG;  // bytes per B stage: 16 fragment blocks + NG scale rows
     constexpr int BDMA = 4 * P + 2 * NG;       // DMA instructions per wave for one B stage
@@ -589,12 +591,17 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
 #pragma unroll
                 for (int i = s * NDMA / 7; i < (s + 1) * NDMA / 7; ++i) dma_one(cd, dbuf, dstage, i);
             }
+            if constexpr (BSPREAD) {
+                // chunk c + 2's B into chunk c's stage (its registers were read one trip earlier)
+#pragma unroll
+                for (int i = 8 + s * BDMA / 7; i < 8 + (s + 1) * BDMA / 7; ++i) dma_one(cd, buf, stage, i);
+            }
             mfmas(a, bf);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                 if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                if (SPREAD && (q == 1 || q == 3 || q == 5)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
+                if ((SPREAD || BSPREAD) && (q == 1 || q == 3 || q == 5)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
             }
 #pragma unroll
@@ -606,7 +613,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         // with three B stages and no spreading chunk c + 2's B, may still be
         // in flight); every wave's reads of chunk c's A buffer and of the B
         // stage refilled below are done
-        wait_vmcnt<SPREAD ? NDMA : (NBST == 3 ? BDMA : 0)>();
+        wait_vmcnt<SPREAD ? NDMA : (BSPREAD || NBST == 3 ? BDMA : 0)>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -631,7 +638,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         // which the counter wait above relies on)
         __builtin_amdgcn_sched_barrier(0);
         // second half: the B DMAs and the dequant of chunk c + 1's first step
-        if constexpr (!SPREAD) dma_b(c + NBST < last ? c + NBST : last, stage);
+        if constexpr (!SPREAD && !BSPREAD) dma_b(c + NBST < last ? c + NBST : last, stage);
 #pragma unroll
         for (int t = 0; t < 2; ++t) bn[t] = b_frag<2, G, WB>(b, t, 0);
 #pragma unroll
