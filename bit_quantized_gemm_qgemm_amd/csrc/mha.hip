@@ -149,15 +149,25 @@ __global__ __launch_bounds__(64 * NW, 2) void mha_int8_kernel(
         }
         return acc;
     };
-    // Runs body(kb, buf) over every block with the staging pipeline around it.
-    auto sweep = [&](bool with_v, auto body) {
+    // Runs full(kb, buf) over the blocks below nfull and masked(kb, buf) over
+    // the rest, with the staging pipeline around them.  Two loops rather than
+    // one with a branch per block: the accumulators then stay in place (with
+    // a join in the loop body the compiler copied all of them every block).
+    auto sweep = [&](bool with_v, auto full, auto masked) {
         Stage st;
         load(st, 0, with_v);
         store(st, 0, with_v);
         barrier();
-        for (int kb = 0; kb < nkb; ++kb) {
+        int kb = 0;
+        for (; kb < nfull; ++kb) {
             load(st, kb + 1 < nkb ? kb + 1 : kb, with_v);
-            body(kb, kb & 1);
+            full(kb, kb & 1);
+            store(st, (kb + 1) & 1, with_v);
+            barrier();
+        }
+        for (; kb < nkb; ++kb) {
+            load(st, kb + 1 < nkb ? kb + 1 : kb, with_v);
+            masked(kb, kb & 1);
             store(st, (kb + 1) & 1, with_v);
             barrier();
         }
@@ -202,10 +212,7 @@ __global__ __launch_bounds__(64 * NW, 2) void mha_int8_kernel(
         }
         lsum += part;
     };
-    sweep(false, [&](int kb, int buf) {
-        if (kb >= nfull) pass1(Masked(), kb, buf);
-        else pass1(Full(), kb, buf);
-    });
+    sweep(false, [&](int kb, int buf) { pass1(Full(), kb, buf); }, [&](int kb, int buf) { pass1(Masked(), kb, buf); });
     const float l = lsum + __shfl_xor(lsum, 32);
     const float cq = 127.0f / l;  // code = rne(e * fl(127 / l))
 
@@ -238,10 +245,7 @@ __global__ __launch_bounds__(64 * NW, 2) void mha_int8_kernel(
             oacc[t] = mfma_i8(a, pb, oacc[t]);
         }
     };
-    sweep(true, [&](int kb, int buf) {
-        if (kb >= nfull) pass2(Masked(), kb, buf);
-        else pass2(Full(), kb, buf);
-    });
+    sweep(true, [&](int kb, int buf) { pass2(Full(), kb, buf); }, [&](int kb, int buf) { pass2(Masked(), kb, buf); });
 
     // ---- epilogue: t = fl(acc) * pv_scale (+ bias), code = clamp(rne(t * out_mult), +-127);
     // registers 4g .. 4g + 3 of d tile t are channels 32 t + 8 g + 4 (lane / 32) + 0..3
