@@ -252,3 +252,15 @@ def test_moe_validation(L):
     assert call(ws=None) == 1
     assert call(ws=FAKE + 16) == 3
     assert call(wsb=16) == 4
+    # A element offsets must stay below 2^31 (32-bit byte offsets of the buffer loads)
+    assert call(T=1 << 19, H=4096) == 5                    # T*H = 2^31
+    assert call(T=1 << 14, topK=2, I=1 << 16) == 5         # T*topK*I = 2^31
+
+
+def test_splitk_tactic_limit(L):
+    # the split-K tactic needs M*K < 2^31 (32-bit byte offsets of its A loads)
+    buf = (ctypes.c_int32 * 8)()
+    n = L.qgemm_w4a16_tactics(64, 4096, (1 << 25) - 128, 128, buf, 8)
+    assert 3 in list(buf)[:n]
+    n = L.qgemm_w4a16_tactics(64, 4096, 1 << 25, 128, buf, 8)
+    assert 3 not in list(buf)[:n]
