@@ -80,7 +80,7 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n) {
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (s_waitcnt with only the vector-memory counter constrained).  Loads,
-// including global -> LDS DMA, complete in issue order.
+// including global or buffer -> LDS DMA, complete in issue order.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -17,7 +17,7 @@
 // step, the same (lane half, byte) -> k assignment for both operands, so the
 // K-contiguous rows of A [M][K] and W [N][K] feed it directly.  The tiling is
 // that of the int8 W8A8 kernel: 256x256 output tiles, eight waves (two per
-// SIMD) of 128x64, operands by global -> LDS DMA (two buffers each, one LDS
+// SIMD) of 128x64, operands by buffer -> LDS DMA (two buffers each, one LDS
 // array, compile-time offsets), XOR-swizzled 16-byte pieces, software-
 // pipelined steps.
 #include "common.hpp"

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 // columns 32w .. 32w + 31 of the tile for all rows: it dequantizes its B
 // fragments once per k-step and feeds them to the NRB 32-row MFMA blocks.
 // A rows (gathered tokens for gate/up, contiguous h rows for down) go
-// global -> LDS by DMA, double-buffered, with the XOR swizzle of the prefill
+// buffer -> LDS by DMA, double-buffered, with the XOR swizzle of the prefill
 // kernel; B fragments are prefetched one 128-k chunk ahead in registers.
 // The down projection splits K over KS workgroups (fp32 partials, added in
 // split order by the combine) so that it has enough workgroups.

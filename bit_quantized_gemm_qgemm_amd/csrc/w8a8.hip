@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
 // Large shapes (M >= 256, N % 256 == 0): 256x256 output tiles, eight waves
 // (two per SIMD) of 128x64 (4 x 2 v_mfma_i32_32x32x32_i8 tiles, 128
 // accumulators per lane); one workgroup per CU at M = N = 4096.  Per 128-k
-// chunk a workgroup stages 32 KB of A and 32 KB of W by global -> LDS DMA
+// chunk a workgroup stages 32 KB of A and 32 KB of W by buffer -> LDS DMA
 // (two buffers each, one array, compile-time offsets), so each operand byte
 // fetched feeds 256 output columns or rows (a 128x128 tile fetches twice as
 // much per MFMA).  A DMA instruction fills 1 KB = 8 rows of 128 bytes in lane
