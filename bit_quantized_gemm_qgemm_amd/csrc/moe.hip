@@ -30,11 +30,14 @@ struct Work {
 };
 
 // K splits of the down projection: double until the workgroups cover the
-// chip about four times, keeping whole 128-k chunks per split.
+// chip about twice (two per CU are resident), keeping whole 128-k chunks per
+// split.  At H = 4096, E = 8 that is two splits: on one box the layer took
+// 268.3 us against 273.8 with four (more partials for the combine to read),
+// on another 253.5 us against 271 with one.
 __host__ __device__ inline int down_splits(int H, int I, int E) {
     const int tiles = E * (H / 128), kc = I / 128;
     int ks = 1;
-    while (ks < 8 && tiles * ks < 1024 && kc % (2 * ks) == 0) ks *= 2;
+    while (ks < 8 && tiles * ks < 512 && kc % (2 * ks) == 0) ks *= 2;
     return ks;
 }
 

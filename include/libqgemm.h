@@ -298,7 +298,7 @@ QGEMM_API int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const fl
      fp16  h[T*topK][I]      intermediate activations, sorted order
      fp32  o[S][T*topK][H]   partial expert outputs, sorted order, one slice
                              per split of the down projection's K; S starts
-                             at 1 and doubles while S < 8, E*(H/128)*S < 1024
+                             at 1 and doubles while S < 8, E*(H/128)*S < 512
                              and (I/128) % (2*S) == 0
    The first two parts are part of the documented result (tests read them). */
 QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK);

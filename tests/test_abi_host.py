@@ -76,9 +76,9 @@ def test_size_queries(L):
     P_ = 512
     # down-projection K splits, by the rule the header states
     splits, E, H, I = 1, 8, 4096, 14336
-    while splits < 8 and E * (H // 128) * splits < 1024 and (I // 128) % (2 * splits) == 0:
+    while splits < 8 and E * (H // 128) * splits < 512 and (I // 128) % (2 * splits) == 0:
         splits *= 2
-    assert splits == 4
+    assert splits == 2
     need = 256 + 2 * 2048 + 2 * P_ * I + 4 * splits * P_ * H
     assert need <= ws <= need + 5 * 256
 
