@@ -124,6 +124,18 @@ def test_dequant_fp8_hand_and_bound():
     assert np.all(np.abs(Xh - x) <= bound + 1e-7)
 
 
+def test_dequant_fp8_rounds_in_fp32_then_fp16():
+    """Code 0x3D is 1.625 (exponent field 7, mantissa 101). With s = 5164741 * 2^-23 the exact
+    product is 67141633 * 2^-26 = 1.000488296..., 8392704.125 fp32 spacings of 2^-23: fl32 gives
+    exactly 1 + 2^-11, halfway between the fp16 values 1 and 1 + 2^-10, and the fp16 conversion
+    (ties to even) gives 1.0, where one rounding of the exact product would give 1 + 2^-10.
+    Same for the negative code 0xBD."""
+    s = np.float32(5164741 * 2.0 ** -23)
+    assert Fraction(float(s)) == Fraction(5164741, 2 ** 23)
+    X = oracle.dequant_fp8(np.array([[0x3D, 0xBD, 0x38]], np.uint8), np.array([s], np.float32))
+    assert X.astype(np.float64).tolist() == [[1.0, -1.0, float(np.float16(float(s)))]]
+
+
 def test_fp8_gemm_hand():
     enc = lambda v: oracle.f64_to_e4m3(np.array(v, np.float64))
     A = enc([[1, 2], [-0.5, 448]])

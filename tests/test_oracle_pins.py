@@ -277,14 +277,22 @@ def test_quant_hand_rows():
         x = np.array([row["x"]], np.float16)
         Q, S = oracle.quant_sym_int8(x)
         assert Q[0].tolist() == row["q"]
-        if "s" in row:
-            assert float(S[0]) == row["s"]
-    assert float(S[0]) == float(np.float32(3) / np.float32(127))
+        s_ref = Fraction(row["s_fraction"]) if "s_fraction" in row else Fraction(row["s"])
+        assert Fraction(float(S[0])) == s_ref
 
 
 def test_dequant_hand():
     g = golden("quant_hand.json")["dequant"]
     X = oracle.dequant_sym_int8(np.array([g["q"]], np.int8), np.array([g["s"]], np.float32))
+    assert X[0].astype(np.float64).tolist() == g["x"]
+
+
+def test_dequant_rounds_in_fp32_then_fp16():
+    g = golden("quant_hand.json")["dequant_two_roundings"]
+    s = Fraction(g["s_fraction"])
+    s32 = np.float32(float(s))
+    assert Fraction(float(s32)) == s
+    X = oracle.dequant_sym_int8(np.array([g["q"]], np.int8), np.array([s32], np.float32))
     assert X[0].astype(np.float64).tolist() == g["x"]
 
 
@@ -296,22 +304,78 @@ def round_half_even(fr):
     return fl
 
 
+def round_to_f32(fr):
+    """IEEE binary32 round-to-nearest-even of an exact rational (normal range only)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127
+    ulp = Fraction(2) ** (e - 23)
+    return sign * round_half_even(a / ulp) * ulp
+
+
+def quant_multiply_form(xs):
+    """Codes and scale of one row by the multiply form, in exact rationals: m = fl32(127/amax),
+    q = clamp(rne(fl32(x*m)), -127, 127), s = fl32(amax/127) (interview page, answer step 1)."""
+    xs = [Fraction(float(v)) for v in xs]
+    amax = max(abs(v) for v in xs)
+    if amax == 0:
+        return [0] * len(xs), Fraction(0)
+    m = round_to_f32(Fraction(127) / amax)
+    q = [max(-127, min(127, round_half_even(round_to_f32(v * m)))) for v in xs]
+    return q, round_to_f32(amax / 127)
+
+
+def test_round_to_f32_matches_hardware_float32():
+    r = qi.rng(89)
+    for v in np.concatenate([r.standard_normal(300), r.uniform(-1e4, 1e4, 300)]):
+        a, b = np.float32(v), np.float32(r.uniform(0.5, 2.0))
+        assert Fraction(float(a * b)) == round_to_f32(Fraction(float(a)) * Fraction(float(b)))
+        assert Fraction(float(a / b)) == round_to_f32(Fraction(float(a)) / Fraction(float(b)))
+
+
 def test_quant_against_exact_rationals():
     X = qi.kv_problem(1, 64, 128, 90).reshape(64, 128)
     X[3, 5] = np.float16(0.0)
+    X[7, :] = np.float16(0.0)
     Q, S = oracle.quant_sym_int8(X)
-    mism = 0
     for r in range(X.shape[0]):
-        amax = max(abs(Fraction(float(v))) for v in X[r])
-        for c in range(X.shape[1]):
-            t = Fraction(float(X[r, c])) * 127 / amax
-            qe = round_half_even(t)
-            if qe != Q[r, c]:
-                mism += 1
-                assert abs(qe - int(Q[r, c])) == 1
-                assert abs((t - math.floor(t)) - Fraction(1, 2)) < Fraction(1, 10 ** 4)
-        assert S[r] == np.float32(float(amax / 127))  # correctly rounded amax/127
-    assert mism <= 4
+        q, s = quant_multiply_form(X[r])
+        assert Q[r].tolist() == q
+        assert Fraction(float(S[r])) == s
+
+
+def test_quant_kv_block_multiply_form_not_division():
+    """The full [32, 2048, 128] KV block of the workload: the elements where the multiply form
+    and division by the stored scale give different codes (a few hundred of 8.4 M) carry the
+    multiply form's codes, derived exactly for each of them."""
+    X = qi.kv_problem(32, 2048, 128, 103).reshape(-1, 128)
+    Q, S = oracle.quant_sym_int8(X)
+    x32 = X.astype(np.float32)
+    amax = np.abs(x32).max(axis=1, keepdims=True)
+    m = np.float32(127.0) / amax
+    s = amax / np.float32(127.0)
+    by_mul = np.clip(np.rint(x32 * m), -127, 127)
+    by_div = np.clip(np.rint(x32 / s), -127, 127)
+    rows, cols = np.nonzero(by_mul != by_div)
+    assert len(rows) > 300
+    picks = list(zip(rows.tolist(), cols.tolist()))
+    r = qi.rng(88)
+    picks += list(zip(r.integers(0, X.shape[0], 300).tolist(), r.integers(0, 128, 300).tolist()))
+    for (i, c) in picks:
+        xs = [Fraction(float(v)) for v in X[i]]
+        a = max(abs(v) for v in xs)
+        mm = round_to_f32(Fraction(127) / a)
+        qe = max(-127, min(127, round_half_even(round_to_f32(xs[c] * mm))))
+        assert int(Q[i, c]) == qe
+    assert np.array_equal(Q[rows, cols], by_mul[rows, cols].astype(np.int8))
+    assert not np.any(Q[rows, cols] == by_div[rows, cols].astype(np.int8))
 
 
 def test_quant_error_bounds_and_statistics():
@@ -376,6 +440,19 @@ def test_w8a8_epilogue_hand():
     # without the bias flag the bias is ignored: row 3 (acc = 0) is all zero
     Yn = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 1.0, 0)
     assert Yn[3].tolist() == [0, 0, 0, 0] and Yn[0].tolist() == [10, 2, -6, 48]
+    # saturation on both sides at +-127 (never -128)
+    Y16 = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, 16.0, oracle.EPI_BIAS)
+    assert Y16[0].tolist() == g["bias_only_mult16_row0"]
+
+
+def test_w8a8_epilogue_scale_order():
+    c = golden("w8a8_hand_4x4.json")["scale_order"]
+    sw = np.float32(float(Fraction(c["sw_fraction"])))
+    assert Fraction(float(sw)) == Fraction(c["sw_fraction"])
+    Y = oracle.w8a8_epilogue(np.array(c["qa"], np.int8), np.array(c["qw"], np.int8),
+                             np.array(c["sa"], np.float32), np.array([sw], np.float32), None,
+                             c["out_mult"], c["flags"])
+    assert Y.tolist() == c["q"]
 
 
 def gelu_exact(y):
@@ -397,6 +474,36 @@ def test_gelu28_against_erf():
     big = np.float32(64.5)
     assert oracle.gelu28(big) == big
     assert oracle.gelu28(np.float32(-6.0)) == 0.0
+
+
+# Abramowitz & Stegun 7.1.28 coefficients as published (decimal) and 1/sqrt(2) to eight places
+AS_COEFFS = ["0.0705230784", "0.0422820123", "0.0092705272", "0.0001520143", "0.0002765672", "0.0000430638"]
+
+
+def gelu28_exact_steps(y):
+    """The fixed fp32 sequence of the GELU reading, evaluated step by step in exact rationals with
+    one binary32 rounding per operation (fma rounds once)."""
+    a1, a2, a3, a4, a5, a6 = (round_to_f32(Fraction(c)) for c in AS_COEFFS)
+    y = Fraction(float(y))
+    u = round_to_f32(y * round_to_f32(Fraction("0.70710678")))
+    a = abs(u)
+    p = round_to_f32(a * a6 + a5)
+    for c in (a4, a3, a2, a1, Fraction(1)):
+        p = round_to_f32(a * p + c)
+    for _ in range(4):
+        p = round_to_f32(p * p)
+    e = round_to_f32(1 - round_to_f32(1 / p))
+    if u < 0:
+        e = -e
+    return round_to_f32(round_to_f32(y / 2) * round_to_f32(1 + e))
+
+
+def test_gelu28_bits_against_exact_step_evaluation():
+    ys = np.concatenate([np.linspace(-5.5, 5.5, 301), qi.rng(85).standard_normal(300) * 2.0])
+    ys = ys.astype(np.float32)
+    g = oracle.gelu28(ys)
+    for y, v in zip(ys, g):
+        assert Fraction(float(v)) == gelu28_exact_steps(y), float(y)
 
 
 def test_w8a8_epilogue_matches_acc_path():
@@ -463,6 +570,41 @@ def test_moe_identical_experts_is_dense_swiglu():
     ref = o.astype(np.float16)
     diff = np.abs(Y.astype(np.float64) - ref.astype(np.float64))
     assert np.all(diff <= np.spacing(np.abs(ref)).astype(np.float64))
+
+
+def test_moe_distinct_experts_each_weighted_by_its_own_gate():
+    """Four tokens, four different experts, top-2 with unequal gate weights: the layer output is
+    w[t,0]*o_e0 + w[t,1]*o_e1, each o_e built from W4A16 oracle pieces (gate and up products,
+    SiLU, fp16 h, down product) and each weight from the two-logit softmax 1/(1 + e^-(l0 - l1))
+    (MoE plugin page, constructor: numExperts, topK)."""
+    T, H, I, E, topK, G = 4, 256, 256, 4, 2, 128
+    X, _, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 87)
+    logits = np.array([[2.0, 0.5, -1.0, -3.0],
+                       [-1.0, 0.25, 3.0, 1.0],
+                       [1.0, -2.0, -0.5, 2.5],
+                       [0.5, 1.75, -3.0, 0.75]], np.float16)
+    ids_hand = [[0, 1], [2, 3], [3, 0], [1, 3]]
+    w_hand = []
+    for t, (a, b) in enumerate(ids_hand):
+        w0 = 1.0 / (1.0 + math.exp(-(float(logits[t, a]) - float(logits[t, b]))))
+        w_hand.append([w0, 1.0 - w0])
+    Y, ids, w, Y64 = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, want_f64=True)
+    assert ids.tolist() == ids_hand
+    assert np.allclose(w, np.array(w_hand), rtol=1e-12, atol=0)
+    o = []
+    for e in range(E):
+        _, g = oracle.w4a16(X, Wg[e], Sg[e], G, want_f64=True)
+        _, u = oracle.w4a16(X, Wu[e], Su[e], G, want_f64=True)
+        h = (g / (1.0 + np.exp(-g)) * u).astype(np.float16)
+        o.append(oracle.w4a16(h, Wd[e], Sd[e], G, want_f64=True)[1])
+    ref = np.stack([w_hand[t][0] * o[ids_hand[t][0]][t] + w_hand[t][1] * o[ids_hand[t][1]][t]
+                    for t in range(T)])
+    swapped = np.stack([w_hand[t][1] * o[ids_hand[t][0]][t] + w_hand[t][0] * o[ids_hand[t][1]][t]
+                        for t in range(T)])
+    tol = 1e-6 * np.abs(ref).max()
+    assert np.abs(swapped - ref).max() > 1000 * tol  # the weights really are unequal
+    assert np.all(np.abs(Y64 - ref) <= tol)
+    assert np.array_equal(bits16(Y), bits16(Y64.astype(np.float16)))
 
 
 def test_moe_token_permutation_and_expert_removal():
