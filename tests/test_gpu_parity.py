@@ -224,7 +224,7 @@ def test_quant_shapes_and_edge_rows(qg, rows, cols):
 
 # ------------------------------------------------------------------ W8A8
 
-@pytest.mark.parametrize("flags", [0, 1, 3])
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (64, 256, 256), (128, 128, 384), (200, 256, 256)])
 def test_w8a8_small(qg, M, N, K, flags):
     X, Wf, bias, om = qi.w8a8_problem(M, N, K, 700 + M + N + K)
@@ -241,15 +241,17 @@ def test_w8a8_small(qg, M, N, K, flags):
 
 # M >= 256 with N % 256 == 0 takes the 256x256 DMA kernel: ragged M, one and
 # three 128-k chunks; every output compared (int32 and int8 bit-exact)
+@pytest.mark.parametrize("flags", [2, 3])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 512, 384), (517, 256, 256)])
-def test_w8a8_large(qg, M, N, K):
+def test_w8a8_large(qg, M, N, K, flags):
     X, Wf, bias, om = qi.w8a8_problem(M, N, K, 750 + M + N + K)
     qa, sa = oracle.quant_sym_int8(X)
     qw, sw = oracle.quant_sym_int8(Wf)
     om = np.float32(om * 2)
-    Yr, accr = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, om, 3, want_acc=True)
+    Yr, accr = oracle.w8a8_epilogue(qa, qw, sa, sw, bias, om, flags, want_acc=True)
     acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
-    Y = qg.qgemm_w8a8_epilogue(dev(qa), dev(qw), dev(sa), dev(sw), dev(bias), om, 3, acc_out=acc)
+    Y = qg.qgemm_w8a8_epilogue(dev(qa), dev(qw), dev(sa), dev(sw), dev(bias) if flags & 1 else None,
+                               om, flags, acc_out=acc)
     assert np.array_equal(host(acc), accr)
     assert np.array_equal(host(Y), Yr)
 
@@ -339,9 +341,32 @@ def test_moe_cfg4_sampled(qg):
     offr, pairsr = oracle.moe_permute(idr, E)
     assert np.array_equal(off, offr) and np.array_equal(pairs, pairsr)
     assert np.allclose(w, wr, rtol=1e-6, atol=0)
-    toks = [0, 1, 77, 128, 200, 255]
+    # 32 tokens (the first and last, then tokens chosen so that every expert is hit at least
+    # six times, both as first and as second choice where possible), all 4096 outputs of each
+    toks = moe_token_sample(idr, E, 32)
+    assert set(idr[toks].ravel()) == set(range(E))
     Yr, _, _ = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=toks)
     assert_fp16_close(Y[toks], Yr[toks], "moe cfg4 sampled tokens")
+
+
+def moe_token_sample(ids, E, count):
+    """Deterministic token subset: tokens 0 and T-1, then repeatedly the lowest-numbered token
+    whose least-hit expert has the fewest hits so far (ties: fewest first-choice hits of its
+    first expert), until ``count`` tokens."""
+    T = ids.shape[0]
+    picked = [0, T - 1]
+    hits = np.zeros(E, int)
+    first = np.zeros(E, int)
+    for t in picked:
+        hits[ids[t]] += 1
+        first[ids[t, 0]] += 1
+    while len(picked) < count:
+        rest = [t for t in range(T) if t not in picked]
+        best = min(rest, key=lambda t: (hits[ids[t]].min(), first[ids[t, 0]], t))
+        picked.append(best)
+        hits[ids[best]] += 1
+        first[ids[best, 0]] += 1
+    return sorted(picked)
 
 
 # ------------------------------------------------------------------ FP8 E4M3
@@ -421,6 +446,11 @@ def test_fp8_gemm_4096_sampled(qg):
     qa, sa = qg.quant_fp8_e4m3(dev(X), per_row=False)
     qw, sw = qg.quant_fp8_e4m3(dev(Wf), per_row=False)
     A, Wc = host(qa), host(qw)
+    # the per-tensor codes and scales of both 4096 x 4096 operands, bit-exact against the oracle
+    for codes, scale, src in ((A, sa, X), (Wc, sw, Wf)):
+        Qr, Sr = oracle.quant_fp8(src, per_row=False)
+        assert np.array_equal(codes, Qr)
+        assert np.array_equal(host(scale).view(np.uint32), Sr.view(np.uint32))
     Y = host(qg.qgemm_fp8(qa, qw, sa, sw))
     ms, ns = qi.sample_positions(M, N, 4000, 11)
     ref = oracle.fp8_gemm_at(A, Wc, host(sa), host(sw), ms, ns)
