@@ -94,6 +94,7 @@ def _declare(L):
                                        _I32, _I32, _I32, _P]),
         "moe_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
         "moe_w4a16": (_I32, [_P] * 11 + [_I32] * 7 + [_P, _SZ, _P]),
+        "moe_w4a16_no_alloc": (_I32, [_P] * 11 + [_I32] * 7 + [_P]),
         "quant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "dequant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "qgemm_fp8": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P]),
@@ -110,7 +111,7 @@ EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
            "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
            "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-           "qgemm_w4a16_autotune")
+           "qgemm_w4a16_autotune", "moe_w4a16_no_alloc")
 
 
 def _ptr(t):
@@ -358,6 +359,34 @@ def moe_w4a16(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_do
                            _ptr(topk_ids), _ptr(topk_w), T, H, I, E, topK, G, activation,
                            _ptr(workspace), workspace.numel(), _stream()))
     return Y, topk_ids, topk_w, workspace
+
+
+MOE_NO_ALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_w4a16_no_alloc(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down,
+                       topK, G, Y, topk_ids, topk_w, I=None, activation=0):
+    """moe_w4a16 on the library's per-GPU scratch array: every output is passed in and nothing
+    is allocated.  Returns (Y, topk_ids, topk_w)."""
+    _need(X, torch.float16, "X")
+    _need(logits, torch.float16, "logits")
+    for name, t in (("w_gate_frag", w_gate_frag), ("w_up_frag", w_up_frag),
+                    ("w_down_frag", w_down_frag)):
+        _need(t, torch.uint8, name)
+    for name, t in (("s_gate", s_gate), ("s_up", s_up), ("s_down", s_down)):
+        _need(t, torch.float16, name)
+    _need(Y, torch.float16, "Y")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    T, H = X.shape
+    E = logits.shape[1]
+    I = s_gate.shape[-1] if I is None else I
+    _check("moe_w4a16_no_alloc",
+           lib().moe_w4a16_no_alloc(_ptr(X), _ptr(logits), _ptr(w_gate_frag), _ptr(w_up_frag),
+                                    _ptr(w_down_frag), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
+                                    _ptr(Y), _ptr(topk_ids), _ptr(topk_w), T, H, I, E, topK, G,
+                                    activation, _stream()))
+    return Y, topk_ids, topk_w
 
 
 # ---------------------------------------------------------------- FP8 E4M3

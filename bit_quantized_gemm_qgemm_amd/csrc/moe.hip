@@ -14,6 +14,9 @@
 //   5. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending,
 //               o being the K-split partials added in split order.
 // Every reduction has a fixed order, so the layer is deterministic.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "wq_pass.hpp"
 
@@ -288,30 +291,20 @@ extern "C" size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int
     return off[5];
 }
 
-extern "C" int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
-                             const uint8_t* w_up_frag, const uint8_t* w_down_frag,
-                             const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
-                             uint16_t* Y, int32_t* topk_ids, float* topk_w, int32_t T, int32_t H,
-                             int32_t I, int32_t E, int32_t topK, int32_t G, int32_t activation,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-    if (T < 0 || H < 0 || I < 0 || E <= 0 || topK <= 0 || topK > E || G <= 0) return QGEMM_BAD_SHAPE;
-    if (H % G != 0 || I % G != 0) return QGEMM_BAD_SHAPE;
-    if (T == 0) return QGEMM_OK;
-    if (!X || !logits || !w_gate_frag || !w_up_frag || !w_down_frag || !s_gate || !s_up || !s_down ||
-        !Y || !topk_ids || !topk_w || !workspace)
-        return QGEMM_NULL_PTR;
-    if (activation != 0 || E > 64 || H == 0 || I == 0 || H % 128 != 0 || I % 128 != 0 ||
-        (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30 ||
-        (size_t)T * H >= (size_t)1 << 31 || (size_t)T * topK * I >= (size_t)1 << 31)
-        return QGEMM_UNSUPPORTED;
-    if (!qgh::aligned(X, 16) || !qgh::aligned(logits, 2) || !qgh::aligned(w_gate_frag, 16) ||
-        !qgh::aligned(w_up_frag, 16) || !qgh::aligned(w_down_frag, 16) || !qgh::aligned(s_gate, 4) ||
-        !qgh::aligned(s_up, 4) || !qgh::aligned(s_down, 4) || !qgh::aligned(Y, 16) ||
-        !qgh::aligned(topk_ids, 4) || !qgh::aligned(topk_w, 4) || !qgh::aligned(workspace, 256))
-        return QGEMM_MISALIGNED;
+// Validation and launch shared by both entry points (workspace given by the
+// caller, or this file's scratch array).
+static int32_t moe_run(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
+                       const uint8_t* w_up_frag, const uint8_t* w_down_frag, const uint16_t* s_gate,
+                       const uint16_t* s_up, const uint16_t* s_down, uint16_t* Y, int32_t* topk_ids,
+                       float* topk_w, int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK,
+                       int32_t G, int32_t activation, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (!workspace) return QGEMM_NULL_PTR;
+    if (!qgh::aligned(workspace, 256)) return QGEMM_MISALIGNED;
     size_t off[6];
     workspace_layout(T, H, I, E, topK, off);
     if (workspace_bytes < off[5]) return QGEMM_WORKSPACE_TOO_SMALL;
+    (void)activation;
     char* base = static_cast<char*>(workspace);
     Work wk;
     wk.offsets = reinterpret_cast<int32_t*>(base + off[0]);
@@ -331,4 +324,117 @@ extern "C" int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const ui
             return launch_moe<128>(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up,
                                    s_down, Y, topk_ids, topk_w, T, H, I, E, topK, wk, st);
     }
+}
+
+// Argument checks common to both entry points, except the workspace.
+static int32_t moe_check(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
+                         const uint8_t* w_up_frag, const uint8_t* w_down_frag,
+                         const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                         const uint16_t* Y, const int32_t* topk_ids, const float* topk_w, int32_t T,
+                         int32_t H, int32_t I, int32_t E, int32_t topK, int32_t G,
+                         int32_t activation) {
+    if (!X || !logits || !w_gate_frag || !w_up_frag || !w_down_frag || !s_gate || !s_up || !s_down ||
+        !Y || !topk_ids || !topk_w)
+        return QGEMM_NULL_PTR;
+    if (activation != 0 || E > 64 || H == 0 || I == 0 || H % 128 != 0 || I % 128 != 0 ||
+        (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30 ||
+        (size_t)T * H >= (size_t)1 << 31 || (size_t)T * topK * I >= (size_t)1 << 31)
+        return QGEMM_UNSUPPORTED;
+    if (!qgh::aligned(X, 16) || !qgh::aligned(logits, 2) || !qgh::aligned(w_gate_frag, 16) ||
+        !qgh::aligned(w_up_frag, 16) || !qgh::aligned(w_down_frag, 16) || !qgh::aligned(s_gate, 4) ||
+        !qgh::aligned(s_up, 4) || !qgh::aligned(s_down, 4) || !qgh::aligned(Y, 16) ||
+        !qgh::aligned(topk_ids, 4) || !qgh::aligned(topk_w, 4))
+        return QGEMM_MISALIGNED;
+    return QGEMM_OK;
+}
+
+extern "C" int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
+                             const uint8_t* w_up_frag, const uint8_t* w_down_frag,
+                             const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                             uint16_t* Y, int32_t* topk_ids, float* topk_w, int32_t T, int32_t H,
+                             int32_t I, int32_t E, int32_t topK, int32_t G, int32_t activation,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || H < 0 || I < 0 || E <= 0 || topK <= 0 || topK > E || G <= 0) return QGEMM_BAD_SHAPE;
+    if (H % G != 0 || I % G != 0) return QGEMM_BAD_SHAPE;
+    if (T == 0) return QGEMM_OK;
+    const int32_t c = moe_check(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down,
+                                Y, topk_ids, topk_w, T, H, I, E, topK, G, activation);
+    if (c != QGEMM_OK) return c;
+    return moe_run(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down, Y,
+                   topk_ids, topk_w, T, H, I, E, topK, G, activation, workspace, workspace_bytes,
+                   stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+
+// Workspace of moe_w4a16_no_alloc: one array per GPU, created with the code
+// object when the library is first used on that GPU and held until the
+// process ends.  Host code never passes `scratch` itself (in host code it
+// names a host-side shadow, not device memory): it looks up the device
+// address once per GPU and passes that.
+static __device__ __align__(256) unsigned char scratch[QGEMM_MOE_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current).
+int32_t scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return QGEMM_HIP_ERROR;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return QGEMM_UNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return QGEMM_HIP_ERROR;
+            }
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return QGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t moe_w4a16_no_alloc(const uint16_t* X, const uint16_t* logits,
+                                      const uint8_t* w_gate_frag, const uint8_t* w_up_frag,
+                                      const uint8_t* w_down_frag, const uint16_t* s_gate,
+                                      const uint16_t* s_up, const uint16_t* s_down, uint16_t* Y,
+                                      int32_t* topk_ids, float* topk_w, int32_t T, int32_t H,
+                                      int32_t I, int32_t E, int32_t topK, int32_t G,
+                                      int32_t activation, void* stream) {
+    if (T < 0 || H < 0 || I < 0 || E <= 0 || topK <= 0 || topK > E || G <= 0) return QGEMM_BAD_SHAPE;
+    if (H % G != 0 || I % G != 0) return QGEMM_BAD_SHAPE;
+    if (T == 0) return QGEMM_OK;
+    const int32_t c = moe_check(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down,
+                                Y, topk_ids, topk_w, T, H, I, E, topK, G, activation);
+    if (c != QGEMM_OK) return c;
+    size_t off[6];
+    workspace_layout(T, H, I, E, topK, off);
+    if (off[5] > QGEMM_MOE_NO_ALLOC_SCRATCH_BYTES) return QGEMM_WORKSPACE_TOO_SMALL;
+    if (stream) {
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return QGEMM_HIP_ERROR;
+        }
+        if (cur != sdev) return QGEMM_UNSUPPORTED;
+    }
+    void* ws = nullptr;
+    const int32_t s = scratch_address(&ws);
+    if (s != QGEMM_OK) return s;
+    return moe_run(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down, Y,
+                   topk_ids, topk_w, T, H, I, E, topK, G, activation, ws,
+                   QGEMM_MOE_NO_ALLOC_SCRATCH_BYTES, stream);
 }

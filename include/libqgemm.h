@@ -321,6 +321,29 @@ QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uin
                   int32_t G, int32_t activation, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* moe_w4a16 without a workspace argument, for callers that cannot allocate
+   device memory (code under HIP graph capture, tight serving loops, harnesses
+   that forbid hipMalloc).  Same arguments, limits, kernels and results as
+   moe_w4a16; the workspace is a library-owned array of
+   QGEMM_MOE_NO_ALLOC_SCRATCH_BYTES bytes per GPU, created with the library's
+   code object on the first use on that GPU and held until the process ends.
+   The call itself allocates nothing.
+   Returns QGEMM_WORKSPACE_TOO_SMALL when moe_w4a16_workspace_bytes(T, H, I, E,
+   topK) exceeds that size (the layer of 256 tokens, hidden 4096, intermediate
+   14336, 8 experts, top-2 needs about 31.5 MB), QGEMM_UNSUPPORTED when a
+   non-NULL stream belongs to another device than the current one.
+   Every call on one GPU shares that GPU's array and leaves its contents
+   behind (no part has to start at zero): calls that may overlap on one GPU
+   (different streams, or host threads) race and must be serialized by the
+   caller. */
+#define QGEMM_MOE_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+QGEMM_API int32_t moe_w4a16_no_alloc(const uint16_t* X, const uint16_t* logits,
+                  const uint8_t* w_gate_frag, const uint8_t* w_up_frag,
+                  const uint8_t* w_down_frag, const uint16_t* s_gate, const uint16_t* s_up,
+                  const uint16_t* s_down, uint16_t* Y, int32_t* topk_ids, float* topk_w,
+                  int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK, int32_t G,
+                  int32_t activation, void* stream);
+
 /* ------------------------------------------------------------------------
  * FP8 E4M3  (FP8-vs-INT8 article for TensorRT-LLM: the E4M3 format for the
  * GEMMs and the KV cache, scaling factors from the activation A-max,

@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
         "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
         "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
         "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-        "qgemm_w4a16_autotune"])
+        "qgemm_w4a16_autotune", "moe_w4a16_no_alloc"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -237,6 +237,23 @@ def test_w8a8_validation(L):
     assert f(*args(4, 128, 133248)) == 5              # accumulator could overflow
     assert f(*args(4, 128, 128, a=FAKE + 1)) == 3
     assert f(*args(-4, 128, 128)) == 2
+
+
+def test_moe_no_alloc_validation(L):
+    # every rejection here happens before the library touches HIP
+    f = L.moe_w4a16_no_alloc
+    def call(T=4, H=128, I=128, E=4, topK=2, G=128, act=0, ptr=FAKE):
+        return f(*([ptr] * 11), T, H, I, E, topK, G, act, None)
+    assert call(T=0) == 0
+    assert call(topK=5) == 2
+    assert call(act=1) == 5
+    assert call(ptr=None) == 1
+    assert call(ptr=FAKE + 2) == 3
+    limit = 64 << 20
+    # the 256-token layer fits the scratch array; 4096 tokens do not
+    assert L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2) <= limit
+    assert L.moe_w4a16_workspace_bytes(4096, 4096, 14336, 8, 2) > limit
+    assert call(T=4096, H=4096, I=14336, E=8) == 4
 
 
 def test_moe_validation(L):
