@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile", default=None,
                     choices=["decode1", "decode4", "decode8", "prefill", "w8a8", "quant_act",
-                             "kvquant", "kvdequant", "moe", "mha", "copy"],
+                             "kvquant", "kvdequant", "moe", "mha", "copy", "stream"],
                     help="launch one workload's kernels --launches times (eagerly) and exit; "
                          "for rocprofv3 runs")
     ap.add_argument("--launches", type=int, default=20)
@@ -104,10 +104,10 @@ def main():
                 f()
         return g
 
-    def time_graph(g, launches, reps, warm_s=0.05):
-        # untimed replays for at least warm_s seconds first: the shader clock
-        # takes tens of milliseconds of load to settle (an MFMA-bound GEMM ran
-        # 15 % slower in its first 50 ms than afterwards)
+    def settle(g, warm_s=0.05):
+        # untimed replays for at least warm_s seconds: the shader clock takes
+        # tens of milliseconds of load to settle (an MFMA-bound GEMM ran 15 %
+        # slower in its first 50 ms than afterwards)
         t0, n = time.perf_counter(), 0
         while n < 3 or time.perf_counter() - t0 < warm_s:
             g.replay()
@@ -115,6 +115,9 @@ def main():
             if n % 8 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
+
+    def time_graph(g, launches, reps, warm_s=0.05):
+        settle(g, warm_s)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -160,7 +163,7 @@ def main():
             step_graphs[k].replay()
 
     run_steps(args.warmup)
-    torch.cuda.synchronize()
+    settle(block_graph)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -183,11 +186,34 @@ def main():
         log(f"[bench] decode M={M}: {per_m[M]}")
 
     b1 = w4a16_bytes(1, DEC_N, DEC_K, DEC_G)
+    # achievable read bandwidth at the decode working set: the library's plain
+    # streaming-read kernel over 16 rotated buffers of one M=1 launch's bytes,
+    # timed like the decode kernel (graph of 48 launches)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    bufs = [torch.empty(b1, dtype=torch.uint8, device=dev).fill_(r) for r in range(ROT)]
+    g = graph_of([(lambda r=r: qg.qgemm_stream_read(bufs[r % ROT], sink)) for r in range(3 * ROT)])
+    t_s = time_graph(g, 3 * ROT, reps=max(4, args.steps // 16))
+    stream_23 = b1 / t_s / 1e9
+    del bufs
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    g = graph_of([lambda: qg.qgemm_stream_read(big, sink)] * 8)
+    t_b = time_graph(g, 8, reps=4)
+    stream_1g = (1 << 30) / t_b / 1e9
+    del big
+    log(f"[bench] stream read: {b1} B x16 rotated {t_s * 1e6:.2f} us {stream_23:.1f} GB/s; "
+        f"1 GiB {stream_1g:.1f} GB/s")
     achieved = b1 / (per_m[1]["us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic(), "kernel": "wq_decode_kernel<WB=4,MT=1,NSW=1,KCW=4,G=128,BAL=false> (M=1)",
-                "bytes_per_launch": b1}
+                "bytes_per_launch": b1, "us_per_launch": per_m[1]["us"],
+                "measured_read_ceiling": {"GB/s": round(stream_23, 1), "us": round(t_s * 1e6, 3),
+                                          "kernel": "stream_read_kernel, 16-B non-temporal loads",
+                                          "working_set": f"{b1} B per launch, 16 rotated buffers"},
+                "frac_of_measured_ceiling": round(achieved / stream_23, 4),
+                "read_1GiB_GB/s": round(stream_1g, 1)}
+    for M in DEC_MS:
+        per_m[M]["frac_of_measured_ceiling"] = round(per_m[M]["GB/s"] / stream_23, 4)
 
     rows = {}
     if not args.no_rows:
@@ -253,18 +279,30 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
             qg.qgemm_w4a16(p[0], p[1], p[2], G, Y=Y)
     elif name in ("w8a8", "quant_act"):
         M = N = K = 4096
+        RQ = 8
         X, Wf16, bias, om = qi.w8a8_problem(M, N, K, 103)
-        Xd = to_dev(X)
-        qw, sw = qg.quant_sym_int8(to_dev(Wf16))
-        qa, sa = qg.quant_sym_int8(Xd)
+        Xs = [to_dev(X)] + [to_dev(qi.activations(M, K, 1103 + r)) for r in range(1, RQ)]
+        qws = [qg.quant_sym_int8(to_dev(Wf16))]
+        qws += [qg.quant_sym_int8(to_dev(qi.activations(N, K, 1203 + r))) for r in range(1, RQ)]
+        qas = [qg.quant_sym_int8(x) for x in Xs]
         biasd = to_dev(bias)
-        Yq = torch.empty((M, N), dtype=torch.int8, device=dev)
+        Yqs = [torch.empty((M, N), dtype=torch.int8, device=dev) for _ in range(RQ)]
         torch.cuda.synchronize()
-        for _ in range(launches):
+        for i in range(launches):
+            r = i % RQ
             if name == "w8a8":
-                qg.qgemm_w8a8_epilogue(qa, qw, sa, sw, biasd, float(om), 3, Y=Yq)
+                qg.qgemm_w8a8_epilogue(qas[r][0], qws[r][0], qas[r][1], qws[r][1], biasd, float(om), 3,
+                                       Y=Yqs[r])
             else:
-                qg.quant_sym_int8(Xd, Q=qa, scales=sa)
+                qg.quant_sym_int8(Xs[r], Q=qas[r][0], scales=qas[r][1])
+    elif name == "stream":
+        # the streaming-read reference over 16 rotated buffers of one M=1 decode launch's bytes
+        b1 = w4a16_bytes(1, DEC_N, DEC_K, DEC_G)
+        bufs = [torch.empty(b1, dtype=torch.uint8, device=dev).fill_(r) for r in range(ROT)]
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            qg.qgemm_stream_read(bufs[i % ROT], sink)
     elif name in ("kvquant", "kvdequant"):
         kvs = [to_dev(qi.kv_problem(32, 2048, 128, 103 + 1000 * r)) for r in range(16)]
         Q = torch.empty((32, 2048, 128), dtype=torch.int8, device=dev)
@@ -367,28 +405,36 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
     log(f"[bench] prefill {rows['w4a16_prefill_M2048_K4096_N4096']}")
     del probs
 
-    # cfg3a: W8A8 M=N=K=4096: per-token activation quant + GEMM with epilogue
+    # cfg3a: W8A8 M=N=K=4096: per-token activation quant + GEMM with epilogue.
+    # RQ = 8 rotated sets (activation quant: 8 x 50 MB in + out; GEMM: 8 x (A, W,
+    # Y) = 8 x 50 MB), past the 256 MB Infinity Cache
     M = N = K = 4096
+    RQ = 8
     X, Wf16, bias, om = qi.w8a8_problem(M, N, K, 103)
-    Xd = to_dev(X)
-    qw, sw = qg.quant_sym_int8(to_dev(Wf16))
-    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
-    sa = torch.empty(M, dtype=torch.float32, device=dev)
+    Xs = [to_dev(X)] + [to_dev(qi.activations(M, K, 1103 + r)) for r in range(1, RQ)]
+    qws = [qg.quant_sym_int8(to_dev(Wf16))]
+    qws += [qg.quant_sym_int8(to_dev(qi.activations(N, K, 1203 + r))) for r in range(1, RQ)]
+    qas = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(RQ)]
+    sas = [torch.empty(M, dtype=torch.float32, device=dev) for _ in range(RQ)]
     biasd = to_dev(bias)
-    Yq = torch.empty((M, N), dtype=torch.int8, device=dev)
-    gq = graph_of([lambda: qg.quant_sym_int8(Xd, Q=qa, scales=sa)] * 8)
-    tq = time_graph(gq, 8, reps=10)
+    Yqs = [torch.empty((M, N), dtype=torch.int8, device=dev) for _ in range(RQ)]
+    gq = graph_of([(lambda r=r: qg.quant_sym_int8(Xs[r], Q=qas[r], scales=sas[r])) for r in range(RQ)])
+    tq = time_graph(gq, RQ, reps=10)
     qb = 3 * M * K + 4 * M
     rows["quant_sym_int8_act_4096x4096"] = {"us": round(tq * 1e6, 2), "GB/s": round(qb / tq / 1e9, 1),
-                                            "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4)}
-    qg.quant_sym_int8(Xd, Q=qa, scales=sa)
-    gg = graph_of([lambda: qg.qgemm_w8a8_epilogue(qa, qw, sa, sw, biasd, float(om), 3, Y=Yq)] * 8)
-    tg = time_graph(gg, 8, reps=10)
+                                            "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
+                                            "rotation_sets": RQ}
+    for r in range(RQ):
+        qg.quant_sym_int8(Xs[r], Q=qas[r], scales=sas[r])
+    gg = graph_of([(lambda r=r: qg.qgemm_w8a8_epilogue(qas[r], qws[r][0], sas[r], qws[r][1], biasd,
+                                                       float(om), 3, Y=Yqs[r])) for r in range(RQ)])
+    tg = time_graph(gg, RQ, reps=10)
     ops = 2 * M * N * K
     rows["w8a8_gemm_gelu_4096"] = {"us": round(tg * 1e6, 2), "TOPS": round(ops / tg / 1e12, 1),
-                                   "mfma_frac": round(ops / tg / 1e12 / I8_MFMA_PEAK_TOPS, 4)}
+                                   "mfma_frac": round(ops / tg / 1e12 / I8_MFMA_PEAK_TOPS, 4),
+                                   "rotation_sets": RQ}
     log(f"[bench] w8a8 {rows['w8a8_gemm_gelu_4096']} quant {rows['quant_sym_int8_act_4096x4096']}")
-    del Xd, qw, qa, Yq
+    del Xs, qws, qas, sas, Yqs
 
     # cfg3b: KV cache [32, 2048, 128] quant + dequant, 16 rotated sets
     R = 16
@@ -445,26 +491,34 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
 
     # FP8 E4M3: per-tensor activation quant 4096 x 4096, FP8 GEMM M=N=K=4096
     # (fp16 out), per-row KV cache [32, 2048, 128] quant + dequant (16 rotated sets)
+    # (8 rotated sets each, as for W8A8: 8 x 50 MB)
     M = N = K = 4096
     X, Wf16, _, _ = qi.w8a8_problem(M, N, K, 106)
-    Xd = to_dev(X)
-    qw8, sw8 = qg.quant_fp8_e4m3(to_dev(Wf16), per_row=False)
-    qa8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa8 = torch.empty(1, dtype=torch.float32, device=dev)
-    Y8 = torch.empty((M, N), dtype=torch.float16, device=dev)
-    gq = graph_of([lambda: qg.quant_fp8_e4m3(Xd, per_row=False, Q=qa8, scales=sa8)] * 8)
-    tq = time_graph(gq, 8, reps=10)
+    Xs = [to_dev(X)] + [to_dev(qi.activations(M, K, 1106 + r)) for r in range(1, RQ)]
+    qw8s = [qg.quant_fp8_e4m3(to_dev(Wf16), per_row=False)]
+    qw8s += [qg.quant_fp8_e4m3(to_dev(qi.activations(N, K, 1206 + r)), per_row=False)
+             for r in range(1, RQ)]
+    qa8s = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(RQ)]
+    sa8s = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(RQ)]
+    Y8s = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(RQ)]
+    gq = graph_of([(lambda r=r: qg.quant_fp8_e4m3(Xs[r], per_row=False, Q=qa8s[r], scales=sa8s[r]))
+                   for r in range(RQ)])
+    tq = time_graph(gq, RQ, reps=10)
     qb = 3 * M * K + 4
     rows["fp8_quant_per_tensor_4096x4096"] = {"us": round(tq * 1e6, 2), "GB/s": round(qb / tq / 1e9, 1),
-                                              "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4)}
-    qg.quant_fp8_e4m3(Xd, per_row=False, Q=qa8, scales=sa8)
-    gg = graph_of([lambda: qg.qgemm_fp8(qa8, qw8, sa8, sw8, Y=Y8)] * 8)
-    tg = time_graph(gg, 8, reps=10)
+                                              "hbm_frac": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
+                                              "rotation_sets": RQ}
+    for r in range(RQ):
+        qg.quant_fp8_e4m3(Xs[r], per_row=False, Q=qa8s[r], scales=sa8s[r])
+    gg = graph_of([(lambda r=r: qg.qgemm_fp8(qa8s[r], qw8s[r][0], sa8s[r], qw8s[r][1], Y=Y8s[r]))
+                   for r in range(RQ)])
+    tg = time_graph(gg, RQ, reps=10)
     fl = 2 * M * N * K
     rows["fp8_gemm_4096"] = {"us": round(tg * 1e6, 2), "TFLOP/s": round(fl / tg / 1e12, 1),
-                             "mfma_frac": round(fl / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)}
+                             "mfma_frac": round(fl / tg / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                             "rotation_sets": RQ}
     log(f"[bench] fp8 gemm {rows['fp8_gemm_4096']} quant {rows['fp8_quant_per_tensor_4096x4096']}")
-    del Xd, qw8, qa8, Y8
+    del Xs, qw8s, qa8s, sa8s, Y8s
     R = 16
     kvs = [to_dev(qi.kv_problem(32, 2048, 128, 105 + 1000 * r)) for r in range(R)]
     Q8 = torch.empty((32, 2048, 128), dtype=torch.uint8, device=dev)
@@ -552,8 +606,16 @@ def cpu_baseline(np, qi, step_bytes, seconds, log):
             break
     per_step = el / reps
     log(f"[bench] cpu oracle: {reps} steps in {el:.1f} s")
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(step_bytes / per_step / 1e9, 3), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
+            "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model, "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"{reps} decode steps (M=1,4,8 full outputs, K=4096 N=11008 G=128), "
                       f"{el:.1f} s, fp64 sums, OpenMP over output columns",
             "s_per_step": round(per_step, 4)}

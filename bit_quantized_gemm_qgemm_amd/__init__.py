@@ -95,6 +95,7 @@ def _declare(L):
         "moe_w4a16_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
         "moe_w4a16": (_I32, [_P] * 11 + [_I32] * 7 + [_P, _SZ, _P]),
         "moe_w4a16_no_alloc": (_I32, [_P] * 11 + [_I32] * 7 + [_P]),
+        "qgemm_stream_read": (_I32, [_P, _SZ, _P, _P]),
         "quant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "dequant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "qgemm_fp8": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P]),
@@ -111,7 +112,7 @@ EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
            "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
            "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-           "qgemm_w4a16_autotune", "moe_w4a16_no_alloc")
+           "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read")
 
 
 def _ptr(t):
@@ -471,3 +472,15 @@ def mha_int8(Q, K, V, alpha, pv_scale, out_mult, bias=None, O=None, s_out=None, 
                                       B, H, Lq, Lk, D, float(alpha), float(pv_scale), float(out_mult), flags,
                                       _stream()))
     return O
+
+
+# ---------------------------------------------------------------- measurement aid
+
+def qgemm_stream_read(buf, sink):
+    """Read every byte of the CUDA tensor ``buf`` (a multiple of 16 bytes) with 16-byte loads;
+    ``sink`` is a 1-element int32 tensor the kernel may write.  For bandwidth reference runs."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf: expected a contiguous CUDA tensor")
+    _need(sink, torch.int32, "sink")
+    _check("qgemm_stream_read", lib().qgemm_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                                         _ptr(sink), _stream()))

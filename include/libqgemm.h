@@ -428,6 +428,17 @@ QGEMM_API int32_t mha_int8(const int8_t* Q, const int8_t* K, const int8_t* V, co
                            int32_t D, float alpha, float pv_scale, float out_mult, uint32_t flags,
                            void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid (not a step of the method): reads `bytes` bytes of device
+ * memory at `buf` with one 16-byte non-temporal load per lane and address,
+ * eight per lane in flight, and discards them (a store to sink[0] that depends
+ * on the data keeps the loads; it happens only if the data XOR to one fixed
+ * value).  Its rate over a working set is the achievable read bandwidth that
+ * the memory-bound kernels are compared with.  bytes must be a multiple of 16,
+ * buf 16-byte and sink 4-byte aligned; bytes == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+QGEMM_API int32_t qgemm_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

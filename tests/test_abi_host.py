@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
         "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
         "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
         "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-        "qgemm_w4a16_autotune", "moe_w4a16_no_alloc"])
+        "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -254,6 +254,14 @@ def test_moe_no_alloc_validation(L):
     assert L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2) <= limit
     assert L.moe_w4a16_workspace_bytes(4096, 4096, 14336, 8, 2) > limit
     assert call(T=4096, H=4096, I=14336, E=8) == 4
+
+
+def test_stream_read_validation(L):
+    f = L.qgemm_stream_read
+    assert f(None, 0, None, None) == 0
+    assert f(None, 16, FAKE, None) == 1
+    assert f(FAKE, 24, FAKE, None) == 2
+    assert f(FAKE + 8, 32, FAKE, None) == 3
 
 
 def test_moe_validation(L):
