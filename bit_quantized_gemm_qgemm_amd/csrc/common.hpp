@@ -76,6 +76,21 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n) {
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
+// Output tile (row tr, column tc) of workgroup b in a grid of mt x nt tiles.
+// Each XCD takes a contiguous run of the tile order (xcd_contiguous), and the
+// order walks bands of GM tile rows column by column, so the tiles of one XCD
+// form a block of about GM rows by (its share / GM) columns: its workgroups
+// share A row tiles and weight column tiles in that XCD's L2, and no XCD
+// streams the whole weight matrix (at 16 x 16 tiles and GM = 4: a 4 x 8 block
+// per XCD instead of 2 rows x all 16 columns).
+__device__ __forceinline__ void xcd_tile(int b, int mt, int nt, int GM, int& tr, int& tc) {
+    const int o = xcd_contiguous(b, mt * nt);
+    const int g = o / (GM * nt), w = o - g * GM * nt;
+    const int gs = mt - g * GM < GM ? mt - g * GM : GM;  // rows of this band (the last may be short)
+    tr = g * GM + w % gs;
+    tc = w / gs;
+}
+
 // ---------------------------------------------------------------- loads
 
 // Wait until at most N vector-memory operations of this wave are outstanding

@@ -185,11 +185,12 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
     // tell the copies' LDS targets from the buffer being read)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    // tile (x, y) of workgroup L: y = L % (row tiles), so the workgroups on
-    // one XCD (dealt round-robin by id) share their A row tiles in its L2
+    // tile of workgroup L: each XCD (workgroups are dealt round-robin by id)
+    // owns a block of tiles sharing A rows and W columns in its L2
     const int mtiles = (M + FB - 1) / FB;
-    const int L = blockIdx.x;
-    const int m0 = (L % mtiles) * FB, n0 = (L / mtiles) * FB;
+    int tr, tc;
+    xcd_tile(blockIdx.x, mtiles, (N + FB - 1) / FB, 4, tr, tc);
+    const int m0 = tr * FB, n0 = tc * FB;
     const int kchunks = K / 128, last = kchunks - 1;
     const int h = lane >> 5, c32 = lane & 31;
 

@@ -437,7 +437,9 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups are dealt to the 8 XCDs round-robin by id.  Tile (x, y) of
     // id L has y = L % (row tiles), so the workgroups on one XCD share their
-    // A row tiles in that XCD's L2 and stream distinct B tiles.
+    // A row tiles in that XCD's L2 and stream distinct B tiles.  (Grouping
+    // each XCD's tiles into a 4 x 8 block, xcd_tile, cuts the L2 misses but
+    // measured 0.3 us slower at M = 2048, N = K = 4096.)
     const int mtiles = (M + PL_BM - 1) / PL_BM;
     const int L = blockIdx.x;
     const int m0 = (L % mtiles) * PL_BM, n0 = (L / mtiles) * PL_BN;
