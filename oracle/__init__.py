@@ -55,10 +55,12 @@ def _declare(lib):
         "qo_w4a16_at": (None, [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32, _I32]),
         "qo_frag_nibble_index": (_I64, [_I32, _I32, _I32]),
         "qo_w4a16_prepack": (None, [_P, _P, _I32, _I32]),
+        "qo_w4a16_packed_bytes": (_I64, [_I32, _I32]),
         "qo_w8a16": (None, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32]),
         "qo_w8a16_at": (None, [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I32]),
         "qo_frag8_byte_index": (_I64, [_I32, _I32, _I32]),
         "qo_w8a16_prepack": (None, [_P, _P, _I32, _I32]),
+        "qo_w8a16_packed_bytes": (_I64, [_I32, _I32]),
         "qo_quant_sym_int8": (None, [_P, _P, _P, _I64, _I32]),
         "qo_dequant_sym_int8": (None, [_P, _P, _P, _I64, _I32]),
         "qo_w8a8_acc": (None, [_P, _P, _P, _I32, _I32, _I32]),
@@ -132,13 +134,14 @@ def int4_unpack(w, K, N):
 # ---------------------------------------------------------------- W4A16
 
 def w4a16(A, W, S, G, want_f64=False):
-    """Y = fp16(A @ dequant(W, S)) with fp64 sums; A fp16 [M,K], W uint8 [K,N/2], S fp16 [K/G,N]."""
+    """Y = fp16(A @ dequant(W, S)) with fp64 sums; A fp16 [M,K], W uint8 [K,N/2],
+    S fp16 [ceil(K/G),N]."""
     A = _c(A, np.float16)
     W = _c(W, np.uint8)
     S = _c(S, np.float16)
     M, K = A.shape
     N = S.shape[1]
-    assert W.shape == (K, N // 2) and S.shape == (K // G, N)
+    assert W.shape == (K, N // 2) and S.shape == (-(-K // G), N)
     Y = np.empty((M, N), np.float16)
     Y64 = np.empty((M, N), np.float64) if want_f64 else None
     _load().qo_w4a16(_ptr(A), _ptr(W), _ptr(S), _ptr(Y), _ptr(Y64), M, N, K, G)
@@ -167,9 +170,10 @@ def frag_nibble_index(K, k, n):
 
 
 def w4a16_prepack(W, K, N):
+    """Fragment-layout bytes (padded to whole 128 x 128 tiles) of natural int4 W [K][N/2]."""
     W = _c(W, np.uint8)
-    assert W.size == K * N // 2 and K % 128 == 0 and N % 128 == 0
-    F = np.empty(K * N // 2, np.uint8)
+    assert W.size == K * N // 2 and N % 2 == 0
+    F = np.empty(_load().qo_w4a16_packed_bytes(K, N), np.uint8)
     _load().qo_w4a16_prepack(_ptr(W), _ptr(F), K, N)
     return F
 
@@ -177,14 +181,14 @@ def w4a16_prepack(W, K, N):
 # ---------------------------------------------------------------- W8A16
 
 def w8a16(A, W, S, G, want_f64=False):
-    """Y = fp16(A @ (W * S)) with fp64 sums; A fp16 [M,K], W int8 [K,N], S fp16 [K/G,N]
+    """Y = fp16(A @ (W * S)) with fp64 sums; A fp16 [M,K], W int8 [K,N], S fp16 [ceil(K/G),N]
     (G == K: one scale per column)."""
     A = _c(A, np.float16)
     W = _c(W, np.int8)
     S = _c(S, np.float16)
     M, K = A.shape
     N = W.shape[1]
-    assert W.shape == (K, N) and K % G == 0 and S.shape == (K // G, N)
+    assert W.shape == (K, N) and S.shape == (-(-K // G), N)
     Y = np.empty((M, N), np.float16)
     Y64 = np.empty((M, N), np.float64) if want_f64 else None
     _load().qo_w8a16(_ptr(A), _ptr(W), _ptr(S), _ptr(Y), _ptr(Y64), M, N, K, G)
@@ -197,7 +201,7 @@ def w8a16_at(A, W, S, G, ms, ns, want_f64=False):
     S = _c(S, np.float16)
     M, K = A.shape
     N = W.shape[1]
-    assert W.shape == (K, N) and K % G == 0 and S.shape == (K // G, N)
+    assert W.shape == (K, N) and S.shape == (-(-K // G), N)
     ms = _c(np.asarray(ms, np.int32), np.int32)
     ns = _c(np.asarray(ns, np.int32), np.int32)
     assert ms.shape == ns.shape
@@ -214,9 +218,10 @@ def frag8_byte_index(K, k, n):
 
 
 def w8a16_prepack(W, K, N):
+    """Fragment-layout bytes (padded to whole 128 x 128 tiles) of int8 W [K][N]."""
     W = _c(W, np.int8)
-    assert W.shape == (K, N) and K % 128 == 0 and N % 128 == 0
-    F = np.empty(K * N, np.uint8)
+    assert W.shape == (K, N)
+    F = np.empty(_load().qo_w8a16_packed_bytes(K, N), np.uint8)
     _load().qo_w8a16_prepack(_ptr(W), _ptr(F), K, N)
     return F
 

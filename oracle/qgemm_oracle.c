@@ -131,7 +131,8 @@ QO_API void qo_int4_unpack(const uint8_t* w, int8_t* q, int32_t K, int32_t N) {
 /* ------------------------------------------------------------------------ */
 /* W4A16 group-wise GEMM  [P3 class summary]                                */
 /*   Y[m][n] = fp16( sum_k A[m][k] * q(k,n) * S[k/G][n] ),  k ascending      */
-/* A fp16 [M][K] row-major; W natural int4 [K][N/2]; S fp16 [K/G][N];        */
+/* A fp16 [M][K] row-major; W natural int4 [K][N/2]; S fp16 [ceil(K/G)][N]   */
+/* (the last group may be shorter than G);                                  */
 /* Y fp16 [M][N].  Y64 (optional) receives the unrounded fp64 sums.          */
 /* ------------------------------------------------------------------------ */
 
@@ -192,26 +193,36 @@ QO_API void qo_w4a16_at(const uint16_t* A, const uint8_t* W, const uint16_t* S,
 /*     32-bit word at byte (cl + 16*q)*16 + 4*kk;                            */
 /*     nibble position pos = j/2 + 4*(j%2) (bits 4*pos .. 4*pos+3);          */
 /*     stored value (v + 8) & 15 (offset binary).                            */
-/* Requires K % 128 == 0 and N % 128 == 0.                                   */
+/* K and N that are not multiples of 128 are padded to whole tiles (the      */
+/* page's fragment rows = ceil(N/128) * ceil(K/64) * 8): the layout has      */
+/* ceil(K/128) chunks per strip and ceil(N/128) tiles, and every padding     */
+/* position holds the offset-binary code of weight 0 (nibble 8).             */
 /* ------------------------------------------------------------------------ */
 
 QO_API int64_t qo_frag_nibble_index(int32_t K, int32_t k, int32_t n) {
     const int32_t s = n / 16, cl = n % 16, c = k / 128, r = k % 128;
     const int32_t kk = r / 32, q = (r % 32) / 8, j = r % 8;
-    const int64_t block = ((int64_t)(s / 8) * (K / 128) + c) * 8192 + (int64_t)(s % 8) * 1024;
+    const int64_t kchunks = (K + 127) / 128;
+    const int64_t block = ((int64_t)(s / 8) * kchunks + c) * 8192 + (int64_t)(s % 8) * 1024;
     const int64_t word = block + (int64_t)(cl + 16 * q) * 16 + 4 * kk;
     const int32_t pos = j / 2 + 4 * (j % 2);
     return word * 2 + pos; /* nibble index: byte = idx/2, high nibble if idx odd */
 }
 
+/* Bytes of the padded layout: ceil(K/128)*128 x ceil(N/128)*128 nibbles. */
+QO_API int64_t qo_w4a16_packed_bytes(int32_t K, int32_t N) {
+    return ((int64_t)(K + 127) / 128) * 128 * (((int64_t)N + 127) / 128) * 128 / 2;
+}
+
 QO_API void qo_w4a16_prepack(const uint8_t* W, uint8_t* F, int32_t K, int32_t N) {
-    memset(F, 0, (size_t)K * N / 2);
+    memset(F, 0x88, (size_t)qo_w4a16_packed_bytes(K, N));
     for (int32_t k = 0; k < K; ++k)
         for (int32_t n = 0; n < N; ++n) {
             const int v = qo_int4_at(W, N, k, n);
             const uint8_t u = (uint8_t)((v + 8) & 15);
             const int64_t idx = qo_frag_nibble_index(K, k, n);
-            F[idx / 2] |= (idx & 1) ? (uint8_t)(u << 4) : u;
+            F[idx / 2] = (idx & 1) ? (uint8_t)((F[idx / 2] & 0x0f) | (u << 4))
+                                   : (uint8_t)((F[idx / 2] & 0xf0) | u);
         }
 }
 
@@ -269,17 +280,24 @@ QO_API void qo_w8a16_at(const uint16_t* A, const int8_t* W, const uint16_t* S,
 /*     byte (kk/2)*1024 + (cl + 16*q)*16 + (kk%2)*8 + j;                     */
 /*     stored value v + 128 (offset binary).                                 */
 /* The k of each byte is that of the int4 layout's nibble with the same      */
-/* (block, cl, q, kk, j).  Requires K % 128 == 0 and N % 128 == 0.           */
+/* (block, cl, q, kk, j).  K and N are padded to whole 128 x 128 tiles as    */
+/* for int4; padding bytes hold the offset-binary code of 0 (128).           */
 /* ------------------------------------------------------------------------ */
 
 QO_API int64_t qo_frag8_byte_index(int32_t K, int32_t k, int32_t n) {
     const int32_t s = n / 16, cl = n % 16, c = k / 128, r = k % 128;
     const int32_t kk = r / 32, q = (r % 32) / 8, j = r % 8;
-    const int64_t block = ((int64_t)(s / 8) * (K / 128) + c) * 16384 + (int64_t)(s % 8) * 2048;
+    const int64_t kchunks = (K + 127) / 128;
+    const int64_t block = ((int64_t)(s / 8) * kchunks + c) * 16384 + (int64_t)(s % 8) * 2048;
     return block + (int64_t)(kk / 2) * 1024 + (int64_t)(cl + 16 * q) * 16 + (kk % 2) * 8 + j;
 }
 
+QO_API int64_t qo_w8a16_packed_bytes(int32_t K, int32_t N) {
+    return ((int64_t)(K + 127) / 128) * 128 * (((int64_t)N + 127) / 128) * 128;
+}
+
 QO_API void qo_w8a16_prepack(const int8_t* W, uint8_t* F, int32_t K, int32_t N) {
+    memset(F, 128, (size_t)qo_w8a16_packed_bytes(K, N));
     for (int32_t k = 0; k < K; ++k)
         for (int32_t n = 0; n < N; ++n)
             F[qo_frag8_byte_index(K, k, n)] = (uint8_t)((int)W[(int64_t)k * N + n] + 128);

@@ -18,11 +18,16 @@ def rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 
 
+def groups(K, G):
+    """Scale rows of a K-deep weight matrix with group size G: ceil(K / G)."""
+    return -(-K // G)
+
+
 def w4a16_weights(K, N, G, seed):
     """int4 weights (natural packed bytes) and fp16 group scales U[0.005, 0.02]."""
     r = rng(seed)
     W = r.integers(0, 256, size=(K, N // 2), dtype=np.uint8)
-    S = r.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    S = r.uniform(0.005, 0.02, size=(groups(K, G), N)).astype(np.float16)
     return W, S
 
 
@@ -35,17 +40,17 @@ def w4a16_problem(M, K, N, G, seed):
     r = rng(seed)
     A = r.standard_normal((M, K)).astype(np.float16)
     W = r.integers(0, 256, size=(K, N // 2), dtype=np.uint8)
-    S = r.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    S = r.uniform(0.005, 0.02, size=(groups(K, G), N)).astype(np.float16)
     return A, W, S
 
 
 def w8a16_problem(M, K, N, G, seed):
     """fp16 activations ~ N(0, 1); int8 weights [K][N] uniform over [-128, 127]
-    (random bytes); fp16 scales [K/G][N] U[0.0005, 0.002] (G == K: per column)."""
+    (random bytes); fp16 scales [ceil(K/G)][N] U[0.0005, 0.002] (G == K: per column)."""
     r = rng(seed)
     A = r.standard_normal((M, K)).astype(np.float16)
     W = r.integers(0, 256, size=(K, N), dtype=np.uint8).view(np.int8)
-    S = r.uniform(0.0005, 0.002, size=(K // G, N)).astype(np.float16)
+    S = r.uniform(0.0005, 0.002, size=(groups(K, G), N)).astype(np.float16)
     return A, W, S
 
 

@@ -269,6 +269,55 @@ def test_prepack_moves_every_nibble():
             assert nib[oracle.frag_nibble_index(K, k, n)] == q[k, n] + 8
 
 
+@pytest.mark.parametrize("K,N", [(200, 136), (8, 8), (136, 264), (1000, 24)])
+def test_prepack_ragged_is_the_zero_padded_layout(K, N):
+    """K and N that are not multiples of 128 (GEMM plugin page, class summary: scales
+    [ceil(K/G), N], fragment rows ceil(N/128) * ceil(K/64) * 8) pad to whole tiles: the
+    bytes equal those of the matrix extended with weight-0 rows and columns to the next
+    multiples of 128, and the padding holds weight 0."""
+    Wb = qi.w4a16_weights(K, N, 32, 87 + K + N)[0]
+    Kp, Np = -(-K // 128) * 128, -(-N // 128) * 128
+    Wp = np.zeros((Kp, Np // 2), np.uint8)  # nibble 0 = weight 0 (two's complement)
+    Wp[:K, :N // 2] = Wb
+    F = oracle.w4a16_prepack(Wb, K, N)
+    assert F.size == Kp * Np // 2
+    assert np.array_equal(F, oracle.w4a16_prepack(Wp, Kp, Np))
+    idx = np.array([[oracle.frag_nibble_index(K, k, n) for n in range(N)] for k in range(K)]).ravel()
+    assert np.unique(idx).size == K * N and idx.max() < Kp * Np
+    nib = np.empty(Kp * Np, np.int64)
+    nib[0::2] = F & 15
+    nib[1::2] = F >> 4
+    pad = np.ones(Kp * Np, bool)
+    pad[idx] = False
+    assert np.all(nib[pad] == 8)
+    q = unpack_numpy(Wb, K, N)
+    assert np.array_equal(nib[idx], (q.ravel() + 8))
+
+
+@pytest.mark.parametrize("K,G", [(40, 32), (72, 64), (136, 128), (24, 32)])
+def test_w4a16_partial_last_group_exact(K, G):
+    """K not a multiple of G: scales have ceil(K/G) rows and the last group covers the
+    remaining K % G rows (exact rationals, one fp16 rounding)."""
+    M, N = 3, 8
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 88 + K)
+    assert S.shape == (-(-K // G), N)
+    q = unpack_numpy(Wb, K, N)
+    ex = exact_w4a16(A, q, S, G)
+    Y, Y64 = oracle.w4a16(A, Wb, S, G, want_f64=True)
+    ref64 = np.array([[float(v) for v in row] for row in ex])
+    assert np.allclose(Y64, ref64, rtol=1e-14, atol=0)
+    assert np.array_equal(bits16(Y), bits16(ref64.astype(np.float16)))
+    # the last group's scales act on exactly the last K - (ceil(K/G) - 1) G rows
+    S2 = S.copy()
+    S2[-1] = np.float16(0.0)
+    _, Y64b = oracle.w4a16(A, Wb, S2, G, want_f64=True)
+    k0 = (S.shape[0] - 1) * G
+    Ab = A.copy()
+    Ab[:, k0:] = np.float16(0.0)
+    _, Y64c = oracle.w4a16(Ab, Wb, S, G, want_f64=True)
+    assert np.allclose(Y64b, Y64c, rtol=1e-14, atol=1e-300)
+
+
 # ------------------------------------------------------------------ int8 quant / dequant
 
 def test_quant_hand_rows():

@@ -178,6 +178,35 @@ def test_frag8_offset_binary_values():
     assert (oracle.w8a16_prepack(np.zeros((K, N), np.int8), K, N) == 0x80).all()
 
 
+@pytest.mark.parametrize("K,N", [(200, 136), (8, 8), (1000, 24)])
+def test_frag8_ragged_is_the_zero_padded_layout(K, N):
+    """Ragged K and N pad to whole 128 x 128 tiles with weight 0 (offset-binary 128): the bytes
+    equal the layout of the matrix extended with zero rows and columns."""
+    W = qi.w8a16_problem(1, K, N, 32, 336 + K)[1]
+    Kp, Np = -(-K // 128) * 128, -(-N // 128) * 128
+    Wp = np.zeros((Kp, Np), np.int8)
+    Wp[:K, :N] = W
+    F = oracle.w8a16_prepack(W, K, N)
+    assert F.size == Kp * Np
+    assert np.array_equal(F, oracle.w8a16_prepack(Wp, Kp, Np))
+    idx = np.array([[oracle.frag8_byte_index(K, k, n) for n in range(N)] for k in range(K)]).ravel()
+    assert np.unique(idx).size == K * N
+    pad = np.ones(F.size, bool)
+    pad[idx] = False
+    assert np.all(F[pad] == 128)
+
+
+@pytest.mark.parametrize("K,G", [(40, 32), (200, 64), (72, 72)])
+def test_w8a16_partial_last_group_exact(K, G):
+    M, N = 2, 5
+    A, W, S = qi.w8a16_problem(M, K, N, G, 337 + K)
+    assert S.shape == (-(-K // G), N)
+    ref64 = np.array([[float(v) for v in row] for row in exact(A, W, S, G)])
+    Y, Y64 = oracle.w8a16(A, W, S, G, want_f64=True)
+    assert np.allclose(Y64, ref64, rtol=1e-14, atol=0)
+    assert np.array_equal(bits16(Y), bits16(ref64.astype(np.float16)))
+
+
 def test_frag8_moves_every_byte():
     K, N = 256, 384
     W = qi.w8a16_problem(1, K, N, 128, 335)[1]
