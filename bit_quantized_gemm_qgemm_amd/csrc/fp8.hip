@@ -358,7 +358,10 @@ extern "C" int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, 
     if (!qgh::aligned(X, 16) || !qgh::aligned(Q, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
     hipStream_t st = (hipStream_t)stream;
     if (per_row) {
-        if (cols <= 256) {
+        if (cols <= 128) {  // one 16-byte chunk per lane (the KV rows of 128 values)
+            hipLaunchKernelGGL((fp8_quant_rows_kernel<16, 1>), dim3((rows + 15) / 16), dim3(256), 0, st, X, Q,
+                               scales, rows, cols);
+        } else if (cols <= 256) {
             hipLaunchKernelGGL((fp8_quant_rows_kernel<16, 2>), dim3((rows + 15) / 16), dim3(256), 0, st, X, Q,
                                scales, rows, cols);
         } else {

@@ -20,14 +20,16 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
     const int c = blockIdx.y;           // 128-k chunk
     const int t = threadIdx.x;
     const int row_bytes = N / 2;
-    // 128 rows x 16 words: 2048 words, 8 per thread
+    // 128 rows x 16 words: 2048 words, 8 per thread; words past K or N (a
+    // ragged shape's last tile) are weight 0, nibbles 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int w = t + 256 * i;
         const int r = w >> 4, cw = w & 15;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(
-            wn + (size_t)(c * 128 + r) * row_bytes + (size_t)n_tile * 64);
-        tile[r][cw] = src[cw];
+        const int k = c * 128 + r, byte = n_tile * 64 + cw * 4;
+        tile[r][cw] = (k < K && byte < row_bytes)
+                          ? *reinterpret_cast<const uint32_t*>(wn + (size_t)k * row_bytes + byte)
+                          : 0u;
     }
     __syncthreads();
     // thread t writes words 8t .. 8t+7 of the tile
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
         }
         out[i] = word;
     }
-    const int kchunks = K / 128;
+    const int kchunks = (K + 127) / 128;
     uint8_t* dst = wf + ((size_t)n_tile * kchunks + c) * 8192u + (size_t)t * 32u;
     reinterpret_cast<qg::uintx4*>(dst)[0] = qg::uintx4{out[0], out[1], out[2], out[3]};
     reinterpret_cast<qg::uintx4*>(dst)[1] = qg::uintx4{out[4], out[5], out[6], out[7]};
@@ -59,9 +61,10 @@ __global__ __launch_bounds__(256) void prepack_kernel(const uint8_t* __restrict_
 
 }  // namespace
 
+// K and N are padded to whole 128 x 128 tiles (weight 0 in the padding).
 extern "C" size_t qgemm_w4a16_packed_bytes(int32_t K, int32_t N) {
-    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 128 != 0) return 0;
-    return (size_t)K * (size_t)N / 2;
+    if (K <= 0 || N <= 0 || K % 8 != 0 || N % 8 != 0) return 0;
+    return (size_t)((K + 127) / 128) * 128 * (size_t)((N + 127) / 128) * 128 / 2;
 }
 
 extern "C" int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag, int32_t K,
@@ -69,12 +72,12 @@ extern "C" int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag
     if (!w_natural || !w_frag) return QGEMM_NULL_PTR;
     if (K < 0 || N < 0) return QGEMM_BAD_SHAPE;
     if (K == 0 || N == 0) return QGEMM_OK;
-    if (K % 128 != 0 || N % 128 != 0) return QGEMM_UNSUPPORTED;
+    if (K % 8 != 0 || N % 8 != 0) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(w_natural, 16) || !qgh::aligned(w_frag, 16)) return QGEMM_MISALIGNED;
-    const size_t bytes = (size_t)K * N / 2;
+    const size_t in_bytes = (size_t)K * N / 2, out_bytes = qgemm_w4a16_packed_bytes(K, N);
     const uintptr_t a = (uintptr_t)w_natural, b = (uintptr_t)w_frag;
-    if (a < b + bytes && b < a + bytes) return QGEMM_BAD_SHAPE;  // overlapping buffers
-    dim3 grid(N / 128, K / 128);
+    if (a < b + out_bytes && b < a + in_bytes) return QGEMM_BAD_SHAPE;  // overlapping buffers
+    dim3 grid((N + 127) / 128, (K + 127) / 128);
     hipLaunchKernelGGL(prepack_kernel, grid, dim3(256), 0, (hipStream_t)stream, w_natural, w_frag,
                        (int)K, (int)N);
     return qgh::launch_status();

@@ -9,6 +9,8 @@
 // and 128x256 prefill (chosen by default when it has enough tiles to fill
 // the chip; A tiles and B fragment blocks reach LDS by direct DMA).  Each
 // launch shape is also a tactic a caller can list, select or autotune.
+// K or N that are not multiples of 128 (the page's ceil(K/G) scale rows and
+// padded fragment tiles) run the decode or the 128x128 prefill kernel.
 #include "common.hpp"
 #include "wq_gemm.hpp"
 
@@ -25,9 +27,9 @@ bool tactic_valid(int tactic, int M, int N, int K) {
     switch (tactic) {
         case QGEMM_W4A16_TACTIC_DECODE_NARROW: return M <= 2;
         case QGEMM_W4A16_TACTIC_DECODE_BALANCED: return M <= 16;
-        case QGEMM_W4A16_TACTIC_SPLITK: return M <= 512 && (size_t)M * K < ((size_t)1 << 31);
+        case QGEMM_W4A16_TACTIC_SPLITK: return !ragged(N, K) && M <= 512 && (size_t)M * K < ((size_t)1 << 31);
         case QGEMM_W4A16_TACTIC_PREFILL: return true;
-        case QGEMM_W4A16_TACTIC_PREFILL_LARGE: return N % PL_BN == 0;
+        case QGEMM_W4A16_TACTIC_PREFILL_LARGE: return !ragged(N, K) && N % PL_BN == 0;
         default: return false;
     }
 }
@@ -41,6 +43,7 @@ bool tactic_valid(int tactic, int M, int N, int K) {
 int default_tactic(int M, int N, int K, bool workspace) {
     if (M <= 2) return QGEMM_W4A16_TACTIC_DECODE_NARROW;
     if (M <= 16) return QGEMM_W4A16_TACTIC_DECODE_BALANCED;
+    if (ragged(N, K)) return QGEMM_W4A16_TACTIC_PREFILL;
     if (workspace && mid_path(M, K)) return QGEMM_W4A16_TACTIC_SPLITK;
     const long large_tiles = (long)(N / PL_BN) * ((M + PL_BM - 1) / PL_BM);
     if (N % PL_BN != 0 || large_tiles < 160) return QGEMM_W4A16_TACTIC_PREFILL;
@@ -74,18 +77,18 @@ int32_t launch_w4a16_g(int tactic, const uint16_t* A, const uint8_t* wf, const u
     return qgh::launch_status();
 }
 
-// Shape and group support of every W4A16 call (M > 0).
+// Shape and group support of every W4A16 call (M > 0): K and N multiples of
+// 8 (16-byte rows of A and Y), not necessarily of 128 or of G.
 bool w4a16_shape_ok(int M, int N, int K, int G) {
-    return M > 0 && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 && (G == 32 || G == 64 || G == 128);
+    return M > 0 && N > 0 && K > 0 && N % 8 == 0 && K % 8 == 0 && (G == 32 || G == 64 || G == 128);
 }
 
 // Validation shared by the launching entry points; QGEMM_OK means "launch".
 int32_t w4a16_check(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales, uint16_t* Y, int M, int N,
                     int K, int G) {
     if (M < 0 || N < 0 || K < 0 || G <= 0) return QGEMM_BAD_SHAPE;
-    if (K % G != 0) return QGEMM_BAD_SHAPE;
     if (!A || !w_frag || !scales || !Y) return QGEMM_NULL_PTR;
-    if (N == 0 || K == 0 || N % 128 != 0 || K % 128 != 0) return QGEMM_UNSUPPORTED;
+    if (N == 0 || K == 0 || N % 8 != 0 || K % 8 != 0) return QGEMM_UNSUPPORTED;
     if (G != 32 && G != 64 && G != 128) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(A, 16) || !qgh::aligned(w_frag, 16) || !qgh::aligned(scales, 4) ||
         !qgh::aligned(Y, 16))
@@ -97,18 +100,18 @@ int32_t w4a16_check(const uint16_t* A, const uint8_t* w_frag, const uint16_t* sc
 
 // the mid-M path's fp32 split partials; 0 for every other shape
 extern "C" size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G) {
-    if (M <= 0 || N <= 0 || K <= 0 || G <= 0 || N % 128 != 0 || K % 128 != 0 || K % G != 0) return 0;
+    if (!w4a16_shape_ok(M, N, K, G) || ragged(N, K)) return 0;
     return mid_path(M, K) ? mid_workspace_bytes(M, N, K) : 0;
 }
 
 extern "C" int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const uint16_t* scales,
                                uint16_t* Y, int32_t M, int32_t N, int32_t K, int32_t G,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    if (M == 0 && N >= 0 && K >= 0 && G > 0 && K % G == 0) return QGEMM_OK;
+    if (M == 0 && N >= 0 && K >= 0 && G > 0) return QGEMM_OK;
     const int32_t st = w4a16_check(A, w_frag, scales, Y, M, N, K, G);
     if (st != QGEMM_OK) return st;
     float* part = nullptr;
-    if (mid_path(M, K) && workspace && qgh::aligned(workspace, 16) &&
+    if (!ragged(N, K) && mid_path(M, K) && workspace && qgh::aligned(workspace, 16) &&
         workspace_bytes >= mid_workspace_bytes(M, N, K))
         part = static_cast<float*>(workspace);
     return launch_w4a16_g(default_tactic(M, N, K, part != nullptr), A, w_frag, scales, Y, M, N, K, G, part,
@@ -139,7 +142,7 @@ extern "C" int32_t qgemm_w4a16_tactic(const uint16_t* A, const uint8_t* w_frag, 
                                       size_t workspace_bytes, void* stream) {
     if (tactic == QGEMM_TACTIC_DEFAULT)
         return qgemm_w4a16(A, w_frag, scales, Y, M, N, K, G, workspace, workspace_bytes, stream);
-    if (M == 0 && N >= 0 && K >= 0 && G > 0 && K % G == 0) return QGEMM_OK;
+    if (M == 0 && N >= 0 && K >= 0 && G > 0) return QGEMM_OK;
     const int32_t st = w4a16_check(A, w_frag, scales, Y, M, N, K, G);
     if (st != QGEMM_OK) return st;
     if (!tactic_valid(tactic, M, N, K)) return QGEMM_UNSUPPORTED;

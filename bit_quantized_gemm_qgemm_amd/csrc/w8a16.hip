@@ -29,14 +29,17 @@ __global__ __launch_bounds__(256) void prepack8_kernel(const int8_t* __restrict_
                                                        uint8_t* __restrict__ wf, int K, int N) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128 * P8_PITCH];
     const int n_tile = blockIdx.x, c = blockIdx.y, t = threadIdx.x;
+    // 8-byte pieces (rows of N % 8 == 0 bytes are 8-byte aligned); pieces past
+    // K or N (a ragged shape's last tile) are weight 0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = t + 256 * i, r = idx >> 3, col = idx & 7;
-        *reinterpret_cast<uintx4*>(&tile[r * P8_PITCH + col * 16]) = *reinterpret_cast<const uintx4*>(
-            wn + (size_t)(c * 128 + r) * N + (size_t)n_tile * 128 + col * 16);
+    for (int i = 0; i < 8; ++i) {
+        const int idx = t + 256 * i, r = idx >> 4, col = idx & 15;
+        const int k = c * 128 + r, n = n_tile * 128 + col * 8;
+        *reinterpret_cast<uintx2*>(&tile[r * P8_PITCH + col * 8]) =
+            (k < K && n < N) ? *reinterpret_cast<const uintx2*>(wn + (size_t)k * N + n) : uintx2{0u, 0u};
     }
     __syncthreads();
-    const int kchunks = K / 128;
+    const int kchunks = (K + 127) / 128;
     uint8_t* dst = wf + ((size_t)n_tile * kchunks + c) * 16384u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -66,7 +69,7 @@ int32_t launch_w8a16(const uint16_t* A, const uint8_t* wf, const uint16_t* S, in
         launch_wq_decode<8, G>(A, wf, S, ldS, Y, M, N, K, st);
     } else if (part) {
         launch_wq_mid<8, G>(A, wf, S, ldS, Y, M, N, K, part, st);
-    } else if (N % PL_BN != 0 || (long)(N / PL_BN) * ((M + PL_BM - 1) / PL_BM) < 160) {
+    } else if (ragged(N, K) || N % PL_BN != 0 || (long)(N / PL_BN) * ((M + PL_BM - 1) / PL_BM) < 160) {
         launch_wq_prefill<8, G>(A, wf, S, ldS, Y, M, N, K, st);
     } else {
         // the 128x256 kernel once it has enough tiles for the chip (the W4A16 rule)
@@ -80,9 +83,10 @@ bool w8a16_group_ok(int G, int K) { return G == 32 || G == 64 || G == 128 || G =
 
 }  // namespace
 
+// K and N are padded to whole 128 x 128 tiles (weight 0 in the padding).
 extern "C" size_t qgemm_w8a16_packed_bytes(int32_t K, int32_t N) {
-    if (K <= 0 || N <= 0 || K % 128 != 0 || N % 128 != 0) return 0;
-    return (size_t)K * (size_t)N;
+    if (K <= 0 || N <= 0 || K % 8 != 0 || N % 8 != 0) return 0;
+    return (size_t)((K + 127) / 128) * 128 * (size_t)((N + 127) / 128) * 128;
 }
 
 extern "C" int32_t qgemm_w8a16_prepack(const int8_t* w_natural, uint8_t* w_frag, int32_t K, int32_t N,
@@ -90,18 +94,18 @@ extern "C" int32_t qgemm_w8a16_prepack(const int8_t* w_natural, uint8_t* w_frag,
     if (!w_natural || !w_frag) return QGEMM_NULL_PTR;
     if (K < 0 || N < 0) return QGEMM_BAD_SHAPE;
     if (K == 0 || N == 0) return QGEMM_OK;
-    if (K % 128 != 0 || N % 128 != 0) return QGEMM_UNSUPPORTED;
+    if (K % 8 != 0 || N % 8 != 0) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(w_natural, 16) || !qgh::aligned(w_frag, 16)) return QGEMM_MISALIGNED;
-    const size_t bytes = (size_t)K * N;
+    const size_t in_bytes = (size_t)K * N, out_bytes = qgemm_w8a16_packed_bytes(K, N);
     const uintptr_t a = (uintptr_t)w_natural, b = (uintptr_t)w_frag;
-    if (a < b + bytes && b < a + bytes) return QGEMM_BAD_SHAPE;  // overlapping buffers
-    hipLaunchKernelGGL(prepack8_kernel, dim3(N / 128, K / 128), dim3(256), 0, (hipStream_t)stream, w_natural,
-                       w_frag, (int)K, (int)N);
+    if (a < b + out_bytes && b < a + in_bytes) return QGEMM_BAD_SHAPE;  // overlapping buffers
+    hipLaunchKernelGGL(prepack8_kernel, dim3((N + 127) / 128, (K + 127) / 128), dim3(256), 0, (hipStream_t)stream,
+                       w_natural, w_frag, (int)K, (int)N);
     return qgh::launch_status();
 }
 
 extern "C" size_t qgemm_w8a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G) {
-    if (M <= 0 || N <= 0 || K <= 0 || G <= 0 || N % 128 != 0 || K % 128 != 0 || K % G != 0) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || G <= 0 || N % 8 != 0 || K % 8 != 0 || ragged(N, K)) return 0;
     if (!w8a16_group_ok(G, K)) return 0;
     return mid_path(M, K) ? mid_workspace_bytes(M, N, K) : 0;
 }
@@ -110,17 +114,16 @@ extern "C" int32_t qgemm_w8a16(const uint16_t* A, const uint8_t* w_frag, const u
                                int32_t M, int32_t N, int32_t K, int32_t G, void* workspace,
                                size_t workspace_bytes, void* stream) {
     if (M < 0 || N < 0 || K < 0 || G <= 0) return QGEMM_BAD_SHAPE;
-    if (K % G != 0) return QGEMM_BAD_SHAPE;
     if (M == 0) return QGEMM_OK;
     if (!A || !w_frag || !scales || !Y) return QGEMM_NULL_PTR;
-    if (N == 0 || K == 0 || N % 128 != 0 || K % 128 != 0) return QGEMM_UNSUPPORTED;
+    if (N == 0 || K == 0 || N % 8 != 0 || K % 8 != 0) return QGEMM_UNSUPPORTED;
     if (!w8a16_group_ok(G, K)) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(A, 16) || !qgh::aligned(w_frag, 16) || !qgh::aligned(scales, 4) ||
         !qgh::aligned(Y, 16))
         return QGEMM_MISALIGNED;
     hipStream_t st = (hipStream_t)stream;
     float* part = nullptr;
-    if (mid_path(M, K) && workspace && qgh::aligned(workspace, 16) &&
+    if (!ragged(N, K) && mid_path(M, K) && workspace && qgh::aligned(workspace, 16) &&
         workspace_bytes >= mid_workspace_bytes(M, N, K))
         part = static_cast<float*>(workspace);
     // one scale per column (G == K > 128): 128-k groups that all read scale row 0

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     // NSW x 256); a slot past the range repeats its last strip and is not stored
     int strip0, nst;
     if constexpr (BAL) {
-        const int wg = xcd_contiguous(blockIdx.x, gridDim.x), nstrips = N / 16;
+        const int wg = xcd_contiguous(blockIdx.x, gridDim.x), nstrips = (N + 15) / 16;
         strip0 = (int)((long)wg * nstrips / gridDim.x);
         nst = (int)((long)(wg + 1) * nstrips / gridDim.x) - strip0;
     } else {
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
         nst = NSW;
     }
     const int cl = lane & 15, q = lane >> 4;
-    const int kchunks = K / 128;
+    const int kchunks = (K + 127) / 128;  // of the (padded) fragment layout
     const int arow = cl & (MT - 1);  // rows >= MT of the MFMA tile are never stored
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     floatx4 acc[NSW];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
             ast[p] = *reinterpret_cast<const uintx4*>(A + (size_t)row * K + kw0 * (kwl > 0) + c8 * 8);
         }
         const int sp_g = lane / (NSW * 2), sp_r = lane % (NSW * 2);  // group, 8-column piece
-        const bool sp_ok = lane < SPL && sp_g * G < kwl && sp_r < 2 * nst;
+        const bool sp_ok = lane < SPL && sp_g * G < kwl && sp_r < 2 * nst && strip0 * 16 + sp_r * 8 < N;
         const uintx4 sreg = *reinterpret_cast<const uintx4*>(
             Sc + (sp_ok ? (size_t)(kw0 / G + sp_g) * ldS + strip0 * 16 + sp_r * 8 : 0));
         uintx4 braw[KCW][NSW][P];
@@ -173,8 +173,11 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
         for (int p = 0; p < APL; ++p) {
             const int idx = lane + 64 * p, row = idx / (KW / 8), c8 = idx % (KW / 8);
             // (Whole-vector bit casts only: a bit cast of one element of a
-            // u32x4 was miscompiled by this toolchain into element 0.)
-            const half8 h = __builtin_bit_cast(half8, ast[p]);
+            // u32x4 was miscompiled by this toolchain into element 0.)  A
+            // piece at or past K (a ragged K's last chunk) stages as zeros, so
+            // that it adds nothing to the raw products or to C.
+            const bool kin = idx < APIECES && c8 * 8 < kwl;
+            const half8 h = __builtin_bit_cast(half8, kin ? ast[p] : uintx4{0u, 0u, 0u, 0u});
             if constexpr (CM) {
                 if (idx < APIECES) *reinterpret_cast<half8*>(&L.a[row * LDA + c8 * 8]) = h;
             } else {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 4 * q + j;  // accumulator layout: rows 4*(l/16)+j, column l%16
-            if (row < M) Y[(size_t)row * N + n] = f2h(t[j]);
+            if (row < M && n < N) Y[(size_t)row * N + n] = f2h(t[j]);
         }
     }
 }
@@ -271,7 +274,8 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
     const int mtiles = (M + PF_BM - 1) / PF_BM;
     const int L = blockIdx.x;
     const int m0 = (L % mtiles) * PF_BM, n0 = (L / mtiles) * PF_BN;
-    const int kchunks = K / 128;
+    const int kchunks = (K + 127) / 128;  // of the (padded) fragment layout
+    const int gmax = (K + (G < 128 ? G : 128) - 1) / (G < 128 ? G : 128) - 1;  // last scale row
     const int h = lane >> 5, c32 = lane & 31;
     const int ncol0 = n0 + wn * 64;
 
@@ -290,8 +294,12 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
         for (int i = 0; i < 8; ++i) {
             const int idx = tid + 256 * i, row = idx >> 4, col = idx & 15;
             const int gm = m0 + row;
-            // rows >= M repeat row M-1 (unconditional load; those rows are not stored)
-            areg[i] = *reinterpret_cast<const uintx4*>(A + (size_t)(gm < M ? gm : M - 1) * K + c * 128 + col * 8);
+            // rows >= M repeat row M-1 (unconditional load; those rows are not
+            // stored); pieces at or past K (ragged K) read the row's first
+            // piece and become zeros
+            const int k8 = c * 128 + col * 8;
+            const uintx4 v = *reinterpret_cast<const uintx4*>(A + (size_t)(gm < M ? gm : M - 1) * K + (k8 < K ? k8 : 0));
+            areg[i] = k8 < K ? v : uintx4{0u, 0u, 0u, 0u};
         }
     };
     auto store_a = [&](int buf) {
@@ -328,13 +336,13 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
     // leaves one staged chunk for the tail.
     Chunk b0, b1;
     load_a(0);
-    load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, 0, ncol0, lane);
+    load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, 0, ncol0, lane, gmax, N - 1);
     store_a(0);
     __syncthreads();
     int c = 0;
     for (; c + 1 < kchunks; c += 2) {
         load_a(c + 1);
-        load_b_chunk<2, G, WB>(b1, wf, S, ldS, kchunks, c + 1, ncol0, lane);
+        load_b_chunk<2, G, WB>(b1, wf, S, ldS, kchunks, c + 1, ncol0, lane, gmax, N - 1);
         __builtin_amdgcn_sched_barrier(0);
         compute(sA[0], b0);
         __builtin_amdgcn_sched_barrier(0);
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
         __syncthreads();
         const int c2 = c + 2 < kchunks ? c + 2 : c + 1;
         load_a(c2);
-        load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, c2, ncol0, lane);
+        load_b_chunk<2, G, WB>(b0, wf, S, ldS, kchunks, c2, ncol0, lane, gmax, N - 1);
         __builtin_amdgcn_sched_barrier(0);
         compute(sA[1], b1);
         __builtin_amdgcn_sched_barrier(0);
@@ -374,11 +382,12 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
                     uintx2{e0, e1};
             }
     __syncthreads();
-    // 128 rows x 16 pieces of 8 outputs (N % 128 == 0: whole, aligned pieces)
+    // 128 rows x 16 pieces of 8 outputs (N % 8 == 0: a piece is all inside
+    // or all past N)
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int idx = tid + 256 * p, row = idx >> 4, piece = idx & 15;
-        if (m0 + row < M)
+        if (m0 + row < M && n0 + piece * 8 < N)
             *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8) =
                 *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
     }
@@ -811,18 +820,19 @@ __global__ __launch_bounds__(256) void wq_splitk_reduce_kernel(const float* __re
 template <int WB, int G>
 void launch_wq_decode_narrow(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
                              int M, int N, int K, hipStream_t st) {
+    const int nstrips = (N + 15) / 16;
     if (M == 1)
-        hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(nstrips), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
     else
-        hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(N / 16), dim3(512), 0, st, A, wf,
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(nstrips), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
 }
 
 template <int WB, int G>
 void launch_wq_decode_balanced(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
                                int M, int N, int K, hipStream_t st) {
-    const int nstrips = N / 16;
+    const int nstrips = (N + 15) / 16;
     int nwg = nstrips < 256 ? nstrips : 256;
     if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
     if (M <= 4)
@@ -849,7 +859,7 @@ void launch_wq_decode(const uint16_t* A, const uint8_t* wf, const uint16_t* S, i
 template <int WB, int G>
 void launch_wq_prefill(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y, int M,
                        int N, int K, hipStream_t st) {
-    dim3 grid((N / PF_BN) * ((M + PF_BM - 1) / PF_BM));
+    dim3 grid(((N + PF_BN - 1) / PF_BN) * ((M + PF_BM - 1) / PF_BM));
     hipLaunchKernelGGL((wq_prefill_kernel<WB, G>), grid, dim3(256), 0, st, A, wf, S, ldS, Y, M, N, K);
 }
 
@@ -868,5 +878,11 @@ void launch_wq_mid(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int 
 inline bool mid_path(int M, int K) {
     return M > 16 && M <= MID_MAX_M && (size_t)M * K < ((size_t)1 << 31);
 }
+
+// K or N not a multiple of 128: only the decode and 128x128 prefill kernels
+// (register-staged A with a per-piece K test, masked stores) take such
+// shapes; the split-K and 128x256 kernels copy A straight to LDS by DMA and
+// assume whole 128-k chunks and 128-column tiles.
+inline bool ragged(int N, int K) { return N % 128 != 0 || K % 128 != 0; }
 
 }  // namespace

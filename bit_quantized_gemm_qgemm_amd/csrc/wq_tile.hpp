@@ -111,10 +111,13 @@ struct BChunk {
 // Fetch chunk c of columns ncol0 .. ncol0 + 32*WTN - 1 (ncol0 % 32 == 0).
 // Scale row of group g of chunk c: (c * 128 / G + g) * ldS elements from S
 // (ldS = N; ldS = 0 reads row 0 for every group: one scale per column).
+// Scale reads past the last group row (gmax) or column (nmax) of a ragged
+// shape read those instead: they only meet zero A values or padded columns
+// that are never stored, and keep every read inside S.
 template <int WTN, int G, int WB = 4>
 __device__ __forceinline__ void load_b_chunk(BChunk<WTN, G, WB>& b, const uint8_t* __restrict__ wf,
                                              const uint16_t* __restrict__ S, int ldS, int kchunks,
-                                             int c, int ncol0, int lane) {
+                                             int c, int ncol0, int lane, int gmax, int nmax) {
     constexpr int P = WFormat<WB>::kPieces;
     const int h = lane >> 5;
 #pragma unroll
@@ -130,7 +133,8 @@ __device__ __forceinline__ void load_b_chunk(BChunk<WTN, G, WB>& b, const uint8_
                     ldg_nt(reinterpret_cast<const uintx4*>(blk + p * 1024 + (cl + 16 * (h + 2 * qi)) * 16));
 #pragma unroll
         for (int g = 0; g < BChunk<WTN, G, WB>::NG; ++g) {
-            b.sc[t][g] = S[(size_t)(c * BChunk<WTN, G, WB>::NG + g) * ldS + n];
+            const int gr = c * BChunk<WTN, G, WB>::NG + g;
+            b.sc[t][g] = S[(size_t)(gr < gmax ? gr : gmax) * ldS + (n < nmax ? n : nmax)];
         }
     }
 }

@@ -72,12 +72,19 @@ QGEMM_API const char* qgemm_status_str(int32_t status);
  * (bits 0-3) of byte [k][n/2] for even n and the high nibble for odd n; each
  * nibble is a two's-complement int4 in [-8, 7].
  *
- * Supported in this version: K % 128 == 0, N % 128 == 0, G in {32, 64, 128}
- * (K % G == 0 then holds); other shapes return QGEMM_UNSUPPORTED.
+ * Supported in this version: K % 8 == 0 and N % 8 == 0 (rows of A and Y stay
+ * 16-byte aligned), G in {32, 64, 128}; other shapes return
+ * QGEMM_UNSUPPORTED.  K need not be a multiple of 128 or of G (the page's
+ * ceil(K/G) scale rows: the last group covers the remaining K % G rows) and
+ * N need not be a multiple of 128: the fragment layout is padded to whole
+ * 128 x 128 tiles with weight 0 (the page's fragment rows
+ * ceil(N/128) * ceil(K/64) * 8), and such shapes run the decode or the
+ * 128x128 prefill kernel (tactics 1, 2 and 4).
  * ---------------------------------------------------------------------- */
 
-/* Bytes of the fragment-layout weight buffer for a K x N int4 matrix
-   (= K*N/2); 0 if the shape is unsupported. */
+/* Bytes of the fragment-layout weight buffer for a K x N int4 matrix,
+   padded to whole 128 x 128 tiles: ceil(K/128)*128 * ceil(N/128)*128 / 2
+   (= K*N/2 when both are multiples of 128); 0 if the shape is unsupported. */
 QGEMM_API size_t qgemm_w4a16_packed_bytes(int32_t K, int32_t N);
 
 /* Repack natural int4 weights into the library's gfx950 fragment layout.
@@ -90,15 +97,15 @@ QGEMM_API int32_t qgemm_w4a16_prepack(const uint8_t* w_natural, uint8_t* w_frag,
                             void* stream);
 
 /* Workspace bytes qgemm_w4a16 uses for this shape: for 16 < M <= 128 (and
-   M*K < 2^31) the fp32 partial sums of its split-K path,
-   S * M * N * 4 bytes with S = max(1, min(floor(512 / (N/128)), K/128, 16)); 0 for
-   every other shape and for invalid arguments. */
+   M*K < 2^31, K and N multiples of 128) the fp32 partial sums of its split-K
+   path, S * M * N * 4 bytes with S = max(1, min(floor(512 / (N/128)), K/128, 16));
+   0 for every other shape and for invalid arguments. */
 QGEMM_API size_t qgemm_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t G);
 
 /* Y = A x dequant(w_frag, scales).
    A:      fp16 [M][K] activations (M = batch * sequence length).
    w_frag: prepacked weights from qgemm_w4a16_prepack(K, N).
-   scales: fp16 [K/G][N].
+   scales: fp16 [ceil(K/G)][N].
    Y:      fp16 [M][N] output; must not overlap the inputs.
    workspace: device memory of workspace_bytes bytes (16-byte aligned), or
    NULL / 0.  M == 0 is a successful no-op.  M <= 16 runs the memory-bound
@@ -123,10 +130,12 @@ QGEMM_API int32_t qgemm_w4a16(const uint16_t* A, const uint8_t* w_frag, const ui
  * fp16 tolerance, not bit for bit; each tactic alone is deterministic):
  *   1 decode, one 16-column strip per workgroup      valid for M <= 2
  *   2 decode, balanced ranges of up to 3 strips      valid for M <= 16
- *   3 split-K with fp32 partials + ordered reduction valid for M <= 512 and
- *     M*K < 2^31; needs qgemm_w4a16_tactic_workspace_bytes() of workspace
+ *   3 split-K with fp32 partials + ordered reduction valid for M <= 512,
+ *     M*K < 2^31, K % 128 == 0 and N % 128 == 0; needs
+ *     qgemm_w4a16_tactic_workspace_bytes() of workspace
  *   4 prefill, 128x128 tiles                         valid for every M
  *   5 prefill, 128x256 tiles (LDS DMA)               valid for N % 256 == 0
+ *                                                    and K % 128 == 0
  * The library keeps no tactic state: a caller that autotunes keeps the
  * result per shape.
  * ---------------------------------------------------------------------- */
@@ -178,12 +187,16 @@ QGEMM_API int32_t qgemm_w4a16_autotune(const uint16_t* A, const uint8_t* w_frag,
  * Natural weight format: int8 [K][N] (two's complement, full range
  * [-128, 127]).  G = K means one scale per column (S is fp16 [1][N]).
  *
- * Supported in this version: K % 128 == 0, N % 128 == 0, G in {32, 64, 128}
- * or G == K; other shapes return QGEMM_UNSUPPORTED.
+ * Supported in this version: K % 8 == 0, N % 8 == 0, G in {32, 64, 128} or
+ * G == K; other shapes return QGEMM_UNSUPPORTED.  As for W4A16, K and N need
+ * not be multiples of 128 nor K of G (scales [ceil(K/G)][N], the layout
+ * padded to whole 128 x 128 tiles with weight 0; such shapes run the decode
+ * or the 128x128 prefill kernel).
  * ---------------------------------------------------------------------- */
 
-/* Bytes of the int8 fragment-layout buffer for a K x N matrix (= K*N); 0 if
-   the shape is unsupported. */
+/* Bytes of the int8 fragment-layout buffer for a K x N matrix, padded to
+   whole 128 x 128 tiles: ceil(K/128)*128 * ceil(N/128)*128 (= K*N when both
+   are multiples of 128); 0 if the shape is unsupported. */
 QGEMM_API size_t qgemm_w8a16_packed_bytes(int32_t K, int32_t N);
 
 /* Repack natural int8 weights into the library's int8 fragment layout.
@@ -202,7 +215,7 @@ QGEMM_API size_t qgemm_w8a16_workspace_bytes(int32_t M, int32_t N, int32_t K, in
 /* Y = A x (W * S).
    A:      fp16 [M][K] activations.
    w_frag: prepacked weights from qgemm_w8a16_prepack(K, N).
-   scales: fp16 [K/G][N] ([1][N] for G == K).
+   scales: fp16 [ceil(K/G)][N] ([1][N] for G == K).
    Y:      fp16 [M][N] output; must not overlap the inputs.
    workspace: as for qgemm_w4a16.  M <= 16 runs the memory-bound decode
    kernel, 16 < M <= 128 with enough workspace the split-K kernel, every

@@ -61,8 +61,11 @@ def test_version_and_status_strings(L):
 
 def test_size_queries(L):
     assert L.qgemm_w4a16_packed_bytes(4096, 11008) == 4096 * 11008 // 2
-    assert L.qgemm_w4a16_packed_bytes(4000, 11008) == 0
+    # ragged K and N pad to whole 128 x 128 tiles; K and N must be multiples of 8
+    assert L.qgemm_w4a16_packed_bytes(4000, 11008) == 4096 * 11008 // 2
+    assert L.qgemm_w4a16_packed_bytes(200, 136) == 256 * 256 // 2
     assert L.qgemm_w4a16_packed_bytes(4096, 100) == 0
+    assert L.qgemm_w4a16_packed_bytes(4092, 128) == 0
     assert L.qgemm_w4a16_workspace_bytes(1, 11008, 4096, 128) == 0
     assert L.qgemm_w4a16_workspace_bytes(16, 11008, 4096, 128) == 0
     assert L.qgemm_w4a16_workspace_bytes(129, 11008, 4096, 128) == 0
@@ -71,7 +74,7 @@ def test_size_queries(L):
                     (64, 131072, 4096)]:
         S = max(1, min(512 // (N // 128), K // 128, 16))
         assert L.qgemm_w4a16_workspace_bytes(M, N, K, 128) == S * M * N * 4, (M, N, K)
-    assert L.qgemm_w4a16_workspace_bytes(64, 11008, 4000, 128) == 0   # invalid K
+    assert L.qgemm_w4a16_workspace_bytes(64, 11008, 4000, 128) == 0   # ragged K: no split-K path
     ws = L.moe_w4a16_workspace_bytes(256, 4096, 14336, 8, 2)
     P_ = 512
     # down-projection K splits, by the rule the header states
@@ -91,8 +94,9 @@ def test_w4a16_validation(L):
     assert f(None, None, None, None, 0, 128, 128, 128, None, 0, None) == 0  # M == 0: no-op
     assert f(None, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, -1, 128, 128, 128, None, 0, None) == 2
-    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 128, 96, None, 0, None) == 2  # G does not divide K
-    assert f(FAKE, FAKE, FAKE, FAKE, 4, 120, 128, 128, None, 0, None) == 5
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 128, 96, None, 0, None) == 5  # G = 96
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 124, 128, 128, None, 0, None) == 5  # N % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 132, 128, None, 0, None) == 5  # K % 8
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 256, 256, None, 0, None) == 5  # G = 256
     assert f(FAKE + 2, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 3
     assert f(FAKE, FAKE, FAKE, FAKE + 8, 4, 128, 128, 128, None, 0, None) == 3
@@ -100,7 +104,8 @@ def test_w4a16_validation(L):
 
 def test_w8a16_size_queries_and_validation(L):
     assert L.qgemm_w8a16_packed_bytes(4096, 11008) == 4096 * 11008
-    assert L.qgemm_w8a16_packed_bytes(4000, 11008) == 0
+    assert L.qgemm_w8a16_packed_bytes(4000, 11008) == 4096 * 11008
+    assert L.qgemm_w8a16_packed_bytes(4000, 11004) == 0
     for M, N, K, G in [(17, 11008, 4096, 128), (64, 11008, 4096, 4096), (128, 256, 256, 64)]:
         S = max(1, min(512 // (N // 128), K // 128, 16))
         assert L.qgemm_w8a16_workspace_bytes(M, N, K, G) == S * M * N * 4, (M, N, K, G)
@@ -110,16 +115,16 @@ def test_w8a16_size_queries_and_validation(L):
     assert f(None, None, None, None, 0, 128, 128, 128, None, 0, None) == 0
     assert f(None, FAKE, FAKE, FAKE, 4, 128, 128, 128, None, 0, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, 4, -128, 128, 128, None, 0, None) == 2
-    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 384, 256, None, 0, None) == 2  # G does not divide K
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 384, 256, None, 0, None) == 5  # G = 256, neither <= 128 nor K
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 512, 256, None, 0, None) == 5  # G = 256 < K
-    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 200, 200, None, 0, None) == 5  # K % 128
-    assert f(FAKE, FAKE, FAKE, FAKE, 4, 96, 128, 128, None, 0, None) == 5   # N % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 128, 204, 204, None, 0, None) == 5  # K % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 100, 128, 128, None, 0, None) == 5  # N % 8
     assert f(FAKE, FAKE, FAKE + 2, FAKE, 4, 128, 128, 128, None, 0, None) == 3
     p = L.qgemm_w8a16_prepack
     assert p(None, FAKE, 128, 128, None) == 1
     assert p(FAKE, FAKE, 128, 0, None) == 0
     assert p(FAKE, FAKE, -128, 128, None) == 2
-    assert p(FAKE, FAKE, 128, 192, None) == 5
+    assert p(FAKE, FAKE, 128, 196, None) == 5
     assert p(FAKE + 4, FAKE + 65536, 128, 128, None) == 3
     assert p(FAKE, FAKE + 8192, 128, 128, None) == 2  # overlapping buffers
 
@@ -156,7 +161,10 @@ def test_w4a16_tactic_lists(L):
     assert tactics(512, 4096, 4096) == [3, 4, 5]
     assert tactics(513, 4096, 4096) == [4, 5]
     assert tactics(2048, 384, 4096) == [4]
-    assert tactics(0, 4096, 4096) == [] and tactics(8, 4096, 4000) == [] and tactics(8, 4096, 4096, 256) == []
+    assert tactics(0, 4096, 4096) == [] and tactics(8, 4096, 4092) == [] and tactics(8, 4096, 4096, 256) == []
+    # ragged K or N: the decode kernels and the 128x128 prefill only
+    assert tactics(8, 4096, 4000) == [2, 4] and tactics(1, 136, 4096) == [1, 2, 4]
+    assert tactics(64, 4096, 200) == [4] and tactics(2048, 4104, 4096) == [4]
     assert L.qgemm_w4a16_tactics(1, 4096, 4096, 128, None, 0) == 5
     buf = (ctypes.c_int32 * 2)()
     assert L.qgemm_w4a16_tactics(1, 4096, 4096, 128, buf, 2) == 5 and list(buf) == [1, 2]

@@ -183,6 +183,29 @@ def test_w4a16_deterministic(qg, M):
     assert np.array_equal(bits(y1), bits(y2))
 
 
+# K or N not a multiple of 128 (and K not a multiple of G): the prepack pads to whole tiles,
+# scales have ceil(K/G) rows, and every kernel that takes such shapes (decode, 128x128
+# prefill) is compared in full, under the default dispatch and under each valid tactic.
+RAGGED = [(1, 200, 136, 32), (2, 8, 8, 32), (5, 1000, 24, 64), (16, 4104, 264, 128), (9, 136, 1000, 128),
+          (40, 136, 1000, 128), (300, 520, 136, 32), (129, 4000, 1000, 128), (64, 264, 4104, 64)]
+
+
+@pytest.mark.parametrize("M,K,N,G", RAGGED)
+def test_w4a16_ragged(qg, M, K, N, G):
+    A, Wb, S = qi.w4a16_problem(M, K, N, G, 1300 + M + K + N)
+    assert S.shape == (-(-K // G), N)
+    Wf = qg.qgemm_w4a16_prepack(dev(Wb), K, N)
+    assert np.array_equal(host(Wf), oracle.w4a16_prepack(Wb, K, N))
+    ref = oracle.w4a16(A, Wb, S, G)
+    Ad, Sd = dev(A), dev(S)
+    assert_fp16_close(host(qg.qgemm_w4a16(Ad, Wf, Sd, G)), ref, f"w4a16 ragged M={M} K={K} N={N} G={G}")
+    tactics = qg.qgemm_w4a16_tactics(M, N, K, G)
+    assert 4 in tactics and 3 not in tactics and 5 not in tactics
+    for t in tactics:
+        Y = host(qg.qgemm_w4a16(Ad, Wf, Sd, G, tactic=t))
+        assert_fp16_close(Y, ref, f"w4a16 ragged tactic {t} M={M} K={K} N={N} G={G}")
+
+
 def test_w4a16_zero_m_is_noop(qg):
     Wb, S = qi.w4a16_weights(128, 128, 128, 1)
     Y = torch.full((1, 128), 7.0, dtype=torch.float16, device="cuda")

@@ -66,6 +66,19 @@ def run(qg, A, W, S, G, workspace=None):
     return host(qg.qgemm_w8a16(dev(A), Wf, dev(S), G, workspace=workspace))
 
 
+@pytest.mark.parametrize("G", [32, 128, "K"])
+@pytest.mark.parametrize("M,K,N", [(1, 200, 136), (7, 1000, 24), (16, 72, 264), (40, 136, 1000),
+                                   (300, 520, 136), (129, 4000, 520)])
+def test_w8a16_ragged(qg, M, K, N, G):
+    """K or N not a multiple of 128, K not a multiple of G: padded prepack, ceil(K/G) scale rows."""
+    g = gsize(G, K)
+    A, W, S = qi.w8a16_problem(M, K, N, g, 1400 + M + K + N)
+    Wf = qg.qgemm_w8a16_prepack(dev(W), K, N)
+    assert np.array_equal(host(Wf), oracle.w8a16_prepack(W, K, N))
+    Y = host(qg.qgemm_w8a16(dev(A), Wf, dev(S), g))
+    assert_fp16_close(Y, oracle.w8a16(A, W, S, g), f"w8a16 ragged M={M} K={K} N={N} G={G}")
+
+
 @pytest.mark.parametrize("K,N", [(128, 128), (256, 384), (512, 512), (4096, 11008)])
 def test_w8a16_prepack_bytes_match_oracle(qg, K, N):
     W = qi.w8a16_problem(1, K, N, 128, 600 + K + N)[1]
