@@ -71,7 +71,8 @@ def _declare(lib):
         "qo_moe_route": (None, [_P, _I32, _I32, _I32, _P, _P]),
         "qo_moe_permute": (None, [_P, _I32, _I32, _I32, _P, _P]),
         "qo_moe": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                          _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32]),
+                          _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32]),
+        "qo_moe_act": (ctypes.c_double, [ctypes.c_double, _I32]),
         "qo_e4m3_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
         "qo_f64_to_e4m3": (ctypes.c_uint8, [ctypes.c_double]),
         "qo_e4m3_to_f64_array": (None, [_P, _P, _I64]),
@@ -390,8 +391,17 @@ def moe_permute(ids, E):
     return offsets, pairs
 
 
-def moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=None, want_f64=False):
-    """SiLU-gated INT4 MoE.  Wg/Wu uint8 [E,H,I/2], Wd uint8 [E,I,H/2];
+MOE_SILU, MOE_GELU_ERF, MOE_GELU_TANH, MOE_RELU = 0, 1, 2, 3
+
+
+def moe_act(z, activation):
+    """The gate activation of the gated expert FFN, in fp64 (0 SiLU, 1 GELU erf form,
+    2 GELU tanh form, 3 ReLU)."""
+    return _load().qo_moe_act(float(z), int(activation))
+
+
+def moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=None, want_f64=False, activation=0):
+    """Gated INT4 MoE, h = fp16(act(g) * u).  Wg/Wu uint8 [E,H,I/2], Wd uint8 [E,I,H/2];
     Sg/Su fp16 [E,H/G,I], Sd fp16 [E,I/G,H].  Returns (Y, ids, w[, Y64]);
     with ``tokens`` only those rows of Y are computed (others are zero)."""
     X = _c(X, np.float16)
@@ -410,7 +420,7 @@ def moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, tokens=None, want_f64=False)
     tok = None if tokens is None else _c(np.asarray(tokens, np.int32), np.int32)
     _load().qo_moe(_ptr(X), _ptr(logits), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(Sg), _ptr(Su),
                    _ptr(Sd), _ptr(Y), _ptr(Y64), _ptr(ids), _ptr(w), T, H, I, E, topK, G,
-                   _ptr(tok), 0 if tok is None else tok.size)
+                   int(activation), _ptr(tok), 0 if tok is None else tok.size)
     return (Y, ids, w, Y64) if want_f64 else (Y, ids, w)
 
 

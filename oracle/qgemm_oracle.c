@@ -48,6 +48,7 @@
  *        (numExperts, topK, hiddenSize, moeInterSize, activationType,
  *        quantizationGroupSize).
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
@@ -491,16 +492,31 @@ QO_API void qo_moe_permute(const int32_t* ids, int32_t T, int32_t topK, int32_t 
     offsets[E] = pos;
 }
 
-/* One token through one expert: SiLU-gated FFN with W4A16 weights.
+/* Gate activation of the gated FFN (MoE plugin page, constructor:
+   activationType), in fp64:
+     0 SiLU       z / (1 + exp(-z))
+     1 GELU, erf form   z/2 * (1 + erf(z / sqrt(2)))
+     2 GELU, tanh form  z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3)))
+     3 ReLU       max(z, 0) */
+QO_API double qo_moe_act(double z, int32_t activation) {
+    switch (activation) {
+        case 1: return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+        case 2: return 0.5 * z * (1.0 + tanh(sqrt(2.0 / M_PI) * (z + 0.044715 * z * z * z)));
+        case 3: return z > 0.0 ? z : 0.0;
+        default: return z / (1.0 + exp(-z));
+    }
+}
+
+/* One token through one expert: gated FFN with W4A16 weights.
      g = x . Wg, u = x . Wu   (fp64 sums over H, ascending)
-     h = fp16( silu(g) * u ),  silu(z) = z / (1 + exp(-z))
+     h = fp16( act(g) * u )   (act: qo_moe_act)
      o = h . Wd               (fp64 sum over I, ascending)
    Wg, Wu natural int4 [H][I/2], scales [H/G][I]; Wd natural [I][H/2],
    scales [I/G][H]. */
 static void qo_expert_ffn(const uint16_t* x, const uint8_t* Wg, const uint8_t* Wu,
                           const uint8_t* Wd, const uint16_t* Sg, const uint16_t* Su,
                           const uint16_t* Sd, double* o, double* hbuf, int32_t H, int32_t I,
-                          int32_t G) {
+                          int32_t G, int32_t activation) {
 #pragma omp parallel for schedule(static)
     for (int32_t i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
@@ -509,8 +525,7 @@ static void qo_expert_ffn(const uint16_t* x, const uint8_t* Wg, const uint8_t* W
             g += xv * ((double)qo_int4_at(Wg, I, h, i) * qo_f16_to_f64(Sg[(int64_t)(h / G) * I + i]));
             u += xv * ((double)qo_int4_at(Wu, I, h, i) * qo_f16_to_f64(Su[(int64_t)(h / G) * I + i]));
         }
-        const double silu = g / (1.0 + exp(-g));
-        hbuf[i] = qo_f16_to_f64(qo_f64_to_f16(silu * u));
+        hbuf[i] = qo_f16_to_f64(qo_f64_to_f16(qo_moe_act(g, activation) * u));
     }
 #pragma omp parallel for schedule(static)
     for (int32_t n = 0; n < H; ++n) {
@@ -524,14 +539,14 @@ static void qo_expert_ffn(const uint16_t* x, const uint8_t* Wg, const uint8_t* W
 /* Full layer for the listed tokens (tokens == NULL: all T tokens).
    y[t] = fp16( sum_{j < topK} w[t][j] * o[t][j] ), j ascending.
    Weights for expert e start at e * (H*I/2) bytes (gate/up/down) and scales
-   at e * (H/G)*I (gate/up) or e * (I/G)*H (down) elements.  activation 0 is
-   the SiLU-gated FFN, the only one defined here.  Y is [T][H]; only the rows
+   at e * (H/G)*I (gate/up) or e * (I/G)*H (down) elements.  activation
+   selects the gate nonlinearity (qo_moe_act).  Y is [T][H]; only the rows
    of the listed tokens are written.  ids/w receive the routing of all T. */
 QO_API void qo_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* Wg,
                    const uint8_t* Wu, const uint8_t* Wd, const uint16_t* Sg, const uint16_t* Su,
                    const uint16_t* Sd, uint16_t* Y, double* Y64, int32_t* ids, double* w,
                    int32_t T, int32_t H, int32_t I, int32_t E, int32_t topK, int32_t G,
-                   const int32_t* tokens, int32_t ntok) {
+                   int32_t activation, const int32_t* tokens, int32_t ntok) {
     (void)E;
     qo_moe_route(logits, T, E, topK, ids, w);
     const int64_t wbytes = (int64_t)H * I / 2;
@@ -546,7 +561,7 @@ QO_API void qo_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* Wg,
         for (int32_t j = 0; j < topK; ++j) {
             const int32_t e = ids[(int64_t)t * topK + j];
             qo_expert_ffn(X + (int64_t)t * H, Wg + e * wbytes, Wu + e * wbytes, Wd + e * wbytes,
-                          Sg + e * sgn, Su + e * sgn, Sd + e * sdn, o, hb, H, I, G);
+                          Sg + e * sgn, Su + e * sgn, Sd + e * sdn, o, hb, H, I, G, activation);
             const double wj = w[(int64_t)t * topK + j];
             for (int32_t n = 0; n < H; ++n) acc[n] += wj * o[n];
         }

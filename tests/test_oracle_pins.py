@@ -606,15 +606,43 @@ def small_moe(seed):
     return qi.moe_problem(c["T"], c["H"], c["I"], c["E"], c["G"], seed)
 
 
-def test_moe_identical_experts_is_dense_swiglu():
+def act_reference(z, activation):
+    """Gate activations from library routines: SiLU = z * expit(z), GELU = z * Phi(z) with
+    Phi from scipy's erf, the tanh approximation of GELU, ReLU."""
+    if activation == oracle.MOE_GELU_ERF:
+        return 0.5 * z * (1.0 + scipy.special.erf(z / math.sqrt(2.0)))
+    if activation == oracle.MOE_GELU_TANH:
+        return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+    if activation == oracle.MOE_RELU:
+        return np.maximum(z, 0.0)
+    return z * scipy.special.expit(z)
+
+
+def test_moe_activation_values():
+    # textbook values at z = 1: SiLU = 1/(1 + 1/e), GELU = Phi(1) (standard normal CDF),
+    # the tanh form of GELU, ReLU
+    assert abs(oracle.moe_act(1.0, oracle.MOE_SILU) - 0.7310585786300049) < 1e-15
+    assert abs(oracle.moe_act(1.0, oracle.MOE_GELU_ERF) - 0.8413447460685429) < 1e-15
+    assert abs(oracle.moe_act(1.0, oracle.MOE_GELU_TANH) - 0.8411919906082768) < 1e-15
+    assert oracle.moe_act(-1.0, oracle.MOE_RELU) == 0.0 and oracle.moe_act(2.5, oracle.MOE_RELU) == 2.5
+    for a in range(4):
+        assert oracle.moe_act(0.0, a) == 0.0
+    zs = np.concatenate([np.linspace(-12, 12, 601), qi.rng(84).standard_normal(200) * 4])
+    for a in range(4):
+        got = np.array([oracle.moe_act(z, a) for z in zs])
+        assert np.allclose(got, act_reference(zs, a), rtol=1e-13, atol=1e-15), a
+
+
+@pytest.mark.parametrize("activation", [0, 1, 2, 3])
+def test_moe_identical_experts_is_dense_swiglu(activation):
     c = SMALL_MOE
     X, logits, Wg, Wu, Wd, Sg, Su, Sd = small_moe(95)
     for arr in (Wg, Wu, Wd, Sg, Su, Sd):
         arr[1:] = arr[0]
-    Y, ids, w = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"])
+    Y, ids, w = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, c["topK"], c["G"], activation=activation)
     _, g = oracle.w4a16(X, Wg[0], Sg[0], c["G"], want_f64=True)
     _, u = oracle.w4a16(X, Wu[0], Su[0], c["G"], want_f64=True)
-    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float16)
+    h = (act_reference(g, activation) * u).astype(np.float16)
     _, o = oracle.w4a16(h, Wd[0], Sd[0], c["G"], want_f64=True)
     ref = o.astype(np.float16)
     diff = np.abs(Y.astype(np.float64) - ref.astype(np.float64))
