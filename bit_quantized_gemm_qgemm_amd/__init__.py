@@ -26,6 +26,11 @@ HIP_ERROR = 6
 EPI_BIAS = 1
 EPI_GELU = 2
 
+MOE_ACT_SILU = 0
+MOE_ACT_GELU_ERF = 1
+MOE_ACT_GELU_TANH = 2
+MOE_ACT_RELU = 3
+
 FP8_PER_TENSOR = 0
 FP8_PER_ROW = 1
 
@@ -333,7 +338,8 @@ def moe_w4a16_workspace_bytes(T, H, I, E, topK):
 
 def moe_w4a16(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up, s_down, topK, G,
               I=None, activation=0, Y=None, topk_ids=None, topk_w=None, workspace=None):
-    """SiLU-gated INT4 MoE layer.  Returns (Y, topk_ids, topk_w, workspace)."""
+    """Gated INT4 MoE layer, h = fp16(act(g) * u) with act = MOE_ACT_SILU, MOE_ACT_GELU_ERF,
+    MOE_ACT_GELU_TANH or MOE_ACT_RELU.  Returns (Y, topk_ids, topk_w, workspace)."""
     _need(X, torch.float16, "X")
     _need(logits, torch.float16, "logits")
     for name, t in (("w_gate_frag", w_gate_frag), ("w_up_frag", w_up_frag),

@@ -8,7 +8,8 @@
 //               atomics on the result order), and records each pair's slot;
 //   3. gate/up: per expert, a W4A16 MFMA GEMM over that expert's gathered
 //               token rows with both the gate and the up matrix, fused with
-//               h = fp16(silu(g) * u);
+//               h = fp16(act(g) * u) (act: the constructor's activation
+//               type, SiLU by default);
 //   4. down:    per expert, W4A16 MFMA GEMM of h with the down matrix, K
 //               split over workgroups, fp32 partial results per slot;
 //   5. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending,
@@ -174,7 +175,7 @@ template <int G, int MODE>
 __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
     const uint16_t* __restrict__ s0, const uint16_t* __restrict__ s1, Work wk, int T, int H, int I,
-    int E, int topK, int splits) {
+    int E, int topK, int splits, int act) {
     constexpr int NB = MODE == 0 ? 2 : 1;
     __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * XP_SLAB];
     const int L = blockIdx.x;
@@ -209,12 +210,12 @@ __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
             else return (uint32_t)(slot0 + r) * (uint32_t)I;
         };
         switch ((R + 31) / 32) {
-            case 1: expert_pass<G, NB, 1, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
-            case 2: expert_pass<G, NB, 2, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
-            case 3: expert_pass<G, NB, 3, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out); break;
+            case 1: expert_pass<G, NB, 1, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
+            case 2: expert_pass<G, NB, 2, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
+            case 3: expert_pass<G, NB, 3, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
             default:
                 if constexpr (PASS == 128)
-                    expert_pass<G, NB, 4, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out);
+                    expert_pass<G, NB, 4, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act);
                 break;
         }
         __syncthreads();  // the next pass refills both LDS buffers
@@ -263,7 +264,7 @@ template <int G>
 int32_t launch_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* wg, const uint8_t* wu,
                    const uint8_t* wd, const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
                    uint16_t* Y, int32_t* ids, float* w, int T, int H, int I, int E, int topK,
-                   const Work& wk, hipStream_t st) {
+                   int act, const Work& wk, hipStream_t st) {
     const int P = T * topK;
     hipLaunchKernelGGL(moe_route_kernel, dim3((T + 255) / 256), dim3(256), 0, st, logits, ids, w, T,
                        E, topK);
@@ -271,9 +272,9 @@ int32_t launch_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* wg,
                        wk.pairs, wk.slot_of);
     const int splits = down_splits(H, I, E);
     hipLaunchKernelGGL((moe_expert_kernel<G, 0>), dim3(E * (I / 128)), dim3(256), 0, st, X, wg, wu,
-                       sg, su, wk, T, H, I, E, topK, 1);
+                       sg, su, wk, T, H, I, E, topK, 1, act);
     hipLaunchKernelGGL((moe_expert_kernel<G, 1>), dim3(E * (H / 128) * splits), dim3(256), 0, st, X,
-                       wd, wd, sd, sd, wk, T, H, I, E, topK, splits);
+                       wd, wd, sd, sd, wk, T, H, I, E, topK, splits, 0);
     const size_t chunks = (size_t)T * H / 8;
     const size_t want = (chunks + 255) / 256;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
@@ -304,7 +305,6 @@ static int32_t moe_run(const uint16_t* X, const uint16_t* logits, const uint8_t*
     size_t off[6];
     workspace_layout(T, H, I, E, topK, off);
     if (workspace_bytes < off[5]) return QGEMM_WORKSPACE_TOO_SMALL;
-    (void)activation;
     char* base = static_cast<char*>(workspace);
     Work wk;
     wk.offsets = reinterpret_cast<int32_t*>(base + off[0]);
@@ -316,13 +316,13 @@ static int32_t moe_run(const uint16_t* X, const uint16_t* logits, const uint8_t*
     switch (G) {
         case 32:
             return launch_moe<32>(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up,
-                                  s_down, Y, topk_ids, topk_w, T, H, I, E, topK, wk, st);
+                                  s_down, Y, topk_ids, topk_w, T, H, I, E, topK, activation, wk, st);
         case 64:
             return launch_moe<64>(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up,
-                                  s_down, Y, topk_ids, topk_w, T, H, I, E, topK, wk, st);
+                                  s_down, Y, topk_ids, topk_w, T, H, I, E, topK, activation, wk, st);
         default:
             return launch_moe<128>(X, logits, w_gate_frag, w_up_frag, w_down_frag, s_gate, s_up,
-                                   s_down, Y, topk_ids, topk_w, T, H, I, E, topK, wk, st);
+                                   s_down, Y, topk_ids, topk_w, T, H, I, E, topK, activation, wk, st);
     }
 }
 
@@ -336,7 +336,8 @@ static int32_t moe_check(const uint16_t* X, const uint16_t* logits, const uint8_
     if (!X || !logits || !w_gate_frag || !w_up_frag || !w_down_frag || !s_gate || !s_up || !s_down ||
         !Y || !topk_ids || !topk_w)
         return QGEMM_NULL_PTR;
-    if (activation != 0 || E > 64 || H == 0 || I == 0 || H % 128 != 0 || I % 128 != 0 ||
+    if (activation < QGEMM_MOE_ACT_SILU || activation > QGEMM_MOE_ACT_RELU || E > 64 || H == 0 || I == 0 ||
+        H % 128 != 0 || I % 128 != 0 ||
         (G != 32 && G != 64 && G != 128) || (size_t)T * topK > (size_t)1 << 30 ||
         (size_t)T * H >= (size_t)1 << 31 || (size_t)T * topK * I >= (size_t)1 << 31)
         return QGEMM_UNSUPPORTED;

@@ -17,17 +17,30 @@ namespace qg {
 
 constexpr int XP_SLAB = 128 * 128;  // halfs per LDS A buffer: 128 rows of 128 k (32 KB)
 
-// MODE 0 (NB = 2, gate and up): out[slot][n] = fp16(silu(g) * u), fp16.
+// MODE 0 (NB = 2, gate and up): out[slot][n] = fp16(act(g) * u), fp16, act
+// the gate activation (moe_act).
 // MODE 1: out[slot][n] = the fp32 partial sum over the pass's chunk range
 // (the K splits of the MoE down projection and of the mid-M GEMM).
 // slot0 + row indexes the output row; row_off(r) is the element offset of
 // A row r of the pass from abase.  N is the row stride of out, ldS that of
 // the scales (0: one scale per column).
+// Gate activation of the gated expert FFN (QGEMM_MOE_ACT_*): SiLU, GELU
+// (erf form, tanh form) or ReLU, in fp32.
+__device__ __forceinline__ float moe_act(float g, int act) {
+    switch (act) {
+        case QGEMM_MOE_ACT_GELU_ERF: return 0.5f * g * (1.0f + erff(g * 0.70710678f));
+        case QGEMM_MOE_ACT_GELU_TANH:
+            return 0.5f * g * (1.0f + tanhf(0.79788456f * (g + 0.044715f * g * g * g)));
+        case QGEMM_MOE_ACT_RELU: return fmaxf(g, 0.0f);
+        default: return g / (1.0f + expf(-g));
+    }
+}
+
 template <int G, int NB, int NRB, int MODE, int WB, typename RowOff>
 __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowOff row_off, int R,
                                             const uint8_t* const* wf, const uint16_t* const* S,
                                             int N, int ldS, int kchunks, int c0, int c1, int ncol0,
-                                            int slot0, void* out) {
+                                            int slot0, void* out, int act = 0) {
     typedef BChunk<1, G, WB> Chunk;
     // (the wave index from threadIdx.x: its known range lets the compiler
     // tell the copies' LDS targets from the buffer being read)
@@ -183,8 +196,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
                 const size_t o = (size_t)(slot0 + row) * N + col;
                 if constexpr (MODE == 0) {
                     const float g = acc[0][i][j], u = acc[NB - 1][i][j];
-                    const float silu = g / (1.0f + expf(-g));
-                    static_cast<uint16_t*>(out)[o] = f2h(silu * u);
+                    static_cast<uint16_t*>(out)[o] = f2h(moe_act(g, act) * u);
                 } else {
                     static_cast<float*>(out)[o] = acc[0][i][j];
                 }

@@ -298,10 +298,18 @@ QGEMM_API int32_t qgemm_w8a8_epilogue(const int8_t* A, const int8_t* W, const fl
  * Routing: per token, the topK experts with the largest logits (the lower
  * expert index wins ties), in descending order; gate weights = softmax over
  * the selected logits (fp32).
- * Expert FFN (activation 0, SiLU-gated):  g = x Wg_e, u = x Wu_e (W4A16,
- * fp32 accumulation), h = fp16(silu(g) * u), o = h Wd_e (W4A16).
+ * Expert FFN (gated, act chosen by activation):  g = x Wg_e, u = x Wu_e (W4A16,
+ * fp32 accumulation), h = fp16(act(g) * u), o = h Wd_e (W4A16).
  * Combine: Y[t] = fp16( sum_{j < topK} w[t][j] * o[t][j] ), j ascending.
  * ---------------------------------------------------------------------- */
+
+/* Gate activation of the expert FFN, h = fp16(act(g) * u) (the constructor's
+   activationType; the page does not list its values, so these are the
+   library's): */
+#define QGEMM_MOE_ACT_SILU 0      /* g / (1 + exp(-g)) */
+#define QGEMM_MOE_ACT_GELU_ERF 1  /* g/2 * (1 + erf(g / sqrt(2))) */
+#define QGEMM_MOE_ACT_GELU_TANH 2 /* g/2 * (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) */
+#define QGEMM_MOE_ACT_RELU 3      /* max(g, 0) */
 
 /* Workspace bytes moe_w4a16 needs (T tokens, hidden H, intermediate I,
    E experts, topK).  Layout, in this order, each part 256-byte aligned:
@@ -324,9 +332,9 @@ QGEMM_API size_t moe_w4a16_workspace_bytes(int32_t T, int32_t H, int32_t I, int3
    s_gate, s_up: fp16 [E][H/G][I]; s_down: fp16 [E][I/G][H].
    Y: fp16 [T][H] (output); topk_ids: int32 [T][topK] (output);
    topk_w: fp32 [T][topK] (output).
+   activation: one of QGEMM_MOE_ACT_*.
    Supported: H % 128 == 0, I % 128 == 0, G in {32, 64, 128}, 1 <= topK <= E
-   <= 64, activation == 0, T*H < 2^31 and T*topK*I < 2^31.  T == 0 is a
-   successful no-op. */
+   <= 64, T*H < 2^31 and T*topK*I < 2^31.  T == 0 is a successful no-op. */
 QGEMM_API int32_t moe_w4a16(const uint16_t* X, const uint16_t* logits, const uint8_t* w_gate_frag,
                   const uint8_t* w_up_frag, const uint8_t* w_down_frag, const uint16_t* s_gate,
                   const uint16_t* s_up, const uint16_t* s_down, uint16_t* Y, int32_t* topk_ids,

@@ -254,7 +254,7 @@ def test_moe_no_alloc_validation(L):
         return f(*([ptr] * 11), T, H, I, E, topK, G, act, None)
     assert call(T=0) == 0
     assert call(topK=5) == 2
-    assert call(act=1) == 5
+    assert call(act=4) == 5
     assert call(ptr=None) == 1
     assert call(ptr=FAKE + 2) == 3
     limit = 64 << 20
@@ -279,7 +279,7 @@ def test_moe_validation(L):
     assert call(T=0) == 0
     assert call(topK=5) == 2
     assert call(E=0) == 2
-    assert call(act=1) == 5
+    assert call(act=4) == 5 and call(act=-1) == 5
     assert call(E=65, topK=2) == 5
     assert call(H=192, G=64) == 5
     assert call(ws=None) == 1

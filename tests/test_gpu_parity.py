@@ -302,13 +302,14 @@ def test_w8a8_cfg3_sampled(qg):
 
 # ------------------------------------------------------------------ MoE
 
-def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G):
+def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation=0):
     E, H, I2 = Wg.shape
     I = I2 * 2
     pg = torch.cat([prepack(qg, Wg[e], H, I) for e in range(E)])
     pu = torch.cat([prepack(qg, Wu[e], H, I) for e in range(E)])
     pd = torch.cat([prepack(qg, Wd[e], I, H) for e in range(E)])
-    Y, ids, w, ws = qg.moe_w4a16(dev(X), dev(logits), pg, pu, pd, dev(Sg), dev(Su), dev(Sd), topK, G)
+    Y, ids, w, ws = qg.moe_w4a16(dev(X), dev(logits), pg, pu, pd, dev(Sg), dev(Su), dev(Sd), topK, G,
+                                 activation=activation)
     T = X.shape[0]
     P = T * topK
     wsh = host(ws)
@@ -333,6 +334,19 @@ def test_moe_small(qg, T, H, I, E, topK, G):
     assert np.array_equal(off, offr) and np.array_equal(pairs, pairsr)
     assert np.allclose(w, wr, rtol=1e-6, atol=0)
     assert_fp16_close(Y, Yr, "moe small")
+
+
+# each gate activation the MoE plugin page's activationType selects (SiLU, GELU in its erf
+# and tanh forms, ReLU), on a layer with several experts and row passes
+@pytest.mark.parametrize("activation", [1, 2, 3])
+@pytest.mark.parametrize("T,H,I,E,topK,G", [(70, 256, 256, 8, 2, 64), (130, 128, 384, 3, 2, 128)])
+def test_moe_activations(qg, T, H, I, E, topK, G, activation):
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 850 + T + activation)
+    Y, ids, w, off, pairs = moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation)
+    Yr, idr, wr = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation=activation)
+    assert np.array_equal(ids, idr)
+    assert np.allclose(w, wr, rtol=1e-6, atol=0)
+    assert_fp16_close(Y, Yr, f"moe activation {activation}")
 
 
 # degenerate routings: every token sent to experts 2 and 5 (six experts hold no
