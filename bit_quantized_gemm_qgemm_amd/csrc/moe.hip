@@ -170,7 +170,13 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 // The down projection splits K over KS workgroups (fp32 partials, added in
 // split order by the combine) so that it has enough workgroups.
 
-// Workgroup L: expert L % E, then column tile, then K split.
+// Workgroup L: expert L % E, then column tile, then K split.  Workgroups are
+// dealt to the eight XCDs by id, so with eight experts each XCD runs one
+// expert and keeps that expert's gathered A rows in its L2 (every workgroup
+// re-reads them per chunk).  Ordering the ids by expert instead (the experts
+// with the most rows first) measured 328 against 282 us for the layer with
+// 256 tokens, hidden 4096, intermediate 14336, top-2 of 8: A then misses in
+// every XCD's L2.
 template <int G, int MODE>
 __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
