@@ -64,11 +64,78 @@ def parse():
                     help="launch one workload's kernels --launches times (eagerly) and exit; "
                          "for rocprofv3 runs")
     ap.add_argument("--launches", type=int, default=20)
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel duration statistics (markdown) of a rocprofv3 kernel-trace CSV "
+                         "and exit: all dispatches, and each run of at least 40 consecutive dispatches of "
+                         "one kernel (the timed graph replays)")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+",
+                    help="print per-kernel means (markdown) of rocprofv3 --pmc counter CSVs found under "
+                         "the given directories and exit")
     return ap.parse_args()
+
+
+def _kernel_short(name):
+    import re
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def summarize_trace(path):
+    """Markdown statistics of a rocprofv3 kernel-trace CSV (durations in us)."""
+    import csv
+    import statistics as st
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    by, runs = {}, []
+    for r in rows:
+        k = _kernel_short(r["Kernel_Name"])
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        by.setdefault(k, []).append(d)
+        if runs and runs[-1][0] == k:
+            runs[-1][1].append(d)
+            runs[-1][3] = int(r["End_Timestamp"])
+        else:
+            runs.append([k, [d], int(r["Start_Timestamp"]), int(r["End_Timestamp"])])
+    q = lambda v, f: sorted(v)[min(len(v) - 1, int(f * len(v)))]
+    print("| kernel | dispatches | mean us | median us | p10 us | p90 us |")
+    print("|---|---|---|---|---|---|")
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k}` | {len(v)} | {st.mean(v):.3f} | {st.median(v):.3f} | {q(v, 0.1):.3f} | {q(v, 0.9):.3f} |")
+    print()
+    print("Runs of at least 40 consecutive dispatches of one kernel (graph replays of one workload):")
+    print()
+    print("| kernel | dispatches | mean us | median us | p10 us | p90 us | span / dispatch us |")
+    print("|---|---|---|---|---|---|---|")
+    for k, v, t0, t1 in runs:
+        if len(v) >= 40:
+            print(f"| `{k}` | {len(v)} | {st.mean(v):.3f} | {st.median(v):.3f} | {q(v, 0.1):.3f} | "
+                  f"{q(v, 0.9):.3f} | {(t1 - t0) / 1000.0 / len(v):.3f} |")
+
+
+def summarize_pmc(dirs):
+    """Markdown per-kernel means of rocprofv3 --pmc counter CSVs (one row per kernel and run)."""
+    import csv
+    import glob
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            agg = {}
+            for r in csv.DictReader(open(f)):
+                k = _kernel_short(r["Kernel_Name"])
+                agg.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for k, cs in agg.items():
+                vals = ", ".join(f"{c} {sum(v) / len(v):.6g}" for c, v in sorted(cs.items()))
+                print(f"| {os.path.relpath(f, d)} | `{k}` | {len(next(iter(cs.values())))} | {vals} |")
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        print("| file | kernel | dispatches | mean per dispatch |")
+        print("|---|---|---|---|")
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(each operation would shard by columns, heads or experts); use --gpus 1", file=sys.stderr)
