@@ -11,6 +11,8 @@
 // (128 k deep) double-buffered through LDS.  The epilogue runs on the int32
 // accumulators in registers and is the bit-exact fp32 sequence of the header
 // (no contraction; division correctly rounded).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace {
@@ -63,6 +65,20 @@ __device__ __forceinline__ int8_t requant(int32_t acc, float sa, float sw, float
     float v = __builtin_rintf(g * out_mult);
     v = fminf(fmaxf(v, -127.0f), 127.0f);
     return (int8_t)(int32_t)v;
+}
+
+// Runs f with the epilogue flags as a compile-time constant, so the per
+// element code has no branches and the compiler can interleave independent
+// elements (with run-time flags every element's GELU is a basic block of its
+// own, a chain of dependent fp32 operations).
+template <typename F>
+__device__ __forceinline__ void with_flags(uint32_t flags, F&& f) {
+    switch (flags & (QGEMM_EPI_BIAS | QGEMM_EPI_GELU)) {
+        case 0: f(std::integral_constant<uint32_t, 0>{}); break;
+        case QGEMM_EPI_BIAS: f(std::integral_constant<uint32_t, QGEMM_EPI_BIAS>{}); break;
+        case QGEMM_EPI_GELU: f(std::integral_constant<uint32_t, QGEMM_EPI_GELU>{}); break;
+        default: f(std::integral_constant<uint32_t, QGEMM_EPI_BIAS | QGEMM_EPI_GELU>{}); break;
+    }
 }
 
 __global__ __launch_bounds__(256, 2) void w8a8_kernel(
@@ -143,24 +159,27 @@ __global__ __launch_bounds__(256, 2) void w8a8_kernel(
         __syncthreads();
     }
 
+    with_flags(flags, [&](auto fl) {
+        constexpr uint32_t FL = decltype(fl)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int col = n0 + wn * 64 + t * 32 + c32;
-        const float swv = sw[col];
-        const float bv = (flags & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
+        for (int t = 0; t < 2; ++t) {
+            const int col = n0 + wn * 64 + t * 32 + c32;
+            const float swv = sw[col];
+            const float bv = (FL & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 2; ++i) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-                if (row < M) {
-                    const int32_t a = acc[i][t][j];
-                    if (acc_out) acc_out[(size_t)row * N + col] = a;
-                    Y[(size_t)row * N + col] = requant(a, sa[row], swv, bv, out_mult, flags);
+                for (int j = 0; j < 16; ++j) {
+                    const int row = m0 + wm * 64 + i * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+                    if (row < M) {
+                        const int32_t a = acc[i][t][j];
+                        if (acc_out) acc_out[(size_t)row * N + col] = a;
+                        Y[(size_t)row * N + col] = requant(a, sa[row], swv, bv, out_mult, FL);
+                    }
                 }
             }
         }
-    }
+    });
 }
 
 // Large shapes (M >= 256, N % 256 == 0): 256x256 output tiles, eight waves
@@ -312,27 +331,30 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
     constexpr int EPW = 72;  // LDS tile pitch in dwords (256 bytes + 32)
     uint32_t* stile = reinterpret_cast<uint32_t*>(lds);
     const int q = lane & 3;
+    with_flags(flags, [&](auto fl) {
+        constexpr uint32_t FL = decltype(fl)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int col = n0 + wn * 64 + t * 32 + c32;
-        const float swv = sw[col];
-        const float bv = (flags & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
+        for (int t = 0; t < 2; ++t) {
+            const int col = n0 + wn * 64 + t * 32 + c32;
+            const float swv = sw[col];
+            const float bv = (FL & QGEMM_EPI_BIAS) ? h2f(bias[col]) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
-                uint32_t d = 0;
+                for (int g = 0; g < 4; ++g) {
+                    const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                    uint32_t d = 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + r0 + r < M ? m0 + r0 + r : M - 1;  // rows >= M are not stored
-                    const int8_t c = requant(acc[i][t][4 * g + r], sa[row], swv, bv, out_mult, flags);
-                    d |= (uint32_t)(uint8_t)c << (8 * r);
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = m0 + r0 + r < M ? m0 + r0 + r : M - 1;  // rows >= M are not stored
+                        const int8_t c = requant(acc[i][t][4 * g + r], sa[row], swv, bv, out_mult, FL);
+                        d |= (uint32_t)(uint8_t)c << (8 * r);
+                    }
+                    stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = quad_rows_u8(d, lane);
                 }
-                stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = quad_rows_u8(d, lane);
             }
         }
-    }
+    });
     __syncthreads();
     const int tid = threadIdx.x;
 #pragma unroll
