@@ -95,18 +95,21 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
             load_b_chunk_buf<G, WB>(bs[b], rb, rs, boff, soff, ldS);
         }
     };
-    // Software-pipelined k-steps: the LDS reads and the dequant of step s + 1
-    // are interleaved with the MFMAs of step s (one MFMA, then at most one
-    // LDS read and a share of the dequant VALU ops), so the wave keeps the
-    // MFMA unit busy while it prepares the next operands.
-    auto operands = [&](const uint16_t* sa, const Chunk* bs, int s, half8 (&a)[NRB],
-                        half8 (&bf)[NB]) {
+    // Software-pipelined k-steps: the A operands of step s + 1 are read from
+    // LDS at the top of step s, fenced off from the rest of the step, so each
+    // read has a whole step of MFMAs to land (left to itself the scheduler
+    // reuses the A registers and waits on every read right before its MFMA);
+    // the dequant of step s + 1 is interleaved with the MFMAs of step s (one
+    // MFMA, then a share of the dequant VALU ops).
+    auto read_a = [&](const uint16_t* sa, int s, half8 (&a)[NRB]) {
         const int kg = kgroup_of_step(s, h);
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
             const int r = i * 32 + c32;
             a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
         }
+    };
+    auto dequant_b = [&](const Chunk* bs, int s, half8 (&bf)[NB]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) bf[b] = b_frag<1, G, WB>(bs[b], 0, s);
     };
@@ -123,15 +126,19 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     auto compute = [&](const uint16_t* sa, const Chunk* bs, auto next, int cn, int nbuf) {
         constexpr bool NEXT = decltype(next)::value;
         half8 a[NRB], bf[NB];
-        operands(sa, bs, 0, a, bf);
+        read_a(sa, 0, a);
+        dequant_b(bs, 0, bf);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             half8 an[NRB], bn[NB];
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 7) read_a(sa, s + 1, an);
+            __builtin_amdgcn_sched_barrier(0);
             if (NEXT && s < 4) {
 #pragma unroll
                 for (int j = s * 2 * NRB / 4; j < (s + 1) * 2 * NRB / 4; ++j) dma_a_one(cn, nbuf, j);
             }
-            if (s < 7) operands(sa, bs, s + 1, an, bn);
+            if (s < 7) dequant_b(bs, s + 1, bn);
 #pragma unroll
             for (int i = 0; i < NRB; ++i)
 #pragma unroll
@@ -141,7 +148,6 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
                 for (int q = 0; q < NM; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     if (NEXT && q < 2 && s < 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
-                    if (q < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
                     __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
                 }
             }
