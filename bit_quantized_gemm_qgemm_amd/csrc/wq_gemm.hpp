@@ -109,7 +109,13 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     };
     constexpr size_t RED = sizeof(floatx4) * WK * NSW * 64;  // K-partials for the reduction
     constexpr size_t STAGE = sizeof(WaveLds) * WK;
-    __shared__ __attribute__((aligned(16))) char lds_raw[STAGE > RED ? STAGE : RED];
+    // The partials get LDS of their own when both fit in 128 KB (then a wave
+    // writes its partials as soon as its loop ends, with no barrier before;
+    // the 16-wave shapes run one workgroup per CU whatever their LDS size);
+    // otherwise they reuse the staging area once every wave is done with it.
+    constexpr bool OWN_RED = STAGE + RED <= 128 * 1024;
+    constexpr size_t LDS_BYTES = OWN_RED ? STAGE + RED : (STAGE > RED ? STAGE : RED);
+    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
     WaveLds* lds = reinterpret_cast<WaveLds*>(lds_raw);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -238,15 +244,21 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     }
 
     // K partials of the workgroup's strips, added in wave order
-    __syncthreads();
-    floatx4* red = reinterpret_cast<floatx4*>(lds_raw);
+    if constexpr (!OWN_RED) __syncthreads();
+    floatx4* red = reinterpret_cast<floatx4*>(lds_raw + (OWN_RED ? STAGE : 0));
 #pragma unroll
     for (int s = 0; s < NSW; ++s) red[(wave * NSW + s) * 64 + lane] = acc[s];
     __syncthreads();
-    // wave w < NSW finalizes strip w
+    // wave w < NSW finalizes strip w: every partial is read before the first
+    // add (a chain of read, wait, add per partial is WK LDS round trips)
     if (wave < nst) {
-        floatx4 t = red[wave * 64 + lane];
-        for (int w = 1; w < WK; ++w) t += red[(w * NSW + wave) * 64 + lane];
+        floatx4 pw[WK];
+#pragma unroll
+        for (int w = 0; w < WK; ++w) pw[w] = red[(w * NSW + wave) * 64 + lane];
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 t = pw[0];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) t += pw[w];
         const int n = (strip0 + wave) * 16 + cl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
