@@ -118,7 +118,8 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
     WaveLds* lds = reinterpret_cast<WaveLds*>(lds_raw);
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // (the wave index as a scalar: the slice bounds and their branches are uniform)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     WaveLds& L = lds[wave];
     // BAL: the workgroups share the N / 16 strips in contiguous ranges of
     // NSW - 1 or NSW strips (every CU busy when N / 16 is not a multiple of
@@ -207,9 +208,7 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
         }
         if (lane < SPL) *reinterpret_cast<uintx4*>(&L.s[sp_g][sp_r * 8]) = sreg;
         __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < KCW; ++i) {
-            if (i * 128 >= kwl) break;
+        auto chunk = [&](int i) __attribute__((always_inline)) {
             const _Float16* ap = L.a + arow * LDA + i * 128 + q * 8;
             half8 a[4];
 #pragma unroll
@@ -238,6 +237,19 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
                     for (int j = 0; j < 4; ++j)
                         acc[s][j] = __builtin_fmaf(tmp[j] - cc[j], sv, acc[s][j]);
                 }
+            }
+        };
+        // A whole slice (every wave but one past a ragged K) runs as one block
+        // of straight-line code, so the LDS reads of a chunk can go out before
+        // the wait for its weights
+        if (kwl >= KW) {
+#pragma unroll
+            for (int i = 0; i < KCW; ++i) chunk(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KCW; ++i) {
+                if (i * 128 >= kwl) break;
+                chunk(i);
             }
         }
         __builtin_amdgcn_wave_barrier();
