@@ -815,23 +815,31 @@ __global__ __launch_bounds__(256, 2) void wq_mid_kernel(const uint16_t* __restri
 }
 
 // Y[i] = fp16(sum over splits s = 0 .. S-1 of part[s][i]), s ascending; eight
-// outputs per lane per step, grid-stride.
+// outputs per lane per step, grid-stride.  S is a compile-time constant, so
+// every split's loads go out before the first add (a loop over a run-time S
+// waited for each split's loads in turn: S memory round trips per output).
+template <int S>
 __global__ __launch_bounds__(256) void wq_splitk_reduce_kernel(const float* __restrict__ part,
                                                                uint16_t* __restrict__ Y, size_t n8,
-                                                               size_t stride_s, int splits) {
+                                                               size_t stride_s) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n8; c += stride) {
         const float* p = part + c * 8;
-        floatx4 lo = *reinterpret_cast<const floatx4*>(p);
-        floatx4 hi = *reinterpret_cast<const floatx4*>(p + 4);
-        for (int s = 1; s < splits; ++s) {
-            lo += *reinterpret_cast<const floatx4*>(p + s * stride_s);
-            hi += *reinterpret_cast<const floatx4*>(p + s * stride_s + 4);
+        floatx4 lo[S], hi[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            lo[s] = *reinterpret_cast<const floatx4*>(p + s * stride_s);
+            hi[s] = *reinterpret_cast<const floatx4*>(p + s * stride_s + 4);
         }
-        const uintx4 o = {(uint32_t)f2h(lo[0]) | ((uint32_t)f2h(lo[1]) << 16),
-                          (uint32_t)f2h(lo[2]) | ((uint32_t)f2h(lo[3]) << 16),
-                          (uint32_t)f2h(hi[0]) | ((uint32_t)f2h(hi[1]) << 16),
-                          (uint32_t)f2h(hi[2]) | ((uint32_t)f2h(hi[3]) << 16)};
+#pragma unroll
+        for (int s = 1; s < S; ++s) {
+            lo[0] += lo[s];
+            hi[0] += hi[s];
+        }
+        const uintx4 o = {(uint32_t)f2h(lo[0][0]) | ((uint32_t)f2h(lo[0][1]) << 16),
+                          (uint32_t)f2h(lo[0][2]) | ((uint32_t)f2h(lo[0][3]) << 16),
+                          (uint32_t)f2h(hi[0][0]) | ((uint32_t)f2h(hi[0][1]) << 16),
+                          (uint32_t)f2h(hi[0][2]) | ((uint32_t)f2h(hi[0][3]) << 16)};
         *reinterpret_cast<uintx4*>(Y + c * 8) = o;
     }
 }
@@ -894,8 +902,16 @@ void launch_wq_mid(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int 
     hipLaunchKernelGGL((wq_mid_kernel<WB, G>), dim3((N / 128) * splits), dim3(256), 0, st, A, wf, S, ldS,
                        part, M, N, K, splits);
     const size_t n8 = (size_t)M * N / 8, want = (n8 + 255) / 256;
-    hipLaunchKernelGGL(wq_splitk_reduce_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
-                       part, Y, n8, (size_t)M * N, splits);
+    const dim3 grid((int)(want < 4096 ? want : 4096));
+    const size_t ss = (size_t)M * N;
+    switch (splits) {  // mid_splits keeps 1 <= splits <= 16
+#define QG_REDUCE(S_) \
+    case S_: hipLaunchKernelGGL(wq_splitk_reduce_kernel<S_>, grid, dim3(256), 0, st, part, Y, n8, ss); break;
+        QG_REDUCE(1) QG_REDUCE(2) QG_REDUCE(3) QG_REDUCE(4) QG_REDUCE(5) QG_REDUCE(6) QG_REDUCE(7) QG_REDUCE(8)
+        QG_REDUCE(9) QG_REDUCE(10) QG_REDUCE(11) QG_REDUCE(12) QG_REDUCE(13) QG_REDUCE(14) QG_REDUCE(15)
+        default: hipLaunchKernelGGL(wq_splitk_reduce_kernel<16>, grid, dim3(256), 0, st, part, Y, n8, ss); break;
+#undef QG_REDUCE
+    }
 }
 
 // Shapes the mid-M path takes (given enough workspace).
