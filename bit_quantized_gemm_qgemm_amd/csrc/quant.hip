@@ -34,6 +34,36 @@ __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float mul
     return out;
 }
 
+// mult = 127 / a and scale = a / 127, correctly rounded, for a = max |x| of
+// fp16 values (so a is 0, +inf or a positive finite fp16 value): v_rcp_f32
+// with one fused correction of the quotient gives the correctly rounded
+// result for every positive finite fp16 a (checked on gfx950 over all 31743
+// of them against the IEEE divisions), in four operations instead of the
+// division's ten; a = 0 gives 0 and 0, a = +inf gives 0 and +inf, as the
+// divisions (and the zero-row rule) do.
+__device__ __forceinline__ void int8_scales(float a, float& mult, float& scale) {
+    const float r = __builtin_amdgcn_rcpf(a);
+    const float q = 127.0f * r;
+    const float m = __builtin_fmaf(__builtin_fmaf(-a, q, 127.0f), r, q);
+    constexpr float r127 = 1.0f / 127.0f;
+    const float s0 = a * r127;
+    const float sc = __builtin_fmaf(__builtin_fmaf(-s0, 127.0f, a), r127, s0);
+    const bool fin = a < __builtin_inff();
+    mult = a > 0.0f ? (fin ? m : 0.0f) : 0.0f;
+    scale = a > 0.0f ? (fin ? sc : a) : 0.0f;
+}
+
+// max |x| of eight fp16 values: sign bits cleared, fp16 maxima of the pairs
+// (exact, and the order of fp16 values is that of their fp32 conversions),
+// then the two halves in fp32; NaNs lose every comparison as in fmaxf.
+__device__ __forceinline__ float absmax8_h(uintx4 v) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a0 = __builtin_bit_cast(h2, v.x & 0x7fff7fffu), a1 = __builtin_bit_cast(h2, v.y & 0x7fff7fffu);
+    const h2 a2 = __builtin_bit_cast(h2, v.z & 0x7fff7fffu), a3 = __builtin_bit_cast(h2, v.w & 0x7fff7fffu);
+    const h2 m = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3));
+    return fmaxf(0.0f, fmaxf((float)m[0], (float)m[1]));
+}
+
 // Rows held in registers: each of LPR lanes holds CPL chunks of 8 values.
 template <int LPR, int CPL>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ X,
@@ -59,12 +89,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
-        amax = fmaxf(amax, qg::absmax8(v[i]));
+        amax = fmaxf(amax, absmax8_h(v[i]));
     }
     amax = qg::group_max<LPR>(amax);
     if (!live) return;
-    const float mult = amax > 0.0f ? 127.0f / amax : 0.0f;
-    if (lane == 0) S[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    float mult, scale;
+    int8_scales(amax, mult, scale);
+    if (lane == 0) S[row] = scale;
     int8_t* q = Q + (size_t)row * cols;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -88,10 +119,11 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
     const int nchunk = cols / 8;
     const uintx4* x = reinterpret_cast<const uintx4*>(X + (size_t)row * cols);
     float amax = 0.0f;
-    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, qg::absmax8(x[c]));
+    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, absmax8_h(x[c]));
     amax = qg::group_max<64>(amax);
-    const float mult = amax > 0.0f ? 127.0f / amax : 0.0f;
-    if (lane == 0) S[row] = amax > 0.0f ? amax / 127.0f : 0.0f;
+    float mult, scale;
+    int8_scales(amax, mult, scale);
+    if (lane == 0) S[row] = scale;
     uintx2* q = reinterpret_cast<uintx2*>(Q + (size_t)row * cols);
     for (int c = lane; c < nchunk; c += 64) {
         const uintx4 v = x[c];
