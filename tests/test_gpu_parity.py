@@ -245,6 +245,28 @@ def test_quant_shapes_and_edge_rows(qg, rows, cols):
     assert np.array_equal(bits(Xd), bits(oracle.dequant_sym_int8(Qr, Sr)))
 
 
+@pytest.mark.parametrize("cols", [16, 4096])
+def test_quant_every_fp16_amax(qg, cols):
+    """One row per positive finite fp16 value a, max |x| = a (at a varying
+    position and sign, the rest of the row below it): scales and codes equal
+    the oracle's, i.e. 127 / amax and amax / 127 are the correctly rounded
+    quotients for every amax the quantizer can meet."""
+    a = np.arange(1, 0x7c00, dtype=np.uint16).view(np.float16)
+    if cols == 4096:
+        a = a[::16]                            # long rows: every 16th value
+    rows = a.size
+    r = np.random.default_rng(77)
+    X = (r.uniform(-1, 1, (rows, cols)) * 0.999).astype(np.float32)
+    X *= a.astype(np.float32)[:, None]
+    X = X.astype(np.float16)
+    pos = r.integers(0, cols, rows)
+    X[np.arange(rows), pos] = np.where(r.random(rows) < 0.5, a, -a)
+    Q, S = qg.quant_sym_int8(dev(X))
+    Qr, Sr = oracle.quant_sym_int8(X)
+    assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32))
+    assert np.array_equal(host(Q), Qr)
+
+
 # ------------------------------------------------------------------ W8A8
 
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
