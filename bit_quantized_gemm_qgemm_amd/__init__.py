@@ -101,6 +101,7 @@ def _declare(L):
         "moe_w4a16": (_I32, [_P] * 11 + [_I32] * 7 + [_P, _SZ, _P]),
         "moe_w4a16_no_alloc": (_I32, [_P] * 11 + [_I32] * 7 + [_P]),
         "qgemm_stream_read": (_I32, [_P, _SZ, _P, _P]),
+        "qgemm_stream_copy": (_I32, [_P, _SZ, _P, _SZ, _P]),
         "quant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "dequant_fp8_e4m3": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P]),
         "qgemm_fp8": (_I32, [_P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _P]),
@@ -117,7 +118,7 @@ EXPORTS = ("qgemm_abi_version", "qgemm_status_str", "qgemm_w4a16_packed_bytes",
            "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
            "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
            "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-           "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read")
+           "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read", "qgemm_stream_copy")
 
 
 def _ptr(t):
@@ -490,3 +491,15 @@ def qgemm_stream_read(buf, sink):
     _need(sink, torch.int32, "sink")
     _check("qgemm_stream_read", lib().qgemm_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
                                                          _ptr(sink), _stream()))
+
+
+def qgemm_stream_copy(src, dst):
+    """Read every byte of the CUDA tensor ``src`` and write every byte of ``dst`` (one half or
+    twice its size, multiples of 16 bytes) in the traffic shapes of the int8 quantizer and
+    dequantizer (dst words: XOR of word pairs when halving, each word pair then the pair plus
+    one when doubling).  For bandwidth reference runs."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous CUDA tensor")
+    _check("qgemm_stream_copy", lib().qgemm_stream_copy(_ptr(src), src.numel() * src.element_size(), _ptr(dst),
+                                                         dst.numel() * dst.element_size(), _stream()))

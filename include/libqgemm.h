@@ -460,6 +460,21 @@ QGEMM_API int32_t mha_int8(const int8_t* Q, const int8_t* K, const int8_t* V, co
  * ---------------------------------------------------------------------- */
 QGEMM_API int32_t qgemm_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid (not a step of the method): reads src_bytes of device
+ * memory at src and writes dst_bytes at dst, in the traffic shapes of the
+ * int8 quantizer (dst_bytes == src_bytes / 2: 16 bytes read, 8 written per
+ * lane step) and dequantizer (dst_bytes == 2 * src_bytes: 8 read, 16
+ * written).  dst receives words derived from src: with s the 32-bit words of
+ * src, dst word i = s[2i] ^ s[2i+1] (halving), or dst words 4j .. 4j+3 =
+ * s[2j], s[2j+1], s[2j] + 1, s[2j+1] + 1 (doubling).  Its rate is the
+ * achievable read+write bandwidth for those shapes.  Both sizes
+ * multiples of 16, both pointers 16-byte aligned, the buffers disjoint; any
+ * other size ratio is QGEMM_BAD_SHAPE; both sizes 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+QGEMM_API int32_t qgemm_stream_copy(const void* src, size_t src_bytes, void* dst, size_t dst_bytes,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
         "quant_fp8_e4m3", "dequant_fp8_e4m3", "qgemm_fp8", "qgemm_w8a16_packed_bytes",
         "qgemm_w8a16_prepack", "qgemm_w8a16_workspace_bytes", "qgemm_w8a16", "mha_int8",
         "qgemm_w4a16_tactics", "qgemm_w4a16_tactic_workspace_bytes", "qgemm_w4a16_tactic",
-        "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read"])
+        "qgemm_w4a16_autotune", "moe_w4a16_no_alloc", "qgemm_stream_read", "qgemm_stream_copy"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -270,6 +270,16 @@ def test_stream_read_validation(L):
     assert f(None, 16, FAKE, None) == 1
     assert f(FAKE, 24, FAKE, None) == 2
     assert f(FAKE + 8, 32, FAKE, None) == 3
+
+
+def test_stream_copy_validation(L):
+    f = L.qgemm_stream_copy
+    assert f(None, 0, None, 0, None) == 0
+    assert f(None, 32, FAKE, 16, None) == 1
+    assert f(FAKE, 32, FAKE, 32, None) == 2       # only the 2:1 and 1:2 shapes
+    assert f(FAKE, 48, FAKE, 24, None) == 2       # sizes multiples of 16
+    assert f(FAKE + 8, 32, FAKE, 16, None) == 3
+    assert f(FAKE, 16, FAKE + 8, 32, None) == 3
 
 
 def test_moe_validation(L):
