@@ -278,7 +278,8 @@ def main():
                                           "kernel": "stream_read_kernel, 16-B non-temporal loads",
                                           "working_set": f"{b1} B per launch, 16 rotated buffers"},
                 "frac_of_measured_ceiling": round(achieved / stream_23, 4),
-                "read_1GiB_GB/s": round(stream_1g, 1)}
+                "read_1GiB_GB/s": round(stream_1g, 1),
+                "rocprof_trace": read_trace()}
     for M in DEC_MS:
         per_m[M]["frac_of_measured_ceiling"] = round(per_m[M]["GB/s"] / stream_23, 4)
 
@@ -287,7 +288,7 @@ def main():
         rows = bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log)
         # every HBM-bound row beside the streaming-read ceiling measured above
         for v in rows.values():
-            if "GB/s" in v:
+            if "hbm_frac" in v:
                 v["frac_of_read_ceiling"] = round(v["GB/s"] / stream_23, 4)
 
     cpu = None
@@ -429,18 +430,30 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch of the M=1 decode kernel from the committed counter
-    summary, if it was taken on the current kernel sources; otherwise None."""
+def read_profile_record():
+    """The committed counter and trace record of the M=1 decode kernel, if it
+    was taken on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
         if d.get("source_sha256_16") != decode_source_hash():
             return None
-        return d.get("bytes_per_launch")
+        return d
     except (OSError, ValueError):
         return None
+
+
+def read_traffic():
+    """HBM bytes per launch of the M=1 decode kernel (counters), or None."""
+    d = read_profile_record()
+    return None if d is None else d.get("bytes_per_launch")
+
+
+def read_trace():
+    """rocprofv3 kernel-trace figures of the M=1 decode kernel, or None."""
+    d = read_profile_record()
+    return None if d is None else d.get("trace")
 
 
 def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
