@@ -241,8 +241,9 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
         };
         // A whole slice (every wave but one past a ragged K) runs as one block
         // of straight-line code, so the LDS reads of a chunk can go out before
-        // the wait for its weights
-        if (kwl >= KW) {
+        // the wait for its weights (int4 only: with the int8 weights' twice as
+        // many registers the hoisted reads make the 16-wave shapes spill)
+        if (P == 1 && kwl >= KW) {
 #pragma unroll
             for (int i = 0; i < KCW; ++i) chunk(i);
         } else {
@@ -261,16 +262,22 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
 #pragma unroll
     for (int s = 0; s < NSW; ++s) red[(wave * NSW + s) * 64 + lane] = acc[s];
     __syncthreads();
-    // wave w < NSW finalizes strip w: every partial is read before the first
-    // add (a chain of read, wait, add per partial is WK LDS round trips)
+    // wave w < NSW finalizes strip w: the partials are read RB at a time
+    // before they are added (a chain of read, wait, add per partial is WK LDS
+    // round trips); int8 weights leave fewer free registers, so four at a
+    // time there
     if (wave < nst) {
-        floatx4 pw[WK];
+        constexpr int RB = P == 1 ? WK : (WK < 4 ? WK : 4);
+        floatx4 t;
 #pragma unroll
-        for (int w = 0; w < WK; ++w) pw[w] = red[(w * NSW + wave) * 64 + lane];
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 t = pw[0];
+        for (int w0 = 0; w0 < WK; w0 += RB) {
+            floatx4 pw[RB];
 #pragma unroll
-        for (int w = 1; w < WK; ++w) t += pw[w];
+            for (int w = 0; w < RB; ++w) pw[w] = red[((w0 + w) * NSW + wave) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int w = 0; w < RB; ++w) t = (w0 + w == 0) ? pw[0] : t + pw[w];
+        }
         const int n = (strip0 + wave) * 16 + cl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
