@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+# QGEMM_LIB: another build of the same sources (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("QGEMM_LIB") or os.path.join(_HERE, "libqgemm.so")
 
 OK = 0
 NULL_PTR = 1

@@ -39,9 +39,20 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (each -fsanitize
+# behind -Xarch_host: the device code is built as usual), against the shared
+# sanitizer runtime of the toolchain's clang, which the loading process must
+# preload; for checking runs of the host tests only.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-shared-libasan"]
+SAN_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-shared-libasan"]
+
+
+def _compile(src, verbose, objdir=OBJ, extra=()):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + CFLAGS + list(extra) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,17 +64,20 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, host_sanitize: bool = False) -> str:
+    objdir = OBJ + ("_san" if host_sanitize else "")
+    extra = SAN_FLAGS if host_sanitize else []
+    os.makedirs(objdir, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, objdir, extra), srcs))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + (SAN_LINK if host_sanitize else [])
+    cmd += ["-o", out + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

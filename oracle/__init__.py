@@ -18,7 +18,9 @@ import numpy as np
 from . import build as _build
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# QGEMM_ORACLE_LIB: another build of the same source (the sanitizer build of
+# tests/test_oracle_sanitized.py)
+_LIB_PATH = os.environ.get("QGEMM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 EPI_BIAS = 1

@@ -12,18 +12,22 @@ SRC = os.path.join(HERE, "qgemm_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """sanitize: AddressSanitizer and UndefinedBehaviorSanitizer instrumentation
+    (-O1, every finding fatal), for a checking run of the pin tests."""
+    opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=all"] if sanitize else ["-O2"])
     cmd = [
-        "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+        "gcc", *opt, "-std=c11", "-fPIC", "-shared", "-fopenmp",
         "-ffp-contract=off", "-fno-fast-math", "-fvisibility=hidden",
         "-Wall", "-Wextra", "-Wno-unused-parameter",
-        SRC, "-o", LIB + ".tmp", "-lm",
+        SRC, "-o", out + ".tmp", "-lm",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
