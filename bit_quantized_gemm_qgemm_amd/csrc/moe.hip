@@ -176,7 +176,8 @@ __global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __rest
 // re-reads them per chunk).  Ordering the ids by expert instead (the experts
 // with the most rows first) measured 328 against 282 us for the layer with
 // 256 tokens, hidden 4096, intermediate 14336, top-2 of 8: A then misses in
-// every XCD's L2.
+// every XCD's L2.  The gate/up pass with eight experts pairs them instead
+// (below), two experts per XCD.
 template <int G, int MODE>
 __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
@@ -185,10 +186,34 @@ __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
     constexpr int NB = MODE == 0 ? 2 : 1;
     __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * XP_SLAB];
     const int L = blockIdx.x;
-    const int e = L % E, rest = L / E;
     const int N = MODE == 0 ? I : H, K = MODE == 0 ? H : I;
     const int ntiles = N / 128;
-    const int ct = rest % ntiles, ks = rest / ntiles;
+    int e = L % E, ct = (L / E) % ntiles;
+    const int ks = (L / E) / ntiles;
+    if (MODE == 0 && E == 8 && ntiles % 2 == 0) {
+        // Balanced pairs: rank the experts by 32-row MFMA blocks (most first,
+        // lower index on ties) and give XCDs 2p and 2p + 1 the experts ranked
+        // p and 7 - p, one half of the column tiles of each, the heavier
+        // expert's tiles first in dispatch order.  So every XCD carries half
+        // of a heavy and half of a light expert instead of one whole expert
+        // (the layer's time is that of its slowest XCD) and still reads the A
+        // rows of only two experts.  Every (expert, tile) is still one
+        // workgroup; results do not depend on the mapping.
+        const int x = L % 8, i = L / 8, half = ntiles / 2;
+        const int p = x >> 1, want = i < half ? p : 7 - p;
+        int nb[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nb[q] = (wk.offsets[q + 1] - wk.offsets[q] + 31) >> 5;
+        e = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            int rank = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rank += (nb[u] > nb[q]) || (nb[u] == nb[q] && u < q);
+            if (rank == want) e = q;
+        }
+        ct = (x & 1) * half + (i < half ? i : i - half);
+    }
     const int off = wk.offsets[e], me = wk.offsets[e + 1] - off;
     if (me == 0) return;
     const int kchunks = K / 128, per = kchunks / splits;
