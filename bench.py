@@ -523,14 +523,13 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
     # cfg3b: KV cache [32, 2048, 128] quant + dequant, 16 rotated sets
     R = 16
     kvs = [to_dev(qi.kv_problem(32, 2048, 128, 103 + 1000 * r)) for r in range(R)]
-    Q = torch.empty((32, 2048, 128), dtype=torch.int8, device=dev)
-    Sk = torch.empty(32 * 2048, dtype=torch.float32, device=dev)
     Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
     Qs = [torch.empty((32, 2048, 128), dtype=torch.int8, device=dev) for _ in range(R)]
     Ss = [torch.empty(32 * 2048, dtype=torch.float32, device=dev) for _ in range(R)]
     for r in range(R):
         qg.quant_sym_int8(kvs[r], Q=Qs[r], scales=Ss[r])
-    gk = graph_of([(lambda r=r: qg.quant_sym_int8(kvs[r], Q=Q, scales=Sk)) for r in range(R)])
+    # codes and scales written over the rotated sets too, like the ceiling's copies
+    gk = graph_of([(lambda r=r: qg.quant_sym_int8(kvs[r], Q=Qs[r], scales=Ss[r])) for r in range(R)])
     tk = time_graph(gk, R, reps=10)
     gd = graph_of([(lambda r=r: qg.dequant_sym_int8(Qs[r], Ss[r], X=Xo)) for r in range(R)])
     td = time_graph(gd, R, reps=10)
@@ -618,14 +617,12 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
     del Xs, qw8s, qa8s, sa8s, Y8s
     R = 16
     kvs = [to_dev(qi.kv_problem(32, 2048, 128, 105 + 1000 * r)) for r in range(R)]
-    Q8 = torch.empty((32, 2048, 128), dtype=torch.uint8, device=dev)
-    Sk = torch.empty(32 * 2048, dtype=torch.float32, device=dev)
     Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
     Qs = [torch.empty((32, 2048, 128), dtype=torch.uint8, device=dev) for _ in range(R)]
     Ss = [torch.empty(32 * 2048, dtype=torch.float32, device=dev) for _ in range(R)]
     for r in range(R):
         qg.quant_fp8_e4m3(kvs[r], Q=Qs[r], scales=Ss[r])
-    gk = graph_of([(lambda r=r: qg.quant_fp8_e4m3(kvs[r], Q=Q8, scales=Sk)) for r in range(R)])
+    gk = graph_of([(lambda r=r: qg.quant_fp8_e4m3(kvs[r], Q=Qs[r], scales=Ss[r])) for r in range(R)])
     tk = time_graph(gk, R, reps=10)
     gd = graph_of([(lambda r=r: qg.dequant_fp8_e4m3(Qs[r], Ss[r], X=Xo)) for r in range(R)])
     td = time_graph(gd, R, reps=10)
@@ -637,7 +634,7 @@ def bench_rows(qg, qi, np, torch, to_dev, graph_of, time_graph, log):
                                           "hbm_frac": round(kb / td / 1e9 / HBM_PEAK_GBS, 4),
                                           "rw_ceiling": rw["dequant"], "frac_of_rw_ceiling": round(tcd / td, 4)}
     log(f"[bench] fp8 kv {rows['fp8_kv_quant_32x2048x128']} {rows['fp8_kv_dequant_32x2048x128']}")
-    del kvs, Qs, Ss, Q8, Sk, Xo
+    del kvs, Qs, Ss, Xo
 
     # W8A16 (int8 weights, fp16 activations, G = 128): decode M = 1, 8 on the
     # K = 4096, N = 11008 weights (16 rotated sets of 45 MB) and prefill

@@ -140,18 +140,19 @@ __device__ __forceinline__ float dpp_max(float v) {
                                                                           CTRL, 0xf, 0xf, false)));
 }
 
-// Maximum over each aligned group of LPR lanes (16 or 64), delivered to every
-// lane of the group, by register moves only: within a 16-lane row lane ^ 1,
-// lane ^ 2 (quad permutations), then the half-row and row mirrors; a whole
-// wave then combines its four row maxima read from lanes 0, 16, 32 and 48.
-// The maximum is exact, so the order does not matter.
+// Maximum over each aligned group of LPR lanes (4, 8, 16 or 64), delivered
+// to every lane of the group, by register moves only: within a 16-lane row
+// lane ^ 1, lane ^ 2 (quad permutations), then the half-row mirror (8 lanes)
+// and the row mirror (16); a whole wave then combines its four row maxima
+// read from lanes 0, 16, 32 and 48.  The maximum is exact, so the order does
+// not matter.
 template <int LPR>
 __device__ __forceinline__ float group_max(float v) {
-    static_assert(LPR == 16 || LPR == 64, "rows of 16 lanes or whole waves");
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 64, "groups of 4, 8 or 16 lanes or whole waves");
     v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
     v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-    v = dpp_max<0x141>(v);  // row_half_mirror
-    v = dpp_max<0x140>(v);  // row_mirror
+    if constexpr (LPR >= 8) v = dpp_max<0x141>(v);  // row_half_mirror
+    if constexpr (LPR >= 16) v = dpp_max<0x140>(v);  // row_mirror
     if constexpr (LPR == 64) {
         const int b = __builtin_bit_cast(int, v);
         const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
@@ -164,15 +165,14 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 __device__ __forceinline__ float absmax8(uintx4 v) {
-    // |x| of eight fp16 values: clear the sign bits, compare as fp16
-    float m = 0.0f;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m = fmaxf(m, h2f(w[i] & 0x7fffu));
-        m = fmaxf(m, h2f((w[i] >> 16) & 0x7fffu));
-    }
-    return m;
+    // max |x| of eight fp16 values: sign bits cleared, fp16 maxima of the
+    // pairs (exact, and the order of fp16 values is that of their fp32
+    // conversions), then the two halves in fp32
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a0 = __builtin_bit_cast(h2, v.x & 0x7fff7fffu), a1 = __builtin_bit_cast(h2, v.y & 0x7fff7fffu);
+    const h2 a2 = __builtin_bit_cast(h2, v.z & 0x7fff7fffu), a3 = __builtin_bit_cast(h2, v.w & 0x7fff7fffu);
+    const h2 m = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3));
+    return fmaxf(0.0f, fmaxf((float)m[0], (float)m[1]));
 }
 
 // ---- accumulator tiles to row-major pieces (GEMM epilogues)

@@ -28,14 +28,25 @@ using namespace qg;
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 
-// four fp16 values (two words) times mult, clamped, -> four E4M3 codes in one word
+// four fp16 values (two words) times mult -> four E4M3 codes in one word.
+// fl32(x * mult) as fma(x, mult, +0) (v_fma_mix_f32 reads the fp16 operand in
+// place): the same single rounding, except that a zero product comes out +0
+// where x * mult is -0 for negative x; since mult > 0 the code's sign is that
+// of x, so the sign bits of the four inputs are ORed into the codes (one byte
+// permute gathers them), which restores -0 as 0x80.  With |x| <= amax and
+// mult = fl32(448 / amax) the product is at most 448 (1 + 2^-24) in
+// magnitude, which the round-to-nearest-even conversion maps to +-448 (the
+// next value up would be 480), so no clamp to [-448, 448] is needed for
+// finite input.
 __device__ __forceinline__ uint32_t fp8x4(uint32_t h01, uint32_t h23, float mult) {
     float x[4] = {h2f(h01 & 0xffffu), h2f(h01 >> 16), h2f(h23 & 0xffffu), h2f(h23 >> 16)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(x[i] * mult, -448.0f), 448.0f);
+    for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(x[i], mult, 0.0f);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);  // bytes 0, 1
     w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);       // bytes 2, 3
-    return (uint32_t)w;
+    // bytes 1 and 3 of each input word hold the fp16 sign bits, in bit 7
+    const uint32_t sgn = __builtin_amdgcn_perm(h23, h01, 0x07050301u) & 0x80808080u;
+    return (uint32_t)w | sgn;
 }
 
 __device__ __forceinline__ uintx2 fp8x8(uintx4 v, float mult) {
@@ -46,7 +57,8 @@ __device__ __forceinline__ uintx2 fp8x8(uintx4 v, float mult) {
 
 // Rows held in registers: each of LPR lanes holds CPL chunks of 8 values;
 // the row's amax by DPP moves, codes written from the same registers.
-template <int LPR, int CPL>
+// FULL: cols == LPR * CPL * 8, so every chunk is in the row.
+template <int LPR, int CPL, bool FULL>
 __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __restrict__ X,
                                                              uint8_t* __restrict__ Q,
                                                              float* __restrict__ S, int rows,
@@ -62,12 +74,12 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        v[i] = ldg_nt(reinterpret_cast<const uintx4*>(x) + (c < nchunk ? c : 0));
+        v[i] = ldg_nt(reinterpret_cast<const uintx4*>(x) + (FULL || c < nchunk ? c : 0));
     }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
+        if (!FULL && lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
         amax = fmaxf(amax, absmax8(v[i]));
     }
     amax = group_max<LPR>(amax);
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        if (c < nchunk) q[c] = fp8x8(v[i], mult);
+        if (FULL || c < nchunk) q[c] = fp8x8(v[i], mult);
     }
 }
 
@@ -358,16 +370,18 @@ extern "C" int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, 
     if (!qgh::aligned(X, 16) || !qgh::aligned(Q, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
     hipStream_t st = (hipStream_t)stream;
     if (per_row) {
-        if (cols <= 128) {  // one 16-byte chunk per lane (the KV rows of 128 values)
-            hipLaunchKernelGGL((fp8_quant_rows_kernel<16, 1>), dim3((rows + 15) / 16), dim3(256), 0, st, X, Q,
-                               scales, rows, cols);
-        } else if (cols <= 256) {
-            hipLaunchKernelGGL((fp8_quant_rows_kernel<16, 2>), dim3((rows + 15) / 16), dim3(256), 0, st, X, Q,
-                               scales, rows, cols);
-        } else {
-            hipLaunchKernelGGL((fp8_quant_rows_kernel<64, 8>), dim3((rows + 3) / 4), dim3(256), 0, st, X, Q,
-                               scales, rows, cols);
-        }
+        // 8 lanes of two chunks per row up to 128 values (the KV rows), as
+        // for the int8 quantizer; variants without bounds selects for rows
+        // that fill the lane group exactly
+        auto launch = [&](auto kern, int lpr) {
+            const int rpb = 256 / lpr;
+            hipLaunchKernelGGL(kern, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, X, Q, scales, rows, cols);
+        };
+        if (cols == 128) launch(fp8_quant_rows_kernel<8, 2, true>, 8);
+        else if (cols < 128) launch(fp8_quant_rows_kernel<8, 2, false>, 8);
+        else if (cols <= 256) launch(fp8_quant_rows_kernel<16, 2, false>, 16);
+        else if (cols == 4096) launch(fp8_quant_rows_kernel<64, 8, true>, 64);
+        else launch(fp8_quant_rows_kernel<64, 8, false>, 64);
         return qgh::launch_status();
     }
     const size_t nchunk = (size_t)rows * cols / 8;

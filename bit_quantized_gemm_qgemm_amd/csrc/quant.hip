@@ -21,14 +21,20 @@ using qg::uintx2;
 using qg::uintx4;
 
 __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float mult) {
-    // four fp16 values (two words) -> four int8 codes in one word
+    // four fp16 values (two words) -> four int8 codes in one word.
+    // fl32(x * mult) as fma(x, mult, +0): one rounding of the same product,
+    // and the fp16 operand is read in place (v_fma_mix_f32, no conversion
+    // instruction); the two can differ only in the sign of a zero product,
+    // which gives code 0 either way.  No clamp to [-127, 127] is needed: with
+    // |x| <= amax and mult = fl32(127 / amax) <= (127 / amax)(1 + 2^-24), the
+    // product is at most 127 (1 + 2^-24) in magnitude and rounds to at most
+    // 127 (inputs are finite).
     const float x[4] = {qg::h2f(h01 & 0xffffu), qg::h2f(h01 >> 16), qg::h2f(h23 & 0xffffu),
                         qg::h2f(h23 >> 16)};
     uint32_t out = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float v = __builtin_rintf(x[i] * mult);
-        v = fminf(fmaxf(v, -127.0f), 127.0f);
+        const float v = __builtin_rintf(__builtin_fmaf(x[i], mult, 0.0f));
         out |= ((uint32_t)(int32_t)v & 0xffu) << (8 * i);
     }
     return out;
@@ -53,19 +59,9 @@ __device__ __forceinline__ void int8_scales(float a, float& mult, float& scale) 
     scale = a > 0.0f ? (fin ? sc : a) : 0.0f;
 }
 
-// max |x| of eight fp16 values: sign bits cleared, fp16 maxima of the pairs
-// (exact, and the order of fp16 values is that of their fp32 conversions),
-// then the two halves in fp32; NaNs lose every comparison as in fmaxf.
-__device__ __forceinline__ float absmax8_h(uintx4 v) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 a0 = __builtin_bit_cast(h2, v.x & 0x7fff7fffu), a1 = __builtin_bit_cast(h2, v.y & 0x7fff7fffu);
-    const h2 a2 = __builtin_bit_cast(h2, v.z & 0x7fff7fffu), a3 = __builtin_bit_cast(h2, v.w & 0x7fff7fffu);
-    const h2 m = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1), __builtin_elementwise_max(a2, a3));
-    return fmaxf(0.0f, fmaxf((float)m[0], (float)m[1]));
-}
-
-// Rows held in registers: each of LPR lanes holds CPL chunks of 8 values.
-template <int LPR, int CPL>
+// Rows held in registers: each of LPR lanes holds CPL chunks of 8 values;
+// FULL: cols == LPR * CPL * 8, so every chunk is in the row.
+template <int LPR, int CPL, bool FULL>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ X,
                                                          int8_t* __restrict__ Q,
                                                          float* __restrict__ S, int rows,
@@ -83,13 +79,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        v[i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + (c < nchunk ? c : 0));
+        v[i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + (FULL || c < nchunk ? c : 0));
     }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        if (lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
-        amax = fmaxf(amax, absmax8_h(v[i]));
+        if (!FULL && lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
+        amax = fmaxf(amax, qg::absmax8(v[i]));
     }
     amax = qg::group_max<LPR>(amax);
     if (!live) return;
@@ -100,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        if (c < nchunk) {
+        if (FULL || c < nchunk) {
             const uint32_t lo = quant4(v[i].x, v[i].y, mult);
             const uint32_t hi = quant4(v[i].z, v[i].w, mult);
             reinterpret_cast<uintx2*>(q)[c] = uintx2{lo, hi};
@@ -119,7 +115,7 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
     const int nchunk = cols / 8;
     const uintx4* x = reinterpret_cast<const uintx4*>(X + (size_t)row * cols);
     float amax = 0.0f;
-    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, absmax8_h(x[c]));
+    for (int c = lane; c < nchunk; c += 64) amax = fmaxf(amax, qg::absmax8(x[c]));
     amax = qg::group_max<64>(amax);
     float mult, scale;
     int8_scales(amax, mult, scale);
@@ -167,21 +163,25 @@ extern "C" int32_t quant_sym_int8(const uint16_t* X, int8_t* Q, float* scales, i
     if (!qgh::aligned(X, 16) || !qgh::aligned(Q, 8) || !qgh::aligned(scales, 4))
         return QGEMM_MISALIGNED;
     hipStream_t st = (hipStream_t)stream;
-    if (cols <= 16 * 8) {
-        // one 16-byte chunk per lane: rows of up to 128 values (the KV cache's
-        // head_dim) with no second, padding load per lane (7.34 -> 6.83 us for
-        // 65,536 rows of 128)
-        const int rpb = 256 / 16;
-        hipLaunchKernelGGL((quant_rows_kernel<16, 1>), dim3((rows + rpb - 1) / rpb), dim3(256), 0,
-                           st, X, Q, scales, (int)rows, (int)cols);
+    // rows of up to 128 values (the KV cache's head_dim): 8 lanes of two
+    // 16-byte chunks per row (7.34 us for 65,536 rows of 128 with 16 lanes of
+    // two chunks, 6.83 with 16 lanes of one, 6.46 with 8 of two, 6.90 with 4
+    // of four; 6.12 once quant4 took the fma-mix product and dropped the clamp)
+    auto launch = [&](auto kern, int lpr) {
+        const int rpb = 256 / lpr;
+        hipLaunchKernelGGL(kern, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, X, Q, scales, (int)rows,
+                           (int)cols);
+    };
+    if (cols == 8 * 8 * 2) {
+        launch(quant_rows_kernel<8, 2, true>, 8);
+    } else if (cols < 8 * 8 * 2) {
+        launch(quant_rows_kernel<8, 2, false>, 8);
     } else if (cols <= 16 * 8 * 2) {
-        const int rpb = 256 / 16;
-        hipLaunchKernelGGL((quant_rows_kernel<16, 2>), dim3((rows + rpb - 1) / rpb), dim3(256), 0,
-                           st, X, Q, scales, (int)rows, (int)cols);
+        launch(quant_rows_kernel<16, 2, false>, 16);
+    } else if (cols == 64 * 8 * 8) {
+        launch(quant_rows_kernel<64, 8, true>, 64);
     } else if (cols <= 64 * 8 * 8) {
-        const int rpb = 256 / 64;
-        hipLaunchKernelGGL((quant_rows_kernel<64, 8>), dim3((rows + rpb - 1) / rpb), dim3(256), 0,
-                           st, X, Q, scales, (int)rows, (int)cols);
+        launch(quant_rows_kernel<64, 8, false>, 64);
     } else {
         hipLaunchKernelGGL(quant_rows_long_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, X, Q,
                            scales, (int)rows, (int)cols);

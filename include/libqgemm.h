@@ -242,7 +242,8 @@ QGEMM_API int32_t qgemm_w8a16(const uint16_t* A, const uint8_t* w_frag, const ui
  * [N][K]) and KV-cache rows (one row per (head, token)).
  * ---------------------------------------------------------------------- */
 
-/* X: fp16 [rows][cols] (input); Q: int8 [rows][cols] (output);
+/* X: fp16 [rows][cols] (input, finite values; a row holding an infinity or
+   NaN gets unspecified codes); Q: int8 [rows][cols] (output);
    scales: fp32 [rows] (output, the dequantization scale amax/127).
    cols must be a multiple of 8 and at most 65536; rows == 0 is a no-op.
    Codes and scales are bit-exact functions of X. */

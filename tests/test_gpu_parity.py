@@ -227,7 +227,7 @@ def test_quant_kv_cfg3(qg):
     assert np.array_equal(bits(Xd), bits(oracle.dequant_sym_int8(Qr, Sr)))
 
 
-@pytest.mark.parametrize("cols", [8, 128, 256, 264, 4096, 4104, 65536])
+@pytest.mark.parametrize("cols", [8, 120, 128, 200, 256, 264, 4096, 4104, 65536])
 @pytest.mark.parametrize("rows", [1, 3, 17, 100])
 def test_quant_shapes_and_edge_rows(qg, rows, cols):
     X = qi.activations(rows, cols, 600 + rows + cols)
@@ -436,7 +436,7 @@ FP8_FINITE = np.array([c for c in range(256) if c & 0x7f != 0x7f], np.uint8)
 
 
 @pytest.mark.parametrize("per_row", [True, False])
-@pytest.mark.parametrize("cols", [8, 128, 256, 264, 4096])
+@pytest.mark.parametrize("cols", [8, 120, 128, 200, 256, 264, 4096])
 @pytest.mark.parametrize("rows", [1, 3, 17, 100])
 def test_fp8_quant_shapes_and_edge_rows(qg, rows, cols, per_row):
     X = qi.activations(rows, cols, 900 + rows + cols)
@@ -453,6 +453,27 @@ def test_fp8_quant_shapes_and_edge_rows(qg, rows, cols, per_row):
     assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32))
     Xd = host(qg.dequant_fp8_e4m3(Q, S, per_row=per_row))
     assert np.array_equal(bits(Xd), bits(oracle.dequant_fp8(Qr, Sr, per_row=per_row)))
+
+
+@pytest.mark.parametrize("cols", [16, 128])
+def test_fp8_quant_every_fp16_amax(qg, cols):
+    """Per-row E4M3 quantization with one row per positive finite fp16 value a
+    as max |x| (varying position and sign): codes and scales equal the
+    oracle's.  For 3144 of these a, a * fl32(448 / a) rounds to 448 (1 + 2^-24)
+    in fp32, so the rows' maxima check that such a product encodes as +-448."""
+    a = np.arange(1, 0x7c00, dtype=np.uint16).view(np.float16)
+    rows = a.size
+    r = np.random.default_rng(78)
+    X = (r.uniform(-1, 1, (rows, cols)) * 0.999).astype(np.float32)
+    X *= a.astype(np.float32)[:, None]
+    X = X.astype(np.float16)
+    pos = r.integers(0, cols, rows)
+    X[np.arange(rows), pos] = np.where(r.random(rows) < 0.5, a, -a)
+    Q, S = qg.quant_fp8_e4m3(dev(X), per_row=True)
+    Qr, Sr = oracle.quant_fp8(X, per_row=True)
+    assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32))
+    assert np.array_equal(host(Q), Qr)
+    assert np.all(np.isin(host(Q)[np.arange(rows), pos], [0x7e, 0xfe]))
 
 
 def test_fp8_dequant_every_code(qg):
