@@ -200,7 +200,9 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, float out_mult, uint32_t flags,
     int8_t* __restrict__ Y, int32_t* __restrict__ acc_out, int M, int N, int K) {
     constexpr int SL = LB * 128;  // bytes per operand buffer
-    __shared__ __attribute__((aligned(1024))) int8_t lds[4 * SL];  // A0, A1, W0, W1
+    // A0, A1, W0, W1, then the activation scales of the tile's rows
+    __shared__ __attribute__((aligned(1024))) int8_t lds[4 * SL + LB * 4];
+    float* const s_sa = reinterpret_cast<float*>(lds + 4 * SL);
     // (the wave index from threadIdx.x: its known range lets the compiler
     // tell the copies' LDS targets from the buffer being read)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -289,9 +291,15 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
         }
     };
 
+    // the tile's 256 activation scales (rows >= M repeat row M - 1) go to LDS
+    // with the first chunk, so the epilogue reads each lane's four
+    // consecutive rows with one LDS read instead of four clamped gathers
+    const int srow = m0 + (int)(threadIdx.x & (LB - 1));
+    const float sa_row = sa[srow < M ? srow : M - 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma_one(0, 0, i);
     wait_vmcnt<0>();
+    if (threadIdx.x < LB) s_sa[threadIdx.x] = sa_row;
     __syncthreads();
     // one trip per chunk: DMA of chunk c + 1 into the idle buffers, MFMAs on
     // chunk c, then wait for this wave's DMA and a bare barrier (buffer
@@ -343,11 +351,11 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
+                    const floatx4 sa4 = *reinterpret_cast<const floatx4*>(&s_sa[r0]);
                     uint32_t d = 0;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = m0 + r0 + r < M ? m0 + r0 + r : M - 1;  // rows >= M are not stored
-                        const int8_t c = requant(acc[i][t][4 * g + r], sa[row], swv, bv, out_mult, FL);
+                        const int8_t c = requant(acc[i][t][4 * g + r], sa4[r], swv, bv, out_mult, FL);
                         d |= (uint32_t)(uint8_t)c << (8 * r);
                     }
                     stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = quad_rows_u8(d, lane);
