@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restr
             o[2 * i] = h0 | (h1 << 16);
             o[2 * i + 1] = h2 | (h3 << 16);
         }
-        reinterpret_cast<uintx4*>(X)[c] = uintx4{o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(uintx4{o[0], o[1], o[2], o[3]}, reinterpret_cast<uintx4*>(X) + c);
     }
 }
 
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void fp8_gemm_kernel(const uint8_t* __restr
         const uint32_t* src = &stile[row * EPW + piece * 4];
         uint16_t* dst = Y + (size_t)(m0 + row) * N + colg;
         if (vec && colg + 8 <= N) {
-            *reinterpret_cast<uintx4*>(dst) = *reinterpret_cast<const uintx4*>(src);
+            __builtin_nontemporal_store(*reinterpret_cast<const uintx4*>(src), reinterpret_cast<uintx4*>(dst));
         } else {
             for (int e = 0; e < 8 && colg + e < N; ++e) dst[e] = (uint16_t)(src[e >> 1] >> (16 * (e & 1)));
         }

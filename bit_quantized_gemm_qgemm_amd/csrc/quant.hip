@@ -148,7 +148,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
                 o[2 * i + j] = a | (b << 16);
             }
         }
-        reinterpret_cast<uintx4*>(X)[c] = uintx4{o[0], o[1], o[2], o[3]};
+        // non-temporal: 6.62 -> 6.24 us for the KV cache (plain stores were
+        // faster for the quantizers' 8-byte code stores)
+        __builtin_nontemporal_store(uintx4{o[0], o[1], o[2], o[3]}, reinterpret_cast<uintx4*>(X) + c);
     }
 }
 

@@ -368,9 +368,9 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int idx = tid + 512 * p, row = idx >> 4, piece = idx & 15;
-        if (m0 + row < M)
-            *reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 16) =
-                *reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]);
+        if (m0 + row < M)  // non-temporal: Y is not read again here
+            __builtin_nontemporal_store(*reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]),
+                                        reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 16));
     }
 }
 
