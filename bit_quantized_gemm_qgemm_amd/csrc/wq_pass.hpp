@@ -212,8 +212,8 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
         uint16_t* h = static_cast<uint16_t*>(out) + (size_t)slot0 * N + (ncol0 - wave * 32);
         for (int idx = tid; idx < R * 16; idx += 256) {
             const int row = idx >> 4, piece = idx & 15;
-            *reinterpret_cast<uintx4*>(h + (size_t)row * N + piece * 8) =
-                *reinterpret_cast<const uintx4*>(&sA[row * TP + piece * 8]);
+            __builtin_nontemporal_store(*reinterpret_cast<const uintx4*>(&sA[row * TP + piece * 8]),
+                                        reinterpret_cast<uintx4*>(h + (size_t)row * N + piece * 8));
         }
     } else {
         const int col = ncol0 + c32;
@@ -222,7 +222,8 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int row = i * 32 + acc_row(j, lane);
-                if (row < R) static_cast<float*>(out)[(size_t)(slot0 + row) * N + col] = acc[0][i][j];
+                if (row < R)
+                    __builtin_nontemporal_store(acc[0][i][j], static_cast<float*>(out) + (size_t)(slot0 + row) * N + col);
             }
     }
 }
