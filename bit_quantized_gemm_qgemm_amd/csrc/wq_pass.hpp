@@ -192,36 +192,43 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     }
     if (c < c1) compute(sA, b0, std::false_type{}, 0, 1);
 
+    // The epilogue's lane-dependent addresses are formed from a copy of the
+    // lane index that the compiler cannot trace back (an empty asm): hoisted
+    // above the k loop, those addresses stayed live through it and were
+    // spilled to scratch memory (16 registers per lane, 14.7 MB of scratch
+    // writes per gate/up launch at the MoE layer's shape).
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int we = __builtin_amdgcn_readfirstlane(wave);
     if constexpr (MODE == 0) {
         // h = fp16(act(g) * u) of the pass's R rows x 128 columns goes through
         // an LDS tile (pitch 136 halfs) so that each row is stored as 16 whole
-        // 16-byte pieces (two-byte stores per lane left half-written lines
-        // behind: 1.47x the bytes of h in writes).  The barrier also drains
-        // every copy still in flight into the buffers the tile reuses.
+        // 16-byte pieces.  The barrier also drains every copy still in flight
+        // into the buffers the tile reuses.
         constexpr int TP = 136;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int row = i * 32 + acc_row(j, lane);
+                const int row = i * 32 + acc_row(j, lane_e);
                 const float g = acc[0][i][j], u = acc[NB - 1][i][j];
-                if (row < R) sA[row * TP + wave * 32 + c32] = f2h(moe_act(g, act) * u);
+                if (row < R) sA[row * TP + we * 32 + (lane_e & 31)] = f2h(moe_act(g, act) * u);
             }
         __syncthreads();
         uint16_t* h = static_cast<uint16_t*>(out) + (size_t)slot0 * N + (ncol0 - wave * 32);
-        for (int idx = tid; idx < R * 16; idx += 256) {
+        for (int idx = we * 64 + lane_e; idx < R * 16; idx += 256) {
             const int row = idx >> 4, piece = idx & 15;
             __builtin_nontemporal_store(*reinterpret_cast<const uintx4*>(&sA[row * TP + piece * 8]),
                                         reinterpret_cast<uintx4*>(h + (size_t)row * N + piece * 8));
         }
     } else {
-        const int col = ncol0 + c32;
+        const int col = __builtin_amdgcn_readfirstlane(ncol0 - wave * 32) + we * 32 + (lane_e & 31);
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int row = i * 32 + acc_row(j, lane);
+                const int row = i * 32 + acc_row(j, lane_e);
                 if (row < R)
                     __builtin_nontemporal_store(acc[0][i][j], static_cast<float*>(out) + (size_t)(slot0 + row) * N + col);
             }
