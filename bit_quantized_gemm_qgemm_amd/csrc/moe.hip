@@ -1,18 +1,18 @@
 // INT4 mixture-of-experts layer (Int4 Moe Plugin page, constructor:
 // numExperts, topK, hiddenSize, moeInterSize, activationType,
-// quantizationGroupSize; one output).  Five stream-ordered launches:
-//   1. route:   per token, top-k experts by logit (lower index wins ties) and
-//               softmax over the selected logits (fp32);
-//   2. permute: one workgroup groups the (token, j) pairs by expert, keeping
+// quantizationGroupSize; one output).  Four stream-ordered launches:
+//   1. route + permute, one workgroup: per token, top-k experts by logit
+//               (lower index wins ties) and softmax over the selected logits
+//               (fp32); then the (token, j) pairs grouped by expert, keeping
 //               ascending pair order inside an expert (wave ballots, no
-//               atomics on the result order), and records each pair's slot;
-//   3. gate/up: per expert, a W4A16 MFMA GEMM over that expert's gathered
+//               atomics on the result order), and each pair's slot recorded;
+//   2. gate/up: per expert, a W4A16 MFMA GEMM over that expert's gathered
 //               token rows with both the gate and the up matrix, fused with
 //               h = fp16(act(g) * u) (act: the constructor's activation
 //               type, SiLU by default);
-//   4. down:    per expert, W4A16 MFMA GEMM of h with the down matrix, K
+//   3. down:    per expert, W4A16 MFMA GEMM of h with the down matrix, K
 //               split over workgroups, fp32 partial results per slot;
-//   5. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending,
+//   4. combine: y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending,
 //               o being the K-split partials added in split order.
 // Every reduction has a fixed order, so the layer is deterministic.
 #include <atomic>
@@ -61,56 +61,59 @@ __host__ __device__ inline void workspace_layout(int T, int H, int I, int E, int
     off[5] = x;
 }
 
-// ------------------------------------------------------------------ route
+// ------------------------------------------------------------------ route + permute
 
-__global__ __launch_bounds__(256) void moe_route_kernel(const uint16_t* __restrict__ logits,
-                                                        int32_t* __restrict__ ids,
-                                                        float* __restrict__ w, int T, int E,
-                                                        int topK) {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= T) return;
-    const uint16_t* l = logits + (size_t)t * E;
-    uint64_t taken = 0;
-    float vals[64];
-    int sel[64];
-    for (int j = 0; j < topK; ++j) {
-        int best = -1;
-        float bv = 0.0f;
-        for (int e = 0; e < E; ++e) {
-            if ((taken >> e) & 1ull) continue;
-            const float v = h2f(l[e]);
-            if (best < 0 || v > bv) {
-                best = e;
-                bv = v;
+// One workgroup.  Route: thread t takes tokens t, t + 1024, ...; per token
+// the top-k experts by logit (lower index wins ties) and the softmax over the
+// selected logits (fp32), the selected logits kept in the output weights
+// until the sum is known (no per-thread arrays, so no scratch memory).
+// Permute: groups the (token, j) pairs by expert, keeping ascending pair
+// order inside an expert (wave ballots, no atomics on the result order), and
+// records each pair's slot.  One launch for both: the routing of a few
+// hundred tokens is far below a launch's cost.
+__global__ __launch_bounds__(1024) void moe_route_permute_kernel(const uint16_t* __restrict__ logits,
+                                                                 int32_t* __restrict__ ids,
+                                                                 float* __restrict__ w, int T, int E,
+                                                                 int topK, int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ pairs,
+                                                                 int32_t* __restrict__ slot_of) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int t = tid; t < T; t += 1024) {
+        const uint16_t* l = logits + (size_t)t * E;
+        int32_t* it = ids + (size_t)t * topK;
+        float* wt = w + (size_t)t * topK;
+        uint64_t taken = 0;
+        for (int j = 0; j < topK; ++j) {
+            int best = -1;
+            float bv = 0.0f;
+            for (int e = 0; e < E; ++e) {
+                if ((taken >> e) & 1ull) continue;
+                const float v = h2f(l[e]);
+                if (best < 0 || v > bv) {
+                    best = e;
+                    bv = v;
+                }
             }
+            taken |= 1ull << best;
+            it[j] = best;
+            wt[j] = bv;
         }
-        taken |= 1ull << best;
-        sel[j] = best;
-        vals[j] = bv;
+        const float lmax = wt[0];
+        float sum = 0.0f;
+        for (int j = 0; j < topK; ++j) {
+            const float v = expf(wt[j] - lmax);
+            wt[j] = v;
+            sum += v;
+        }
+        for (int j = 0; j < topK; ++j) wt[j] = wt[j] / sum;
     }
-    const float lmax = vals[0];
-    float sum = 0.0f;
-    for (int j = 0; j < topK; ++j) {
-        vals[j] = expf(vals[j] - lmax);
-        sum += vals[j];
-    }
-    for (int j = 0; j < topK; ++j) {
-        ids[(size_t)t * topK + j] = sel[j];
-        w[(size_t)t * topK + j] = vals[j] / sum;
-    }
-}
+    __syncthreads();  // the expert ids written above are read by every thread below
 
-// ------------------------------------------------------------------ permute
-
-__global__ __launch_bounds__(1024) void moe_permute_kernel(const int32_t* __restrict__ ids, int P,
-                                                           int E, int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ pairs,
-                                                           int32_t* __restrict__ slot_of) {
     __shared__ int cnt[64];
     __shared__ int base[64];
     __shared__ int wave_cnt[16][64];
     __shared__ int wave_off[16][64];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int P = T * topK;
     if (tid < 64) cnt[tid] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[ids[p]], 1);
@@ -296,11 +299,8 @@ int32_t launch_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* wg,
                    const uint8_t* wd, const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
                    uint16_t* Y, int32_t* ids, float* w, int T, int H, int I, int E, int topK,
                    int act, const Work& wk, hipStream_t st) {
-    const int P = T * topK;
-    hipLaunchKernelGGL(moe_route_kernel, dim3((T + 255) / 256), dim3(256), 0, st, logits, ids, w, T,
-                       E, topK);
-    hipLaunchKernelGGL(moe_permute_kernel, dim3(1), dim3(1024), 0, st, ids, P, E, wk.offsets,
-                       wk.pairs, wk.slot_of);
+    hipLaunchKernelGGL(moe_route_permute_kernel, dim3(1), dim3(1024), 0, st, logits, ids, w, T, E, topK,
+                       wk.offsets, wk.pairs, wk.slot_of);
     const int splits = down_splits(H, I, E);
     hipLaunchKernelGGL((moe_expert_kernel<G, 0>), dim3(E * (I / 128)), dim3(256), 0, st, X, wg, wu,
                        sg, su, wk, T, H, I, E, topK, 1, act);
