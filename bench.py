@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile", default=None,
                     choices=["decode1", "decode4", "decode8", "prefill", "w8a8", "quant_act",
-                             "kvquant", "kvdequant", "moe", "mha", "copy", "stream"],
+                             "kvquant", "kvdequant", "moe", "mha", "copy", "stream",
+                             "w8a16_decode1", "w8a16_decode8", "fp8", "fp8kv"],
                     help="launch one workload's kernels --launches times (eagerly) and exit; "
                          "for rocprofv3 runs")
     ap.add_argument("--launches", type=int, default=20)
@@ -405,6 +406,43 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
         torch.cuda.synchronize()
         for _ in range(launches):
             qg.mha_int8(Qd, Kd, Vd, alpha, pv, om, bias=bd, O=O)
+    elif name.startswith("w8a16_decode"):
+        M = int(name[len("w8a16_decode"):])
+        sets = []
+        for r in range(ROT):
+            _, W, S = qi.w8a16_problem(1, DEC_K, DEC_N, DEC_G, 107 + 1000 * r)
+            sets.append((qg.qgemm_w8a16_prepack(to_dev(W), DEC_K, DEC_N), to_dev(S)))
+        A = to_dev(qi.activations(M, DEC_K, 1070 + M))
+        Y = torch.empty((M, DEC_N), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            Wf, S = sets[i % ROT]
+            qg.qgemm_w8a16(A, Wf, S, DEC_G, Y=Y)
+    elif name == "fp8":
+        # per-tensor activation quant and the FP8 GEMM, 8 rotated sets as in the timed rows
+        M = N = K = 4096
+        RQ = 8
+        X, Wf16, _, _ = qi.w8a8_problem(M, N, K, 106)
+        Xs = [to_dev(X)] + [to_dev(qi.activations(M, K, 1106 + r)) for r in range(1, RQ)]
+        qws = [qg.quant_fp8_e4m3(to_dev(Wf16), per_row=False)]
+        qws += [qg.quant_fp8_e4m3(to_dev(qi.activations(N, K, 1206 + r)), per_row=False) for r in range(1, RQ)]
+        qas = [qg.quant_fp8_e4m3(x, per_row=False) for x in Xs]
+        Ys = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(RQ)]
+        torch.cuda.synchronize()
+        for i in range(launches):
+            r = i % RQ
+            qg.quant_fp8_e4m3(Xs[r], per_row=False, Q=qas[r][0], scales=qas[r][1])
+            qg.qgemm_fp8(qas[r][0], qws[r][0], qas[r][1], qws[r][1], Y=Ys[r])
+    elif name == "fp8kv":
+        # per-row E4M3 KV cache quant then dequant, 16 rotated sets
+        kvs = [to_dev(qi.kv_problem(32, 2048, 128, 105 + 1000 * r)) for r in range(16)]
+        qs = [qg.quant_fp8_e4m3(kv) for kv in kvs]
+        Xo = torch.empty((32, 2048, 128), dtype=torch.float16, device=dev)
+        torch.cuda.synchronize()
+        for i in range(launches):
+            r = i % 16
+            qg.quant_fp8_e4m3(kvs[r], Q=qs[r][0], scales=qs[r][1])
+            qg.dequant_fp8_e4m3(qs[r][0], qs[r][1], X=Xo)
     elif name == "copy":
         # an elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB),
         # to calibrate the HBM byte counters
