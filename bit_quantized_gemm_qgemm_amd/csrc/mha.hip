@@ -80,8 +80,20 @@ __global__ __launch_bounds__(64 * NW, 2) void mha_int8_kernel(
     __shared__ __attribute__((aligned(16))) MhaLds<D> L;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int hh = lane >> 5, c32 = lane & 31;
-    const int b = blockIdx.z, h = blockIdx.y;
-    const int q = blockIdx.x * QB + wave * 32 + c32;  // this lane's query
+    // Workgroups are dealt to the eight XCDs round-robin by linear id.  When
+    // the (batch, head) pairs come in multiples of eight, id L runs query tile
+    // (L / 8) % tiles of pair 8 ((L / 8) / tiles) + L % 8, so all tiles of one
+    // head share an XCD and read its K and V through one L2.
+    const int ntile = gridDim.x, nbh = gridDim.y * gridDim.z;
+    int tile = blockIdx.x, b = blockIdx.z, h = blockIdx.y;
+    if (nbh % 8 == 0) {
+        const int L = blockIdx.x + ntile * (blockIdx.y + gridDim.y * blockIdx.z);
+        const int slot = L >> 3, bh = (slot / ntile) * 8 + (L & 7);
+        tile = slot % ntile;
+        b = bh / H;
+        h = bh % H;
+    }
+    const int q = tile * QB + wave * 32 + c32;  // this lane's query
     const int qc = q < Lq ? q : Lq - 1;
     // element offsets fit 32 bits (B * max(Lq, Lk) * H * D < 2^31 is checked at launch)
     const uint32_t rs = (uint32_t)H * D;  // bytes between consecutive tokens

@@ -78,9 +78,12 @@ def run_case(qg, B, Lq, Lk, H, D, seed, use_bias=True, inputs=None, heads=None):
     return nd
 
 
+# batch x heads a multiple of 8 (the last two cases) takes the XCD-grouped workgroup
+# order: every query tile of a head on one XCD
 @pytest.mark.parametrize("B,Lq,Lk,H,D", [(1, 1, 1, 1, 64), (2, 37, 53, 3, 64), (1, 128, 128, 2, 128),
                                          (1, 77, 197, 12, 64), (2, 129, 31, 2, 128), (1, 300, 1000, 2, 128),
-                                         (3, 5, 65, 4, 64), (1, 256, 33, 1, 128)])
+                                         (3, 5, 65, 4, 64), (1, 256, 33, 1, 128), (2, 300, 100, 4, 64),
+                                         (1, 130, 64, 8, 128)])
 def test_mha_shapes(qg, B, Lq, Lk, H, D):
     run_case(qg, B, Lq, Lk, H, D, 800 + Lq + Lk)
 
