@@ -22,22 +22,25 @@ using qg::uintx4;
 
 __device__ __forceinline__ uint32_t quant4(uint32_t h01, uint32_t h23, float mult) {
     // four fp16 values (two words) -> four int8 codes in one word.
-    // fl32(x * mult) as fma(x, mult, +0): one rounding of the same product,
+    // m = fl32(x * mult) as fma(x, mult, +0): one rounding of the same product,
     // and the fp16 operand is read in place (v_fma_mix_f32, no conversion
     // instruction); the two can differ only in the sign of a zero product,
     // which gives code 0 either way.  No clamp to [-127, 127] is needed: with
     // |x| <= amax and mult = fl32(127 / amax) <= (127 / amax)(1 + 2^-24), the
     // product is at most 127 (1 + 2^-24) in magnitude and rounds to at most
-    // 127 (inputs are finite).
+    // 127 (inputs are finite).  Rounding to an integer: m + 1.5 * 2^23 lies in
+    // [2^23, 2^24), where the fp32 spacing is 1, so the addition rounds m to
+    // nearest, ties to even, and the sum's low mantissa bits hold that integer
+    // (0x4B400000 + rne(m)); its low byte is the two's-complement code.  Four
+    // low bytes are gathered by byte permutes.
     const float x[4] = {qg::h2f(h01 & 0xffffu), qg::h2f(h01 >> 16), qg::h2f(h23 & 0xffffu),
                         qg::h2f(h23 >> 16)};
-    uint32_t out = 0;
+    uint32_t f[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float v = __builtin_rintf(__builtin_fmaf(x[i], mult, 0.0f));
-        out |= ((uint32_t)(int32_t)v & 0xffu) << (8 * i);
-    }
-    return out;
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(uint32_t, __builtin_fmaf(x[i], mult, 0.0f) + 12582912.0f);
+    const uint32_t lo = __builtin_amdgcn_perm(f[1], f[0], 0x0c0c0400u);  // bytes: f0.b0, f1.b0, 0, 0
+    const uint32_t hi = __builtin_amdgcn_perm(f[3], f[2], 0x04000c0cu);  // bytes: 0, 0, f2.b0, f3.b0
+    return lo | hi;
 }
 
 // mult = 127 / a and scale = a / 127, correctly rounded, for a = max |x| of

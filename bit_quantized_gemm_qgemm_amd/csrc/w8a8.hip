@@ -55,16 +55,25 @@ __device__ __forceinline__ float gelu28(float y) {
     return (0.5f * y) * (1.0f + e);
 }
 
-__device__ __forceinline__ int8_t requant(int32_t acc, float sa, float sw, float bias,
-                                          float out_mult, uint32_t flags) {
+// The code in the low byte of the result.  clamp(rne(v), -127, 127) equals
+// rne(clamp(v, -127, 127)) (the bounds are integers), and adding 1.5 * 2^23
+// to a value of magnitude at most 127 lands in [2^23, 2^24), where the fp32
+// spacing is 1: the addition rounds to nearest, ties to even, and leaves
+// 0x4B400000 + rne(v) in the bits, whose low byte is the two's-complement code.
+__device__ __forceinline__ uint32_t requant_bits(int32_t acc, float sa, float sw, float bias,
+                                                 float out_mult, uint32_t flags) {
     float t = (float)acc;
     t = t * sa;
     t = t * sw;
     if (flags & QGEMM_EPI_BIAS) t = t + bias;
     const float g = (flags & QGEMM_EPI_GELU) ? gelu28(t) : t;
-    float v = __builtin_rintf(g * out_mult);
-    v = fminf(fmaxf(v, -127.0f), 127.0f);
-    return (int8_t)(int32_t)v;
+    const float v = fminf(fmaxf(g * out_mult, -127.0f), 127.0f);
+    return __builtin_bit_cast(uint32_t, v + 12582912.0f);
+}
+
+__device__ __forceinline__ int8_t requant(int32_t acc, float sa, float sw, float bias,
+                                          float out_mult, uint32_t flags) {
+    return (int8_t)(requant_bits(acc, sa, sw, bias, out_mult, flags) & 0xffu);
 }
 
 // Runs f with the epilogue flags as a compile-time constant, so the per
@@ -352,12 +361,12 @@ __global__ __launch_bounds__(512, 1) void w8a8_large_kernel(
                 for (int g = 0; g < 4; ++g) {
                     const int r0 = wm * 128 + i * 32 + 8 * g + 4 * h;  // tile row of register 4g
                     const floatx4 sa4 = *reinterpret_cast<const floatx4*>(&s_sa[r0]);
-                    uint32_t d = 0;
+                    uint32_t fb[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int8_t c = requant(acc[i][t][4 * g + r], sa4[r], swv, bv, out_mult, FL);
-                        d |= (uint32_t)(uint8_t)c << (8 * r);
-                    }
+                    for (int r = 0; r < 4; ++r) fb[r] = requant_bits(acc[i][t][4 * g + r], sa4[r], swv, bv, out_mult, FL);
+                    // the four codes' low bytes, rows r = 0..3 in bytes 0..3
+                    const uint32_t d = __builtin_amdgcn_perm(fb[1], fb[0], 0x0c0c0400u) |
+                                       __builtin_amdgcn_perm(fb[3], fb[2], 0x04000c0cu);
                     stile[(r0 + q) * EPW + wn * 16 + t * 8 + (c32 >> 2)] = quad_rows_u8(d, lane);
                 }
             }
