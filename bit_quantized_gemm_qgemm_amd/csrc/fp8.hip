@@ -153,14 +153,17 @@ __global__ void fp8_slot_finalize_kernel(float* slot) {
 
 // Each lane turns a chunk of 8 codes into 8 fp16 values (cols % 8 == 0, so a
 // chunk never straddles rows); grid-stride over chunks.
+// IDX: the chunk index type (32 bits whenever the indexes fit); row_shift >=
+// 0: chunks per row = 1 << row_shift, and the row index is a shift.
+template <typename IDX>
 __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ Q,
                                                           const float* __restrict__ S,
-                                                          uint16_t* __restrict__ X, size_t nchunk,
-                                                          int chunks_per_row, int per_row) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
+                                                          uint16_t* __restrict__ X, IDX nchunk,
+                                                          int chunks_per_row, int row_shift, int per_row) {
+    const IDX stride = (IDX)gridDim.x * blockDim.x;
+    for (IDX c = (IDX)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
         const uintx2 q = ldg_nt(reinterpret_cast<const uintx2*>(Q) + c);
-        const float s = S[per_row ? c / chunks_per_row : 0];
+        const float s = S[!per_row ? 0 : row_shift >= 0 ? c >> row_shift : c / (IDX)chunks_per_row];
         const uint32_t w[2] = {q.x, q.y};
         uint32_t o[4];
 #pragma unroll
@@ -403,8 +406,14 @@ extern "C" int32_t dequant_fp8_e4m3(const uint8_t* Q, const float* scales, uint1
     if (cols == 0 || cols % 8 != 0 || (per_row != 0 && per_row != 1)) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(Q, 16) || !qgh::aligned(X, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
     const size_t nchunk = (size_t)rows * cols / 8;
-    hipLaunchKernelGGL(fp8_dequant_kernel, dim3(grid_for(nchunk)), dim3(256), 0, (hipStream_t)stream, Q, scales,
-                       X, nchunk, cols / 8, per_row);
+    const int blocks = grid_for(nchunk), cpr = cols / 8;
+    const int shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctz((unsigned)cpr) : -1;
+    if (nchunk + (size_t)blocks * 256 < ((size_t)1 << 32))
+        hipLaunchKernelGGL(fp8_dequant_kernel<uint32_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q,
+                           scales, X, (uint32_t)nchunk, cpr, shift, per_row);
+    else
+        hipLaunchKernelGGL(fp8_dequant_kernel<size_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q, scales,
+                           X, nchunk, cpr, shift, per_row);
     return qgh::launch_status();
 }
 

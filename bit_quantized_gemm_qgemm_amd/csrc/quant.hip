@@ -132,14 +132,18 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(const uint16_t* __
 
 // Dequantization: each lane turns a chunk of 8 codes of one row into fp16
 // (cols % 8 == 0, so a chunk never straddles rows); grid-stride over chunks.
+// IDX: the chunk index type (32 bits whenever the indexes fit, which turns
+// the row index's 64-bit division into a 32-bit one); row_shift >= 0: chunks
+// per row = 1 << row_shift, and the row index is a shift.
+template <typename IDX>
 __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__ Q,
                                                       const float* __restrict__ S,
-                                                      uint16_t* __restrict__ X, size_t nchunk,
-                                                      int chunks_per_row) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
+                                                      uint16_t* __restrict__ X, IDX nchunk,
+                                                      int chunks_per_row, int row_shift) {
+    const IDX stride = (IDX)gridDim.x * blockDim.x;
+    for (IDX c = (IDX)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
         const uintx2 q = qg::ldg_nt(reinterpret_cast<const uintx2*>(Q) + c);
-        const float s = S[c / chunks_per_row];
+        const float s = S[row_shift >= 0 ? c >> row_shift : c / (IDX)chunks_per_row];
         const uint32_t w[2] = {q.x, q.y};
         uint32_t o[4];
 #pragma unroll
@@ -205,7 +209,12 @@ extern "C" int32_t dequant_sym_int8(const int8_t* Q, const float* scales, uint16
     const size_t nchunk = (size_t)rows * cols / 8;
     const size_t want = (nchunk + 255) / 256;
     const int blocks = (int)(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL(dequant_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q, scales,
-                       X, nchunk, (int)(cols / 8));
+    const int cpr = cols / 8, shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctz((unsigned)cpr) : -1;
+    if (nchunk + (size_t)blocks * 256 < ((size_t)1 << 32))
+        hipLaunchKernelGGL(dequant_kernel<uint32_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q, scales,
+                           X, (uint32_t)nchunk, cpr, shift);
+    else
+        hipLaunchKernelGGL(dequant_kernel<size_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q, scales,
+                           X, nchunk, cpr, shift);
     return qgh::launch_status();
 }
