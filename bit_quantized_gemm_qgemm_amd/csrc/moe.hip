@@ -260,15 +260,21 @@ __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
 
 // y[t] = fp16(sum_j w[t][j] * o[slot(t, j)]), j ascending; o = the K-split
 // partials added in split order.
+// IDX: the chunk index type (32 bits whenever the indexes fit); row_shift >=
+// 0: H / 8 = 1 << row_shift, and the token of a chunk is a shift (the first
+// loads of a chunk wait for that index: a 64-bit division there sat on the
+// critical path).
+template <typename IDX>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ w, Work wk,
                                                           uint16_t* __restrict__ Y, int T, int H,
-                                                          int topK, int splits) {
+                                                          int topK, int splits, int row_shift) {
     const int per_row = H / 8;
-    const size_t total = (size_t)T * per_row;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const IDX total = (IDX)T * per_row;
+    const IDX stride = (IDX)gridDim.x * blockDim.x;
     const size_t split_stride = (size_t)T * topK * H;
-    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
-        const int t = (int)(c / per_row), c8 = (int)(c % per_row);
+    for (IDX c = (IDX)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+        const int t = (int)(row_shift >= 0 ? c >> row_shift : c / (IDX)per_row);
+        const int c8 = (int)(c - (IDX)t * per_row);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < topK; ++j) {
             const int p = t * topK + j;
@@ -308,8 +314,14 @@ int32_t launch_moe(const uint16_t* X, const uint16_t* logits, const uint8_t* wg,
                        wd, wd, sd, sd, wk, T, H, I, E, topK, splits, 0);
     const size_t chunks = (size_t)T * H / 8;
     const size_t want = (chunks + 255) / 256;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((int)(want < 4096 ? want : 4096)), dim3(256), 0, st,
-                       w, wk, Y, T, H, topK, splits);
+    const int cblocks = (int)(want < 4096 ? want : 4096), per_row = H / 8;
+    const int shift = (per_row & (per_row - 1)) == 0 ? __builtin_ctz((unsigned)per_row) : -1;
+    if (chunks + (size_t)cblocks * 256 < ((size_t)1 << 32))
+        hipLaunchKernelGGL(moe_combine_kernel<uint32_t>, dim3(cblocks), dim3(256), 0, st, w, wk, Y, T, H, topK,
+                           splits, shift);
+    else
+        hipLaunchKernelGGL(moe_combine_kernel<size_t>, dim3(cblocks), dim3(256), 0, st, w, wk, Y, T, H, topK,
+                           splits, shift);
     return qgh::launch_status();
 }
 

@@ -345,11 +345,12 @@ def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation=0):
 # projections (96 rows per gate/up pass, 128 per down pass); eight experts with an
 # even number of column tiles take the paired expert-to-XCD mapping of the gate/up
 # pass: (300, ..., 8, 2) with experts of two and three 32-row blocks, (60, 128, 384,
-# 8, ...) with an odd tile count the plain one
+# 8, ...) with an odd tile count the plain one; hidden 384 (48 chunks of 8 per
+# row, not a power of two) takes the combine's division path
 @pytest.mark.parametrize("T,H,I,E,topK,G", [(37, 256, 384, 4, 2, 128), (70, 256, 256, 8, 2, 64),
                                              (5, 128, 256, 3, 3, 32), (130, 128, 128, 2, 1, 128),
                                              (300, 128, 256, 2, 2, 128), (300, 128, 256, 8, 2, 128),
-                                             (60, 128, 384, 8, 2, 128)])
+                                             (60, 128, 384, 8, 2, 128), (40, 384, 256, 4, 2, 128)])
 def test_moe_small(qg, T, H, I, E, topK, G):
     X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 800 + T)
     logits[3] = logits[3, 0]  # an all-tie row: lower expert index wins
