@@ -8,19 +8,24 @@ namespace {
 
 using namespace qg;
 
-constexpr int kLoads = 8;  // 16-byte loads per lane, all issued before the first wait
+// 16-byte loads per lane (all issued before the first wait) and threads per
+// workgroup: the fastest of a sweep at a 23 MB working set (16 rotated
+// buffers, plain launches): 2 x 128 4.72-4.78 us, 1 x 256 4.77-4.85,
+// 2 x 256 4.82, 2 x 512 4.85, 3 x 256 4.89, 8 x 256 4.92-4.94,
+// 16 x 256 5.27 -- many short workgroups stream best
+constexpr int kLoads = 2, kThreads = 128;
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const uintx4* __restrict__ p, size_t n16,
-                                                          uint32_t* __restrict__ sink) {
-    const size_t base = (size_t)blockIdx.x * kLoads * 256 + threadIdx.x;
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uintx4* __restrict__ p, size_t n16,
+                                                               uint32_t* __restrict__ sink) {
+    const size_t base = (size_t)blockIdx.x * kLoads * kThreads + threadIdx.x;
     uintx4 v[kLoads];
-    if (base + (size_t)(kLoads - 1) * 256 < n16) {
+    if (base + (size_t)(kLoads - 1) * kThreads < n16) {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) v[i] = ldg_nt(p + base + (size_t)i * 256);
+        for (int i = 0; i < kLoads; ++i) v[i] = ldg_nt(p + base + (size_t)i * kThreads);
     } else {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
-            const size_t j = base + (size_t)i * 256;
+            const size_t j = base + (size_t)i * kThreads;
             v[i] = j < n16 ? ldg_nt(p + j) : uintx4{0u, 0u, 0u, 0u};
         }
     }
@@ -98,9 +103,9 @@ extern "C" int32_t qgemm_stream_read(const void* buf, size_t bytes, uint32_t* si
     if (bytes % 16 != 0) return QGEMM_BAD_SHAPE;
     if (!qgh::aligned(buf, 16) || !qgh::aligned(sink, 4)) return QGEMM_MISALIGNED;
     const size_t n16 = bytes / 16;
-    const size_t blocks = (n16 + kLoads * 256 - 1) / (kLoads * 256);
+    const size_t blocks = (n16 + kLoads * kThreads - 1) / (kLoads * kThreads);
     if (blocks > 0x7fffffff) return QGEMM_UNSUPPORTED;
-    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
                        static_cast<const uintx4*>(buf), n16, sink);
     return qgh::launch_status();
 }
