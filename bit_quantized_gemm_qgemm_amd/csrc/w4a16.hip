@@ -62,7 +62,7 @@ void launch_w4a16(int tactic, const uint16_t* A, const uint8_t* wf, const uint16
         case QGEMM_W4A16_TACTIC_PREFILL: launch_wq_prefill<4, G>(A, wf, S, N, Y, M, N, K, st); break;
         default: {
             dim3 grid((N / PL_BN) * ((M + PL_BM - 1) / PL_BM));
-            hipLaunchKernelGGL((wq_prefill_large_kernel<4, G>), grid, dim3(256), 0, st, A, wf, S, N, Y, M, N, K);
+            hipLaunchKernelGGL((wq_prefill_large_pc_kernel<G>), grid, dim3(320), 0, st, A, wf, S, N, Y, M, N, K);
         }
     }
 }

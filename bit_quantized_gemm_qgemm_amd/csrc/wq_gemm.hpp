@@ -433,9 +433,10 @@ __global__ __launch_bounds__(256, 2) void wq_prefill_kernel(const uint16_t* __re
 // its columns, so every B element is dequantized once per workgroup.
 //
 // Every load in the main loop is a buffer -> LDS DMA (no VGPR destinations,
-// no VALU): A and B (fragment blocks plus scale rows) in three buffers each
-// for int4, so both are fetched two chunks ahead, and two each for int8,
-// whose B stages are twice as large.  A wave's A-DMA instruction
+// no VALU).  This kernel takes int8 weights: two A buffers and two B stages
+// (fragment blocks plus scale rows), its B stages being twice the int4
+// size; int4 weights take the producer-wave kernel below, whose A and B have
+// three buffers each.  A wave's A-DMA instruction
 // fills 1 KB of LDS in lane order (four 256-byte rows); the lane that fills
 // position pos of row r fetches piece pos ^ (r & 15) of that row, so the MFMA
 // fragment reads, 16 rows at one k-group, hit 16 distinct 16-byte bank
@@ -453,23 +454,22 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     constexpr int NG = 128 / G;
     constexpr int KBLK = WFormat<WB>::kBlock;  // bytes per 16-column x 128-k block
     constexpr int P = WFormat<WB>::kPieces;
-    constexpr int NBST = WB == 4 ? 3 : 2;      // B stages
-    constexpr int NABUF = WB == 4 ? 3 : 2;     // A buffers
-    // three buffers of each: a chunk's copies can be spread over the k-steps;
-    // with two of each only the B copies can (BSPREAD), A waits for the boundary
-    constexpr bool SPREAD = NABUF == 3 && NBST == 3;
-    constexpr bool BSPREAD = !SPREAD && NBST == 2;
+    static_assert(WB == 8, "int8 weights; int4 takes wq_prefill_large_pc_kernel");
+    // two of each: chunk c + 2's B copies are spread over the k-steps of
+    // trip c, the A copies wait for the boundary
+    constexpr int NBST = 2;   // B stages
+    constexpr int NABUF = 2;  // A buffers
     constexpr int SLAB = PL_BM * 128;          // halfs per A buffer (32 KB)
     constexpr int BST = 16 * KBLK + 512 * NG;  // bytes per B stage: 16 fragment blocks + NG scale rows
     constexpr int BDMA = 4 * P + 2 * NG;       // DMA instructions per wave for one B stage
     // One LDS array for A and B: the compiler tells DMA targets from the
     // buffers being read by their offsets within one array, but not across
     // two arrays (it would then wait for every DMA before each LDS read).
-    // (One size for every instantiation, the largest: int8 B stages with
-    // G = 32.  An array whose size depends on the template parameters, passed
-    // to the DMA builtin, made the host compiler drop the kernel's launch
-    // stub without a diagnostic.)
-    __shared__ __attribute__((aligned(1024))) uint16_t sA[(3 * PL_BM * 128 * 2 + 3 * (16384 + 512 * 4)) / 2];
+    // (One size for every instantiation, the largest: B stages with G = 32.
+    // An array whose size depends on the template parameters, passed to the
+    // DMA builtin, made the host compiler drop the kernel's launch stub
+    // without a diagnostic.)
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[(2 * PL_BM * 128 * 2 + 2 * (32768 + 512 * 4)) / 2];
     static_assert(NABUF * PL_BM * 128 * 2 + NBST * BST <= (int)sizeof(sA), "A buffers and B stages fit the LDS array");
     uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + NABUF * SLAB);
     // (the wave index as a scalar: every DMA's LDS destination and source
@@ -545,7 +545,6 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     };
     // DMA instruction i of chunk c (i < 8: A; then the B blocks, then the
     // scale rows), for issuing a chunk's copies a few at a time
-    constexpr int NDMA = 8 + BDMA;
     auto dma_one = [&](int c, int buf, int stage, int i) __attribute__((always_inline)) {
         if (i < 8) {
             buffer_load_lds<16>(ra, sA + buf * SLAB + (8 * wave + i) * 512, aoff[i], c * 256);
@@ -607,10 +606,10 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     // its first k-step.
     Chunk b;
     half8 a[4], bf[2];
-    // One trip = k-steps 0..6 of chunk c, the boundary, then k-step 7 with
-    // chunk c + 1's set-up and the DMAs of chunk c + 2 (A, into the buffer
-    // chunk c was read from) and chunk c + NBST (B, into chunk c's stage,
-    // whose registers were read one trip earlier).  Every LDS offset a DMA
+    // One trip = k-steps 0..6 of chunk c with chunk c + 2's B copies (into
+    // chunk c's stage, whose registers were read one trip earlier), the
+    // boundary, then k-step 7 with chunk c + 1's set-up and chunk c + 2's A
+    // copies (into the buffer chunk c was read from).  Every LDS offset a DMA
     // writes is a compile-time constant in each trip (buf and stage are
     // literals at every call; after inlining they fold): with a run-time
     // index the compiler cannot tell the DMA target from the buffer being
@@ -618,32 +617,22 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
     // clamp to the last chunk: the copies past the end are never read.
     auto trip = [&](int c, int buf, int stage) __attribute__((always_inline)) {
         const uint16_t* sa = sA + buf * SLAB;
-        // SPREAD: chunk c + 2's copies go out two or three per k-step, into
-        // the buffer and stage chunk c - 1 used (free since the previous
-        // boundary); issued as one burst, the four waves' copies queue up in
-        // the address unit and each wave stalls at issue while the matrix
-        // unit runs dry
+        // chunk c + 2's B copies go out two or three per k-step: issued as
+        // one burst, the four waves' copies queue up in the address unit and
+        // each wave stalls at issue while the matrix unit runs dry
         const int cd = c + 2 < last ? c + 2 : last;
-        const int dbuf = buf == 0 ? NABUF - 1 : buf - 1, dstage = stage == 0 ? NBST - 1 : stage - 1;
 #pragma unroll
         for (int s = 0; s < 7; ++s) {
             half8 an[4], bn[2];
             operands(sa, b, s + 1, an, bn);
-            if constexpr (SPREAD) {
 #pragma unroll
-                for (int i = s * NDMA / 7; i < (s + 1) * NDMA / 7; ++i) dma_one(cd, dbuf, dstage, i);
-            }
-            if constexpr (BSPREAD) {
-                // chunk c + 2's B into chunk c's stage (its registers were read one trip earlier)
-#pragma unroll
-                for (int i = 8 + s * BDMA / 7; i < 8 + (s + 1) * BDMA / 7; ++i) dma_one(cd, buf, stage, i);
-            }
+            for (int i = 8 + s * BDMA / 7; i < 8 + (s + 1) * BDMA / 7; ++i) dma_one(cd, buf, stage, i);
             mfmas(a, bf);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                 if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                if ((SPREAD || BSPREAD) && (q == 1 || q == 3 || q == 5)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
+                if (q == 1 || q == 3 || q == 5) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
             }
 #pragma unroll
@@ -651,11 +640,10 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
 #pragma unroll
             for (int t = 0; t < 2; ++t) bf[t] = bn[t];
         }
-        // chunk c + 1's A and B have landed (the copies this trip issued, or
-        // with three B stages and no spreading chunk c + 2's B, may still be
-        // in flight); every wave's reads of chunk c's A buffer and of the B
-        // stage refilled below are done
-        wait_vmcnt<SPREAD ? NDMA : (BSPREAD || NBST == 3 ? BDMA : 0)>();
+        // chunk c + 1's A and B have landed (chunk c + 2's B copies, issued
+        // this trip, may still be in flight); every wave's reads of chunk c's
+        // A buffer are done
+        wait_vmcnt<BDMA>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -664,7 +652,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         read_b(sB + nstage * BST, b);
         half8 an[4], bn[2];
         a_frags(sA + nbuf * SLAB, 0, an);
-        if constexpr (!SPREAD) dma_a(c + NABUF < last ? c + NABUF : last, buf);
+        dma_a(c + NABUF < last ? c + NABUF : last, buf);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             acc[0][t] = mfma32(a[0], bf[t], acc[0][t]);
@@ -679,8 +667,7 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         // (a barrier to the scheduler: every A DMA is issued before the B DMAs,
         // which the counter wait above relies on)
         __builtin_amdgcn_sched_barrier(0);
-        // second half: the B DMAs and the dequant of chunk c + 1's first step
-        if constexpr (!SPREAD && !BSPREAD) dma_b(c + NBST < last ? c + NBST : last, stage);
+        // second half: the dequant of chunk c + 1's first step
 #pragma unroll
         for (int t = 0; t < 2; ++t) bn[t] = b_frag<2, G, WB>(b, t, 0);
 #pragma unroll
@@ -701,36 +688,18 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
         for (int t = 0; t < 2; ++t) bf[t] = bn[t];
     };
 
-    // chunks 0 .. NABUF - 1 (SPREAD: 0 and 1; the first trip fetches chunk 2)
-    constexpr int PRE = SPREAD ? 2 : NABUF;
+    // chunks 0 and 1
 #pragma unroll
-    for (int ab = 0; ab < PRE; ++ab) dma_a(ab < last ? ab : last, ab);
+    for (int ab = 0; ab < NABUF; ++ab) dma_a(ab < last ? ab : last, ab);
 #pragma unroll
-    for (int st = 0; st < (SPREAD ? 2 : NBST); ++st) dma_b(st < last ? st : last, st);
+    for (int st = 0; st < NBST; ++st) dma_b(st < last ? st : last, st);
     wait_vmcnt<0>();
     __syncthreads();
     read_b(sB, b);
     operands(sA, b, 0, a, bf);
-    if constexpr (NABUF == 3) {
-        for (int c = 0; c < kchunks; c += 3) {
-            trip(c, 0, 0);
-            if (c + 1 < kchunks) trip(c + 1, 1, 1);
-            if (c + 2 < kchunks) trip(c + 2, 2, 2);
-        }
-    } else if constexpr (NBST == 3) {
-        for (int c = 0; c < kchunks; c += 6) {
-            trip(c, 0, 0);
-            if (c + 1 < kchunks) trip(c + 1, 1, 1);
-            if (c + 2 < kchunks) trip(c + 2, 0, 2);
-            if (c + 3 < kchunks) trip(c + 3, 1, 0);
-            if (c + 4 < kchunks) trip(c + 4, 0, 1);
-            if (c + 5 < kchunks) trip(c + 5, 1, 2);
-        }
-    } else {
-        for (int c = 0; c < kchunks; c += 2) {
-            trip(c, 0, 0);
-            if (c + 1 < kchunks) trip(c + 1, 1, 1);
-        }
+    for (int c = 0; c < kchunks; c += 2) {
+        trip(c, 0, 0);
+        if (c + 1 < kchunks) trip(c + 1, 1, 1);
     }
     // ---- epilogue: Y through an LDS tile in 16-byte row pieces.  A quad
     // transpose gives each lane four adjacent columns of one row (8 bytes of
@@ -760,6 +729,238 @@ __global__ __launch_bounds__(256, 1) void wq_prefill_large_kernel(const uint16_t
             }
     __syncthreads();
     // 128 rows x 32 pieces of 8 outputs (N % 256 == 0: every piece is whole and aligned)
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int idx = tid + 256 * p, row = idx >> 5, piece = idx & 31;
+        if (m0 + row < M)
+            __builtin_nontemporal_store(*reinterpret_cast<const uintx4*>(&stile[row * EPW + piece * 4]),
+                                        reinterpret_cast<uintx4*>(Y + (size_t)(m0 + row) * N + n0 + piece * 8));
+    }
+}
+
+// Large-M prefill for int4 weights: the tile, k-step pipeline and epilogue
+// of the kernel above, with three A buffers and three B stages, and a fifth
+// wave that issues every DMA copy.  Waves 0..3 compute and issue no memory
+// instruction in the main loop; wave 4 copies chunk c + 2 (32 A rows of
+// 1 KB, 16 fragment blocks, the scale rows once) during trip c into the
+// buffers chunk c - 1 used, waits for chunk c + 1 and meets the computing
+// waves at the barrier of their trip c.  Against the same kernel with each
+// computing wave issuing its share of the copies, spread over its k-steps:
+// 58.1 against 59.0 us and 61.9 against 62.9 us (two boxes, M = 2048,
+// K = N = 4096), bit-identical outputs; the copies themselves still cost
+// (issued with pauses between groups of eight they arrive late: 66.7 us).
+// The computing waves fit 256 registers (two waves share one SIMD).
+template <int G>
+__global__ __launch_bounds__(320, 1) void wq_prefill_large_pc_kernel(const uint16_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ wf,
+                                                               const uint16_t* __restrict__ S, int ldS,
+                                                               uint16_t* __restrict__ Y, int M, int N, int K) {
+    constexpr int WB = 4;
+    constexpr int NG = 128 / G;
+    constexpr int KBLK = WFormat<WB>::kBlock;
+    constexpr int P = WFormat<WB>::kPieces;
+    constexpr int SLAB = PL_BM * 128;
+    constexpr int BST = 16 * KBLK + 512 * NG;
+    constexpr int NCP = 32 + 16 * P + 2 * NG;  // copies per chunk
+    static_assert(NCP < 64, "one chunk's copies fit the counter");
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[(3 * PL_BM * 128 * 2 + 3 * (16384 + 512 * 4)) / 2];
+    uint8_t* const sB = reinterpret_cast<uint8_t*>(sA + 3 * SLAB);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int mtiles = (M + PL_BM - 1) / PL_BM;
+    const int L = blockIdx.x;
+    const int m0 = (L % mtiles) * PL_BM, n0 = (L / mtiles) * PL_BN;
+    const int kchunks = K / 128, last = kchunks - 1;
+
+    if (wave == 4) {
+        const int rsub = lane >> 4, pos = lane & 15;
+        uint32_t aoff[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int r = 4 * j + rsub;
+            const int gr = m0 + r < M ? r : M - 1 - m0;
+            aoff[j] = ((uint32_t)gr * (uint32_t)K + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
+        }
+        const int arows = M - m0 < PL_BM ? M - m0 : PL_BM;
+        const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(A + (size_t)m0 * K, (uint32_t)arows * (uint32_t)K * 2u);
+        const uint32_t sb_stride = (uint32_t)kchunks * (8 * KBLK);
+        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(wf + (size_t)(n0 >> 7) * sb_stride, 2u * sb_stride);
+        const uint32_t srows = ldS == 0 ? 1u : (uint32_t)(K / G);
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(S + n0, ((srows - 1u) * (uint32_t)ldS + (uint32_t)PL_BN) * 2u);
+        const uint32_t boff = (uint32_t)lane * 16u, soff = (uint32_t)lane * 4u;
+        auto copy = [&](int c, int buf, int i) __attribute__((always_inline)) {
+            if (i < 32) {
+                buffer_load_lds<16>(ra, sA + buf * SLAB + i * 512, aoff[i], c * 256);
+            } else if (i < 32 + 16 * P) {
+                const int strip = (i - 32) / P, p = (i - 32) % P;
+                buffer_load_lds<16>(rb, sB + buf * BST + strip * KBLK + p * 1024, boff,
+                                    (uint32_t)c * (8 * KBLK) + (strip >> 3) * sb_stride + (strip & 7) * KBLK + p * 1024);
+            } else {
+                const int g = (i - 32 - 16 * P) / 2, hh = (i - 32 - 16 * P) % 2;
+                buffer_load_lds<4>(rs, sB + buf * BST + 16 * KBLK + g * 512 + hh * 256, soff,
+                                   ((uint32_t)(c * NG + g) * (uint32_t)ldS + 128u * hh) * 2u);
+            }
+        };
+        // groups of eight, at most 63 copies outstanding
+        auto issue = [&](int c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i0 = 0; i0 < NCP; i0 += 8) {
+                wait_vmcnt<55>();
+#pragma unroll
+                for (int i = i0; i < i0 + 8 && i < NCP; ++i) copy(c, buf, i);
+            }
+        };
+        issue(0, 0);
+        issue(1 < last ? 1 : last, 1);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        // trip c: chunk c + 2 into the buffer chunk c - 1 used (free since the
+        // previous barrier), then wait for chunk c + 1 and meet the computing
+        // waves at the barrier of their trip c
+        auto ptrip = [&](int c, int dbuf) __attribute__((always_inline)) {
+            issue(c + 2 < last ? c + 2 : last, dbuf);
+            wait_vmcnt<NCP>();
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int c = 0; c < kchunks; c += 3) {
+            ptrip(c, 2);
+            if (c + 1 < kchunks) ptrip(c + 1, 0);
+            if (c + 2 < kchunks) ptrip(c + 2, 1);
+        }
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // the epilogue's two barriers
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
+
+    const int h = lane >> 5, c32 = lane & 31;
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][t][j] = 0.f;
+    typedef BChunk<2, G, WB> Chunk;
+    auto read_b = [&](const uint8_t* sb, Chunk& b) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int colt = wave * 64 + t * 32 + c32;
+            const uint8_t* blk = sb + (colt >> 4) * KBLK + (colt & 15) * 16;
+#pragma unroll
+            for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    b.raw[t][qi * P + p] = *reinterpret_cast<const uintx4*>(blk + p * 1024 + 16 * 16 * (h + 2 * qi));
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                b.sc[t][g] = reinterpret_cast<const uint16_t*>(sb + 16 * KBLK)[g * 256 + colt];
+        }
+    };
+    auto a_frags = [&](const uint16_t* sa, int s, half8 (&a)[4]) {
+        const int kg = kgroup_of_step(s, h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = i * 32 + c32;
+            a[i] = *reinterpret_cast<const half8*>(&sa[r * 128 + ((kg ^ (r & 15)) * 8)]);
+        }
+    };
+    auto operands = [&](const uint16_t* sa, const Chunk& b, int s, half8 (&a)[4], half8 (&bf)[2]) {
+        a_frags(sa, s, a);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bf[t] = b_frag<2, G, WB>(b, t, s);
+    };
+    auto mfmas = [&](const half8 (&a)[4], const half8 (&bf)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], bf[t], acc[i][t]);
+    };
+    Chunk b;
+    half8 a[4], bf[2];
+    auto trip = [&](int buf) __attribute__((always_inline)) {
+        const uint16_t* sa = sA + buf * SLAB;
+#pragma unroll
+        for (int s = 0; s < 7; ++s) {
+            half8 an[4], bn[2];
+            operands(sa, b, s + 1, an, bn);
+            mfmas(a, bf);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                if (q < 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = an[i];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bf[t] = bn[t];
+        }
+        // every wave's reads of chunk c are done; the producer has waited for chunk c + 1
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int nbuf = buf + 1 < 3 ? buf + 1 : 0;
+        read_b(sB + nbuf * BST, b);
+        half8 an[4], bn[2];
+        a_frags(sA + nbuf * SLAB, 0, an);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[0][t] = mfma32(a[0], bf[t], acc[0][t]);
+            acc[1][t] = mfma32(a[1], bf[t], acc[1][t]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < 2) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bn[t] = b_frag<2, G, WB>(b, t, 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            acc[2][t] = mfma32(a[2], bf[t], acc[2][t]);
+            acc[3][t] = mfma32(a[3], bf[t], acc[3][t]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = an[i];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bf[t] = bn[t];
+    };
+    __syncthreads();
+    read_b(sB, b);
+    operands(sA, b, 0, a, bf);
+    for (int c = 0; c < kchunks; c += 3) {
+        trip(0);
+        if (c + 1 < kchunks) trip(1);
+        if (c + 2 < kchunks) trip(2);
+    }
+    __syncthreads();
+    constexpr int EPW = 144;
+    uint32_t* stile = reinterpret_cast<uint32_t*>(sA);
+    const int q = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int r0 = i * 32 + 8 * g + 4 * h;
+                const uint32_t v0 = f2h(acc[i][t][4 * g]), v1 = f2h(acc[i][t][4 * g + 1]);
+                const uint32_t v2 = f2h(acc[i][t][4 * g + 2]), v3 = f2h(acc[i][t][4 * g + 3]);
+                uint32_t e0, e1;
+                quad_rows_u16(v0 | (v1 << 16), v2 | (v3 << 16), lane, e0, e1);
+                *reinterpret_cast<uintx2*>(&stile[(r0 + q) * EPW + wave * 32 + t * 16 + 2 * (c32 >> 2)]) =
+                    uintx2{e0, e1};
+            }
+    __syncthreads();
     const int tid = threadIdx.x;
 #pragma unroll 4
     for (int p = 0; p < 16; ++p) {
