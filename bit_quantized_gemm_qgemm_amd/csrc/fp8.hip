@@ -96,24 +96,22 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
 
 // ------------------------------------------------------------------ per-tensor quant
 
-// The tensor's amax is built in the scale slot itself: it is zeroed, every
-// block raises it with an integer atomic max on the fp32 bit pattern (|x| >= 0
-// orders like its bits, and a maximum does not depend on the order of the
-// updates, so the result is deterministic), the codes are written with
-// m = 448 / amax, and the slot is finally turned into s = amax / 448.  Four
-// stream-ordered launches; no memset (the sequence may be graph-captured).
-__global__ void fp8_slot_zero_kernel(uint32_t* slot) { *slot = 0u; }
-
-// One block per CU, eight 16-byte loads in flight per lane, one atomic per
-// block.  Atomics on one address are serialized (about 10 ns each, as
-// measured on MI355X): 1024 blocks spent 10 of their 15 us in them; 256
-// blocks take 6 us for 32 MB.
+// Three stream-ordered launches, no atomics and no memset (the sequence may
+// be graph-captured): (1) each of P <= 256 blocks writes the maximum |x| of
+// its share of X as an fp32 value into bytes 4b .. 4b + 3 of Q (Q has
+// 8 * nchunk >= 4 P bytes); (2) every block takes the maximum of those P
+// values (exact, so the order is free) and writes the codes of every chunk
+// past the first ceil(P / 2), which hold the partial maxima; (3) one block
+// takes the maximum again, writes the codes of those first chunks and the
+// scale s = amax / 448.  (Before: a scale slot zeroed by a one-thread
+// kernel and raised by one integer atomic max per block, serialized at
+// about 10 ns each, then a one-thread kernel turning it into s.)
 constexpr int AMAX_BLOCKS = 256;
 constexpr int AMAX_LD = 8;
 
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t* __restrict__ X, size_t nchunk,
-                                                       uint32_t* __restrict__ slot) {
-    __shared__ float part[4];
+                                                       float* __restrict__ part) {
+    __shared__ float red[4];
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     const uintx4* x = reinterpret_cast<const uintx4*>(X);
     float amax = 0.0f;
@@ -127,26 +125,59 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t* __restric
     }
     for (; c < nchunk; c += stride) amax = fmaxf(amax, absmax8(ldg_nt(x + c)));
     amax = group_max<64>(amax);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const float m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-        atomicMax(slot, __builtin_bit_cast(uint32_t, m));
-    }
-}
-__global__ __launch_bounds__(256) void fp8_quant_tensor_kernel(const uint16_t* __restrict__ X,
-                                                               uint8_t* __restrict__ Q, size_t nchunk,
-                                                               const uint32_t* __restrict__ slot) {
-    const float amax = __builtin_bit_cast(float, *slot);
-    const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride)
-        reinterpret_cast<uintx2*>(Q)[c] = fp8x8(ldg_nt(reinterpret_cast<const uintx4*>(X) + c), mult);
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__global__ void fp8_slot_finalize_kernel(float* slot) {
-    const float amax = *slot;
-    *slot = amax > 0.0f ? amax / 448.0f : 0.0f;
+// The tensor's amax from the P partial maxima (256 threads).
+__device__ __forceinline__ float block_amax(const float* __restrict__ part, int P, float* red) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < P; i += 256) m = fmaxf(m, part[i]);
+    m = group_max<64>(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Chunks head .. nchunk - 1, four per thread per step (loads first), over
+// at most 512 blocks.  At 4096 x 4096 (one box, the three launches): 19.0 us
+// with 512 blocks, 19.2 with 1024, 20.3 with 2048, 21.0 with 8192 (one chunk
+// per thread) and with 256; eight loads per step 21.7, two 20.1; 128, 512
+// or 1024 amax blocks instead of 256 were slower (more partial maxima for
+// every quant block, or fewer loads in flight).
+constexpr int QT_BLOCKS = 512;
+__global__ __launch_bounds__(256) void fp8_quant_tensor_kernel(const uint16_t* __restrict__ X,
+                                                               uint8_t* __restrict__ Q, size_t nchunk, int P) {
+    __shared__ float red[4];
+    const float amax = block_amax(reinterpret_cast<const float*>(Q), P, red);
+    const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const uintx4* x = reinterpret_cast<const uintx4*>(X);
+    uintx2* q = reinterpret_cast<uintx2*>(Q);
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t c = (size_t)((P + 1) / 2) + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; c + 3 * stride < nchunk; c += 4 * stride) {
+        uintx4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = ldg_nt(x + c + i * stride);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[c + i * stride] = fp8x8(v[i], mult);
+    }
+    for (; c < nchunk; c += stride) q[c] = fp8x8(ldg_nt(x + c), mult);
+}
+
+// One block of 256 threads: the first ceil(P / 2) chunks and the scale.
+__global__ __launch_bounds__(256) void fp8_quant_tensor_head_kernel(const uint16_t* __restrict__ X,
+                                                                    uint8_t* __restrict__ Q, int P,
+                                                                    float* __restrict__ scale) {
+    __shared__ float red[4];
+    // (every thread's read of the partial maxima is done at the barrier
+    // inside, before any code overwrites them)
+    const float amax = block_amax(reinterpret_cast<const float*>(Q), P, red);
+    const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    for (int c = threadIdx.x; c < (P + 1) / 2; c += 256)
+        reinterpret_cast<uintx2*>(Q)[c] = fp8x8(reinterpret_cast<const uintx4*>(X)[c], mult);
+    if (threadIdx.x == 0) *scale = amax > 0.0f ? amax / 448.0f : 0.0f;
 }
 
 // ------------------------------------------------------------------ dequant
@@ -388,13 +419,13 @@ extern "C" int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, 
         return qgh::launch_status();
     }
     const size_t nchunk = (size_t)rows * cols / 8;
-    uint32_t* slot = reinterpret_cast<uint32_t*>(scales);
-    hipLaunchKernelGGL(fp8_slot_zero_kernel, dim3(1), dim3(1), 0, st, slot);
-    const int ablocks = grid_for(nchunk) < AMAX_BLOCKS ? grid_for(nchunk) : AMAX_BLOCKS;
-    hipLaunchKernelGGL(fp8_amax_kernel, dim3(ablocks), dim3(256), 0, st, X, nchunk, slot);
-    hipLaunchKernelGGL(fp8_quant_tensor_kernel, dim3(grid_for(nchunk)), dim3(256), 0, st, X, Q, nchunk,
-                       (const uint32_t*)slot);
-    hipLaunchKernelGGL(fp8_slot_finalize_kernel, dim3(1), dim3(1), 0, st, scales);
+    // P partial maxima: at most 256 blocks, at most one per 256 chunks, so
+    // 4 P <= 8 nchunk bytes of Q hold them
+    const int P = grid_for(nchunk) < AMAX_BLOCKS ? grid_for(nchunk) : AMAX_BLOCKS;
+    hipLaunchKernelGGL(fp8_amax_kernel, dim3(P), dim3(256), 0, st, X, nchunk, reinterpret_cast<float*>(Q));
+    const int qblocks = grid_for(nchunk) < QT_BLOCKS ? grid_for(nchunk) : QT_BLOCKS;
+    hipLaunchKernelGGL(fp8_quant_tensor_kernel, dim3(qblocks), dim3(256), 0, st, X, Q, nchunk, P);
+    hipLaunchKernelGGL(fp8_quant_tensor_head_kernel, dim3(1), dim3(256), 0, st, X, Q, P, scales);
     return qgh::launch_status();
 }
 

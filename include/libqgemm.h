@@ -386,10 +386,11 @@ QGEMM_API int32_t moe_w4a16_no_alloc(const uint16_t* X, const uint16_t* logits,
    scales: fp32, [rows] per row or [1] per tensor (output: s).
    per_row: QGEMM_FP8_PER_ROW or QGEMM_FP8_PER_TENSOR.
    cols must be a multiple of 8 (per row also at most 4096); rows == 0 is a
-   no-op.  Codes and scales are bit-exact functions of X.  Per tensor, the
-   amax is accumulated in scales[0] (by an integer atomic max on its bits,
-   whose result does not depend on order) over four stream-ordered launches,
-   so scales must not be read before the call has completed on the stream. */
+   no-op.  Codes and scales are bit-exact functions of X.  Per tensor, three
+   stream-ordered launches: per-block maxima of |x| are written into the
+   first bytes of Q, the codes of the rest of Q follow, then the codes of
+   those first bytes and scales[0]; Q and scales must not be read before the
+   call has completed on the stream. */
 QGEMM_API int32_t quant_fp8_e4m3(const uint16_t* X, uint8_t* Q, float* scales, int32_t rows,
                                  int32_t cols, int32_t per_row, void* stream);
 

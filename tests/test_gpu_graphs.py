@@ -3,8 +3,8 @@ benchmark runs them) and replayed several times, with eager launches and
 synchronizations between the replays, must reproduce the eager result bit
 for bit on every replay.  Covers kernels with device-side state between
 launches of one call: the split-K partials in a workspace, the per-tensor
-FP8 scale slot (zeroed, raised by atomics and finalized on the device) and
-the MoE workspace.
+FP8 partial maxima (written into the head of Q by one launch, read by the
+next two) and the MoE workspace.
 """
 import os
 

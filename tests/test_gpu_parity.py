@@ -460,6 +460,30 @@ def test_fp8_quant_shapes_and_edge_rows(qg, rows, cols, per_row):
     assert np.array_equal(bits(Xd), bits(oracle.dequant_fp8(Qr, Sr, per_row=per_row)))
 
 
+@pytest.mark.parametrize("case", ["zero", "head", "tail", "negative"])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 16), (64, 4096), (512, 1024)])
+def test_fp8_per_tensor_amax_anywhere(qg, rows, cols, case):
+    """Per tensor, the partial maxima pass through the first bytes of Q before those bytes get
+    their codes: the tensor's amax in the first chunk, in the last, negative or zero (scale 0,
+    all codes 0), from 1 to 256 partial maxima; Q starts filled with NaN codes and is used twice."""
+    X = (qi.activations(rows, cols, 77 + rows + cols) * np.float16(0.01)).astype(np.float16)
+    if case == "zero":
+        X[:] = 0
+    elif case == "head":
+        X[0, 0] = 3.5
+    elif case == "tail":
+        X[-1, -1] = 3.5
+    else:
+        X[rows // 2, cols // 2] = -3.5
+    Q = torch.full((rows, cols), 0x7F, dtype=torch.uint8, device="cuda")
+    S = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    for x in (X[::-1].copy(), X):
+        Qr, Sr = oracle.quant_fp8(x, per_row=False)
+        qg.quant_fp8_e4m3(dev(x), per_row=False, Q=Q, scales=S)
+        assert np.array_equal(host(Q), Qr), (rows, cols, case)
+        assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32)), (rows, cols, case)
+
+
 @pytest.mark.parametrize("cols", [16, 128])
 def test_fp8_quant_every_fp16_amax(qg, cols):
     """Per-row E4M3 quantization with one row per positive finite fp16 value a
