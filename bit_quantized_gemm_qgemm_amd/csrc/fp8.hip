@@ -182,32 +182,50 @@ __global__ __launch_bounds__(256) void fp8_quant_tensor_head_kernel(const uint16
 
 // ------------------------------------------------------------------ dequant
 
-// Each lane turns a chunk of 8 codes into 8 fp16 values (cols % 8 == 0, so a
-// chunk never straddles rows); grid-stride over chunks.
+// A lane turns chunks of 8 codes into 8 fp16 values (cols % 8 == 0, so a
+// chunk never straddles rows); grid-stride over chunks, four per lane per
+// step with all their loads first, as in the int8 dequantizer (KV cache:
+// 6.23 -> 5.52 us against one chunk per lane).
 // IDX: the chunk index type (32 bits whenever the indexes fit); row_shift >=
 // 0: chunks per row = 1 << row_shift, and the row index is a shift.
+constexpr int FDQ_U = 4, FDQ_BLOCKS = 1024;
+
+__device__ __forceinline__ uintx4 fp8_dequant8(uintx2 q, float s) {
+    const uint32_t w[2] = {q.x, q.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t h0 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0), s);
+        const uint32_t h1 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 1), s);
+        const uint32_t h2 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2), s);
+        const uint32_t h3 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 3), s);
+        o[2 * i] = h0 | (h1 << 16);
+        o[2 * i + 1] = h2 | (h3 << 16);
+    }
+    return uintx4{o[0], o[1], o[2], o[3]};
+}
+
 template <typename IDX>
 __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ Q,
                                                           const float* __restrict__ S,
                                                           uint16_t* __restrict__ X, IDX nchunk,
                                                           int chunks_per_row, int row_shift, int per_row) {
     const IDX stride = (IDX)gridDim.x * blockDim.x;
-    for (IDX c = (IDX)blockIdx.x * blockDim.x + threadIdx.x; c < nchunk; c += stride) {
-        const uintx2 q = ldg_nt(reinterpret_cast<const uintx2*>(Q) + c);
-        const float s = S[!per_row ? 0 : row_shift >= 0 ? c >> row_shift : c / (IDX)chunks_per_row];
-        const uint32_t w[2] = {q.x, q.y};
-        uint32_t o[4];
+    const uintx2* q2 = reinterpret_cast<const uintx2*>(Q);
+    uintx4* x4 = reinterpret_cast<uintx4*>(X);
+    auto row = [&](IDX c) { return !per_row ? (IDX)0 : row_shift >= 0 ? c >> row_shift : c / (IDX)chunks_per_row; };
+    IDX c = (IDX)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; c + (FDQ_U - 1) * stride < nchunk; c += FDQ_U * stride) {
+        uintx2 q[FDQ_U];
+        float s[FDQ_U];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t h0 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 0), s);
-            const uint32_t h1 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 1), s);
-            const uint32_t h2 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 2), s);
-            const uint32_t h3 = f2h_of_product(__builtin_amdgcn_cvt_f32_fp8((int)w[i], 3), s);
-            o[2 * i] = h0 | (h1 << 16);
-            o[2 * i + 1] = h2 | (h3 << 16);
-        }
-        __builtin_nontemporal_store(uintx4{o[0], o[1], o[2], o[3]}, reinterpret_cast<uintx4*>(X) + c);
+        for (int i = 0; i < FDQ_U; ++i) q[i] = ldg_nt(q2 + c + i * stride);
+#pragma unroll
+        for (int i = 0; i < FDQ_U; ++i) s[i] = S[row(c + i * stride)];
+#pragma unroll
+        for (int i = 0; i < FDQ_U; ++i) __builtin_nontemporal_store(fp8_dequant8(q[i], s[i]), x4 + c + i * stride);
     }
+    for (; c < nchunk; c += stride) __builtin_nontemporal_store(fp8_dequant8(ldg_nt(q2 + c), S[row(c)]), x4 + c);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -437,9 +455,10 @@ extern "C" int32_t dequant_fp8_e4m3(const uint8_t* Q, const float* scales, uint1
     if (cols == 0 || cols % 8 != 0 || (per_row != 0 && per_row != 1)) return QGEMM_UNSUPPORTED;
     if (!qgh::aligned(Q, 16) || !qgh::aligned(X, 16) || !qgh::aligned(scales, 4)) return QGEMM_MISALIGNED;
     const size_t nchunk = (size_t)rows * cols / 8;
-    const int blocks = grid_for(nchunk), cpr = cols / 8;
+    const size_t want = (nchunk + 256 * FDQ_U - 1) / (256 * FDQ_U);
+    const int blocks = (int)(want < FDQ_BLOCKS ? want : FDQ_BLOCKS), cpr = cols / 8;
     const int shift = (cpr & (cpr - 1)) == 0 ? __builtin_ctz((unsigned)cpr) : -1;
-    if (nchunk + (size_t)blocks * 256 < ((size_t)1 << 32))
+    if (nchunk + (size_t)blocks * 256 * FDQ_U < ((size_t)1 << 32))
         hipLaunchKernelGGL(fp8_dequant_kernel<uint32_t>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, Q,
                            scales, X, (uint32_t)nchunk, cpr, shift, per_row);
     else

@@ -42,27 +42,28 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uintx4* __r
 // non-temporal stores ran both shapes faster: 5.76 -> 5.56 and 6.18 ->
 // 6.03 us at the KV-cache size).  RB = 16, WB = 8
 // is the int8 quantizer's shape (16.8 MB of fp16 in, 8.4 MB of codes out at
-// the KV-cache size), RB = 8, WB = 16 the dequantizer's.  L = 2 and L = 1
-// measured fastest for the two shapes, and workgroups of 128 threads 1-4 %
-// faster than of 256 for both (the quantizers and dequantizers themselves
-// gained nothing from 128).
+// the KV-cache size), RB = 8, WB = 16 the dequantizer's.  Four pieces per
+// lane in workgroups of 256 threads, each lane's pieces 256 apart: 4.97 to
+// 5.01 us (dequant shape) and 5.48 to 5.57 us (quant shape), against 5.86 and
+// 5.63 with one or two pieces per lane in 128-thread workgroups and 4.99 and
+// 5.84 with the pieces spread over the whole buffer (one box).
 template <int RB, int WB, int L>
-__global__ __launch_bounds__(128) void stream_copy_kernel(const uint8_t* __restrict__ src,
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint8_t* __restrict__ src,
                                                           uint8_t* __restrict__ dst, size_t n) {
     typedef uint32_t r_t __attribute__((ext_vector_type(RB / 4)));
     typedef uint32_t w_t __attribute__((ext_vector_type(WB / 4)));
     const r_t* in = reinterpret_cast<const r_t*>(src);
     w_t* out = reinterpret_cast<w_t*>(dst);
-    const size_t base = (size_t)blockIdx.x * L * 128 + threadIdx.x;
+    const size_t base = (size_t)blockIdx.x * L * 256 + threadIdx.x;
     r_t v[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const size_t j = base + (size_t)i * 128;
+        const size_t j = base + (size_t)i * 256;
         v[i] = j < n ? __builtin_nontemporal_load(in + j) : r_t{};
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const size_t j = base + (size_t)i * 128;
+        const size_t j = base + (size_t)i * 256;
         w_t o;
         if constexpr (RB > WB) {
 #pragma unroll
@@ -85,16 +86,16 @@ extern "C" int32_t qgemm_stream_copy(const void* src, size_t src_bytes, void* ds
     if (!(shrink || grow) || src_bytes % 16 != 0 || dst_bytes % 16 != 0) return QGEMM_BAD_SHAPE;
     if (!qgh::aligned(src, 16) || !qgh::aligned(dst, 16)) return QGEMM_MISALIGNED;
     const size_t n = shrink ? src_bytes / 16 : src_bytes / 8;  // lane-steps
-    const int L = shrink ? 2 : 1;
-    const size_t blocks = (n + (size_t)L * 128 - 1) / ((size_t)L * 128);
+    constexpr int L = 4;
+    const size_t blocks = (n + (size_t)L * 256 - 1) / ((size_t)L * 256);
     if (blocks > 0x7fffffff) return QGEMM_UNSUPPORTED;
     const auto* s8 = static_cast<const uint8_t*>(src);
     auto* d8 = static_cast<uint8_t*>(dst);
     if (shrink)
-        hipLaunchKernelGGL((stream_copy_kernel<16, 8, 2>), dim3((unsigned)blocks), dim3(128), 0,
+        hipLaunchKernelGGL((stream_copy_kernel<16, 8, L>), dim3((unsigned)blocks), dim3(256), 0,
                            (hipStream_t)stream, s8, d8, n);
     else
-        hipLaunchKernelGGL((stream_copy_kernel<8, 16, 1>), dim3((unsigned)blocks), dim3(128), 0,
+        hipLaunchKernelGGL((stream_copy_kernel<8, 16, L>), dim3((unsigned)blocks), dim3(256), 0,
                            (hipStream_t)stream, s8, d8, n);
     return qgh::launch_status();
 }
