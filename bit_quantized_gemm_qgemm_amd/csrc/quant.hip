@@ -63,46 +63,55 @@ __device__ __forceinline__ void int8_scales(float a, float& mult, float& scale) 
 }
 
 // Rows held in registers: each of LPR lanes holds CPL chunks of 8 values;
-// FULL: cols == LPR * CPL * 8, so every chunk is in the row.
-template <int LPR, int CPL, bool FULL>
+// FULL: cols == LPR * CPL * 8, so every chunk is in the row.  A lane group
+// takes NR rows (rows g + r * RPB of its block's RPB * NR), all their loads
+// issued before the first reduction.
+template <int LPR, int CPL, bool FULL, int NR = 1>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ X,
                                                          int8_t* __restrict__ Q,
                                                          float* __restrict__ S, int rows,
                                                          int cols) {
-    constexpr int RPB = 256 / LPR;  // rows per block
+    constexpr int RPB = 256 / LPR;  // rows per block and pass
     const int lane = threadIdx.x % LPR;
-    const int row = blockIdx.x * RPB + threadIdx.x / LPR;
-    const bool live = row < rows;
     const int nchunk = cols / 8;
-    const uint16_t* x = X + (size_t)(live ? row : 0) * cols;
     // Every load is unconditional (a chunk past the row end reads chunk 0 and
-    // is then zeroed): a load under a branch makes the compiler wait for all
-    // outstanding loads at the join, serializing the lane's loads.
-    uintx4 v[CPL];
+    // is then zeroed; a row past the last reads row 0 and stores nothing): a
+    // load under a branch makes the compiler wait for all outstanding loads
+    // at the join, serializing the lane's loads.
+    int row[NR];
+    uintx4 v[NR][CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = lane + i * LPR;
-        v[i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + (FULL || c < nchunk ? c : 0));
+    for (int r = 0; r < NR; ++r) {
+        row[r] = (blockIdx.x * NR + r) * RPB + threadIdx.x / LPR;
+        const uint16_t* x = X + (size_t)(row[r] < rows ? row[r] : 0) * cols;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * LPR;
+            v[r][i] = qg::ldg_nt(reinterpret_cast<const uintx4*>(x) + (FULL || c < nchunk ? c : 0));
+        }
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        if (!FULL && lane + i * LPR >= nchunk) v[i] = uintx4{0, 0, 0, 0};
-        amax = fmaxf(amax, qg::absmax8(v[i]));
-    }
-    amax = qg::group_max<LPR>(amax);
-    if (!live) return;
-    float mult, scale;
-    int8_scales(amax, mult, scale);
-    if (lane == 0) S[row] = scale;
-    int8_t* q = Q + (size_t)row * cols;
+    for (int r = 0; r < NR; ++r) {
+        float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = lane + i * LPR;
-        if (FULL || c < nchunk) {
-            const uint32_t lo = quant4(v[i].x, v[i].y, mult);
-            const uint32_t hi = quant4(v[i].z, v[i].w, mult);
-            reinterpret_cast<uintx2*>(q)[c] = uintx2{lo, hi};
+        for (int i = 0; i < CPL; ++i) {
+            if (!FULL && lane + i * LPR >= nchunk) v[r][i] = uintx4{0, 0, 0, 0};
+            amax = fmaxf(amax, qg::absmax8(v[r][i]));
+        }
+        amax = qg::group_max<LPR>(amax);
+        if (row[r] >= rows) continue;  // (uniform over the lane group)
+        float mult, scale;
+        int8_scales(amax, mult, scale);
+        if (lane == 0) S[row[r]] = scale;
+        int8_t* q = Q + (size_t)row[r] * cols;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * LPR;
+            if (FULL || c < nchunk) {
+                const uint32_t lo = quant4(v[r][i].x, v[r][i].y, mult);
+                const uint32_t hi = quant4(v[r][i].z, v[r][i].w, mult);
+                reinterpret_cast<uintx2*>(q)[c] = uintx2{lo, hi};
+            }
         }
     }
 }
@@ -197,21 +206,24 @@ extern "C" int32_t quant_sym_int8(const uint16_t* X, int8_t* Q, float* scales, i
     // 16-byte chunks per row (7.34 us for 65,536 rows of 128 with 16 lanes of
     // two chunks, 6.83 with 16 lanes of one, 6.46 with 8 of two, 6.90 with 4
     // of four; 6.12 once quant4 took the fma-mix product and dropped the clamp)
-    auto launch = [&](auto kern, int lpr) {
-        const int rpb = 256 / lpr;
+    // (two rows per lane group for rows of 128 values: 6.17 -> 6.08 us at
+    // 65,536 rows, four loads per lane in flight; four rows 6.66, and
+    // non-temporal code stores 6.41)
+    auto launch = [&](auto kern, int lpr, int nr) {
+        const int rpb = 256 / lpr * nr;
         hipLaunchKernelGGL(kern, dim3((rows + rpb - 1) / rpb), dim3(256), 0, st, X, Q, scales, (int)rows,
                            (int)cols);
     };
     if (cols == 8 * 8 * 2) {
-        launch(quant_rows_kernel<8, 2, true>, 8);
+        launch(quant_rows_kernel<8, 2, true, 2>, 8, 2);
     } else if (cols < 8 * 8 * 2) {
-        launch(quant_rows_kernel<8, 2, false>, 8);
+        launch(quant_rows_kernel<8, 2, false>, 8, 1);
     } else if (cols <= 16 * 8 * 2) {
-        launch(quant_rows_kernel<16, 2, false>, 16);
+        launch(quant_rows_kernel<16, 2, false>, 16, 1);
     } else if (cols == 64 * 8 * 8) {
-        launch(quant_rows_kernel<64, 8, true>, 64);
+        launch(quant_rows_kernel<64, 8, true>, 64, 1);
     } else if (cols <= 64 * 8 * 8) {
-        launch(quant_rows_kernel<64, 8, false>, 64);
+        launch(quant_rows_kernel<64, 8, false>, 64, 1);
     } else {
         hipLaunchKernelGGL(quant_rows_long_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, X, Q,
                            scales, (int)rows, (int)cols);
