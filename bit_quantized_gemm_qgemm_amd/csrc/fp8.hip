@@ -33,24 +33,28 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 // place): the same single rounding, except that a zero product comes out +0
 // where x * mult is -0 for negative x; since mult > 0 the code's sign is that
 // of x, so the sign bits of the four inputs are ORed into the codes (one byte
-// permute gathers them), which restores -0 as 0x80.  With |x| <= amax and
+// permute gathers them), which restores -0 as 0x80.  smask (sign_mask) keeps
+// them out when mult is 0: a row (or tensor) whose maximum is 0 gets code
+// 0x00 for every value, -0 included.  With |x| <= amax and
 // mult = fl32(448 / amax) the product is at most 448 (1 + 2^-24) in
 // magnitude, which the round-to-nearest-even conversion maps to +-448 (the
 // next value up would be 480), so no clamp to [-448, 448] is needed for
 // finite input.
-__device__ __forceinline__ uint32_t fp8x4(uint32_t h01, uint32_t h23, float mult) {
+__device__ __forceinline__ uint32_t sign_mask(float mult) { return mult > 0.0f ? 0x80808080u : 0u; }
+
+__device__ __forceinline__ uint32_t fp8x4(uint32_t h01, uint32_t h23, float mult, uint32_t smask) {
     float x[4] = {h2f(h01 & 0xffffu), h2f(h01 >> 16), h2f(h23 & 0xffffu), h2f(h23 >> 16)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(x[i], mult, 0.0f);
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);  // bytes 0, 1
     w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);       // bytes 2, 3
     // bytes 1 and 3 of each input word hold the fp16 sign bits, in bit 7
-    const uint32_t sgn = __builtin_amdgcn_perm(h23, h01, 0x07050301u) & 0x80808080u;
+    const uint32_t sgn = __builtin_amdgcn_perm(h23, h01, 0x07050301u) & smask;
     return (uint32_t)w | sgn;
 }
 
-__device__ __forceinline__ uintx2 fp8x8(uintx4 v, float mult) {
-    return uintx2{fp8x4(v.x, v.y, mult), fp8x4(v.z, v.w, mult)};
+__device__ __forceinline__ uintx2 fp8x8(uintx4 v, float mult, uint32_t smask) {
+    return uintx2{fp8x4(v.x, v.y, mult, smask), fp8x4(v.z, v.w, mult, smask)};
 }
 
 // ------------------------------------------------------------------ per-row quant
@@ -85,12 +89,13 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
     amax = group_max<LPR>(amax);
     if (!live) return;
     const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const uint32_t smask = sign_mask(mult);
     if (lane == 0) S[row] = amax > 0.0f ? amax / 448.0f : 0.0f;
     uintx2* q = reinterpret_cast<uintx2*>(Q + (size_t)row * cols);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + i * LPR;
-        if (FULL || c < nchunk) q[c] = fp8x8(v[i], mult);
+        if (FULL || c < nchunk) q[c] = fp8x8(v[i], mult, smask);
     }
 }
 
@@ -152,6 +157,7 @@ __global__ __launch_bounds__(256) void fp8_quant_tensor_kernel(const uint16_t* _
     __shared__ float red[4];
     const float amax = block_amax(reinterpret_cast<const float*>(Q), P, red);
     const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const uint32_t smask = sign_mask(mult);
     const uintx4* x = reinterpret_cast<const uintx4*>(X);
     uintx2* q = reinterpret_cast<uintx2*>(Q);
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -161,9 +167,9 @@ __global__ __launch_bounds__(256) void fp8_quant_tensor_kernel(const uint16_t* _
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = ldg_nt(x + c + i * stride);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[c + i * stride] = fp8x8(v[i], mult);
+        for (int i = 0; i < 4; ++i) q[c + i * stride] = fp8x8(v[i], mult, smask);
     }
-    for (; c < nchunk; c += stride) q[c] = fp8x8(ldg_nt(x + c), mult);
+    for (; c < nchunk; c += stride) q[c] = fp8x8(ldg_nt(x + c), mult, smask);
 }
 
 // One block of 256 threads: the first ceil(P / 2) chunks and the scale.
@@ -175,8 +181,9 @@ __global__ __launch_bounds__(256) void fp8_quant_tensor_head_kernel(const uint16
     // inside, before any code overwrites them)
     const float amax = block_amax(reinterpret_cast<const float*>(Q), P, red);
     const float mult = amax > 0.0f ? 448.0f / amax : 0.0f;
+    const uint32_t smask = sign_mask(mult);
     for (int c = threadIdx.x; c < (P + 1) / 2; c += 256)
-        reinterpret_cast<uintx2*>(Q)[c] = fp8x8(reinterpret_cast<const uintx4*>(X)[c], mult);
+        reinterpret_cast<uintx2*>(Q)[c] = fp8x8(reinterpret_cast<const uintx4*>(X)[c], mult, smask);
     if (threadIdx.x == 0) *scale = amax > 0.0f ? amax / 448.0f : 0.0f;
 }
 

@@ -460,6 +460,26 @@ def test_fp8_quant_shapes_and_edge_rows(qg, rows, cols, per_row):
     assert np.array_equal(bits(Xd), bits(oracle.dequant_fp8(Qr, Sr, per_row=per_row)))
 
 
+@pytest.mark.parametrize("per_row", [True, False])
+def test_quant_negative_zero_rows(qg, per_row):
+    """A row (per row) or a tensor (per tensor) whose values are all +0 or -0 has amax 0: scale 0
+    and every code 0, -0 included (the E4M3 codes of -0 in a row with a nonzero maximum are 0x80;
+    the int8 path is checked on the same rows)."""
+    for rows, cols in [(3, 128), (5, 16), (2, 4096)]:
+        X = np.full((rows, cols), np.float16(-0.0))
+        X[0, ::2] = np.float16(0.0)
+        if per_row and rows > 2:
+            X[2, 5] = np.float16(-1.5)
+        Q, S = qg.quant_fp8_e4m3(dev(X), per_row=per_row)
+        Qr, Sr = oracle.quant_fp8(X, per_row=per_row)
+        assert np.array_equal(host(Q), Qr), (rows, cols, per_row)
+        assert np.array_equal(host(S).view(np.uint32), Sr.view(np.uint32)), (rows, cols, per_row)
+        if per_row:
+            Qi, Si = qg.quant_sym_int8(dev(X))
+            Qir, Sir = oracle.quant_sym_int8(X)
+            assert np.array_equal(host(Qi), Qir) and np.array_equal(host(Si).view(np.uint32), Sir.view(np.uint32))
+
+
 @pytest.mark.parametrize("case", ["zero", "head", "tail", "negative"])
 @pytest.mark.parametrize("rows,cols", [(1, 8), (3, 16), (64, 4096), (512, 1024)])
 def test_fp8_per_tensor_amax_anywhere(qg, rows, cols, case):
