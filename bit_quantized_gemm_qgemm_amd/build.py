@@ -30,6 +30,11 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into scalar registers at dispatch (a kernel
+    # otherwise loads them from the argument segment, one or more dependent
+    # round trips before its first address is known): measured on MI355X,
+    # 1-6 % off the 5-20 us memory-bound kernels, no change on the long ones
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -79,6 +79,20 @@ __device__ __forceinline__ float group_sum(float v) {
 // four per eight int8 weights); each group's fp32 partial T becomes
 // acc += s * (T - C).  One A fragment read from
 // LDS feeds the MFMAs of all NSW strips.
+// Workgroups of a decode launch over N columns: one per 16-column strip, or
+// (balanced) at least one per CU where there are enough strips, each over a
+// contiguous range of at most three strips.  The kernel derives its grid size
+// from N with this same function instead of reading gridDim, whose value sits
+// in the hidden kernel arguments: that load, the only one left once the
+// explicit arguments are preloaded into scalar registers, would delay every
+// wave's first weight load by a memory round trip.
+__host__ __device__ inline int decode_grid(int N, bool bal) {
+    const int nstrips = (N + 15) / 16;
+    if (!bal) return nstrips;
+    const int nwg = nstrips < 256 ? nstrips : 256;
+    return nwg < (nstrips + 2) / 3 ? (nstrips + 2) / 3 : nwg;
+}
+
 template <int WB, int MT, int NSW, int KCW, int G, bool BAL>
 __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ wf, const uint16_t* __restrict__ Sc,
@@ -125,12 +139,13 @@ __global__ __launch_bounds__(64 * (32 / KCW)) void wq_decode_kernel(
     // NSW - 1 or NSW strips (every CU busy when N / 16 is not a multiple of
     // NSW x 256); a slot past the range repeats its last strip and is not stored
     int strip0, nst;
+    const int nwg = decode_grid(N, BAL);
     if constexpr (BAL) {
-        const int wg = xcd_contiguous(blockIdx.x, gridDim.x), nstrips = (N + 15) / 16;
-        strip0 = (int)((long)wg * nstrips / gridDim.x);
-        nst = (int)((long)(wg + 1) * nstrips / gridDim.x) - strip0;
+        const int wg = xcd_contiguous(blockIdx.x, nwg), nstrips = (N + 15) / 16;
+        strip0 = (int)((long)wg * nstrips / nwg);
+        nst = (int)((long)(wg + 1) * nstrips / nwg) - strip0;
     } else {
-        strip0 = xcd_contiguous(blockIdx.x, gridDim.x) * NSW;
+        strip0 = xcd_contiguous(blockIdx.x, nwg) * NSW;
         nst = NSW;
     }
     const int cl = lane & 15, q = lane >> 4;
@@ -1062,21 +1077,19 @@ __global__ __launch_bounds__(256) void wq_splitk_reduce_kernel(const float* __re
 template <int WB, int G>
 void launch_wq_decode_narrow(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
                              int M, int N, int K, hipStream_t st) {
-    const int nstrips = (N + 15) / 16;
+    const int nwg = decode_grid(N, false);
     if (M == 1)
-        hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(nstrips), dim3(512), 0, st, A, wf,
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 1, 1, 4, G, false>), dim3(nwg), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
     else
-        hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(nstrips), dim3(512), 0, st, A, wf,
+        hipLaunchKernelGGL((wq_decode_kernel<WB, 2, 1, 4, G, false>), dim3(nwg), dim3(512), 0, st, A, wf,
                            S, ldS, Y, M, N, K);
 }
 
 template <int WB, int G>
 void launch_wq_decode_balanced(const uint16_t* A, const uint8_t* wf, const uint16_t* S, int ldS, uint16_t* Y,
                                int M, int N, int K, hipStream_t st) {
-    const int nstrips = (N + 15) / 16;
-    int nwg = nstrips < 256 ? nstrips : 256;
-    if (nwg < (nstrips + 2) / 3) nwg = (nstrips + 2) / 3;
+    const int nwg = decode_grid(N, true);
     if (M <= 4)
         hipLaunchKernelGGL((wq_decode_kernel<WB, 4, 3, 2, G, true>), dim3(nwg), dim3(1024), 0, st, A, wf, S,
                            ldS, Y, M, N, K);
