@@ -65,47 +65,103 @@ __host__ __device__ inline void workspace_layout(int T, int H, int I, int E, int
 
 // One workgroup.  Route: thread t takes tokens t, t + 1024, ...; per token
 // the top-k experts by logit (lower index wins ties) and the softmax over the
-// selected logits (fp32), the selected logits kept in the output weights
-// until the sum is known (no per-thread arrays, so no scratch memory).
+// selected logits (fp32).  With eight experts (and 16-byte aligned logit
+// rows, topK <= 8) a token's logits arrive in one 16-byte load and the
+// selection runs on registers (arrays indexed by unrolled constants only);
+// otherwise each logit is read from memory as it is compared and the
+// selected logits wait in the output weights until the sum is known (no
+// per-thread arrays, so no scratch memory either way).  The expert ids also
+// go to LDS when the pairs fit (P <= MOE_LDS_PAIRS), so the permute below
+// reads them from there rather than back from global memory.
 // Permute: groups the (token, j) pairs by expert, keeping ascending pair
 // order inside an expert (wave ballots, no atomics on the result order), and
 // records each pair's slot.  One launch for both: the routing of a few
 // hundred tokens is far below a launch's cost.
+constexpr int MOE_LDS_PAIRS = 8192;
+
 __global__ __launch_bounds__(1024) void moe_route_permute_kernel(const uint16_t* __restrict__ logits,
                                                                  int32_t* __restrict__ ids,
                                                                  float* __restrict__ w, int T, int E,
                                                                  int topK, int32_t* __restrict__ offsets,
                                                                  int32_t* __restrict__ pairs,
                                                                  int32_t* __restrict__ slot_of) {
+    __shared__ int sid[MOE_LDS_PAIRS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int t = tid; t < T; t += 1024) {
-        const uint16_t* l = logits + (size_t)t * E;
-        int32_t* it = ids + (size_t)t * topK;
-        float* wt = w + (size_t)t * topK;
-        uint64_t taken = 0;
-        for (int j = 0; j < topK; ++j) {
-            int best = -1;
-            float bv = 0.0f;
-            for (int e = 0; e < E; ++e) {
-                if ((taken >> e) & 1ull) continue;
-                const float v = h2f(l[e]);
-                if (best < 0 || v > bv) {
-                    best = e;
-                    bv = v;
-                }
+    const int P = T * topK;
+    const bool in_lds = P <= MOE_LDS_PAIRS;
+    if (E == 8 && topK <= 8 && ((uintptr_t)logits & 15) == 0) {
+        for (int t = tid; t < T; t += 1024) {
+            const uintx4 raw = *reinterpret_cast<const uintx4*>(logits + (size_t)t * 8);
+            float lv[8], vals[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lv[2 * i] = h2f((uint16_t)(raw[i] & 0xffffu));
+                lv[2 * i + 1] = h2f((uint16_t)(raw[i] >> 16));
             }
-            taken |= 1ull << best;
-            it[j] = best;
-            wt[j] = bv;
+            uint32_t taken = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j >= topK) break;
+                int best = -1;
+                float bv = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((taken >> e) & 1u) continue;
+                    if (best < 0 || lv[e] > bv) {
+                        best = e;
+                        bv = lv[e];
+                    }
+                }
+                taken |= 1u << best;
+                ids[(size_t)t * topK + j] = best;
+                if (in_lds) sid[t * topK + j] = best;
+                vals[j] = bv;
+            }
+            const float lmax = vals[0];
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j >= topK) break;
+                vals[j] = expf(vals[j] - lmax);
+                sum += vals[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j >= topK) break;
+                w[(size_t)t * topK + j] = vals[j] / sum;
+            }
         }
-        const float lmax = wt[0];
-        float sum = 0.0f;
-        for (int j = 0; j < topK; ++j) {
-            const float v = expf(wt[j] - lmax);
-            wt[j] = v;
-            sum += v;
+    } else {
+        for (int t = tid; t < T; t += 1024) {
+            const uint16_t* l = logits + (size_t)t * E;
+            int32_t* it = ids + (size_t)t * topK;
+            float* wt = w + (size_t)t * topK;
+            uint64_t taken = 0;
+            for (int j = 0; j < topK; ++j) {
+                int best = -1;
+                float bv = 0.0f;
+                for (int e = 0; e < E; ++e) {
+                    if ((taken >> e) & 1ull) continue;
+                    const float v = h2f(l[e]);
+                    if (best < 0 || v > bv) {
+                        best = e;
+                        bv = v;
+                    }
+                }
+                taken |= 1ull << best;
+                it[j] = best;
+                if (in_lds) sid[t * topK + j] = best;
+                wt[j] = bv;
+            }
+            const float lmax = wt[0];
+            float sum = 0.0f;
+            for (int j = 0; j < topK; ++j) {
+                const float v = expf(wt[j] - lmax);
+                wt[j] = v;
+                sum += v;
+            }
+            for (int j = 0; j < topK; ++j) wt[j] = wt[j] / sum;
         }
-        for (int j = 0; j < topK; ++j) wt[j] = wt[j] / sum;
     }
     __syncthreads();  // the expert ids written above are read by every thread below
 
@@ -113,10 +169,9 @@ __global__ __launch_bounds__(1024) void moe_route_permute_kernel(const uint16_t*
     __shared__ int base[64];
     __shared__ int wave_cnt[16][64];
     __shared__ int wave_off[16][64];
-    const int P = T * topK;
     if (tid < 64) cnt[tid] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[ids[p]], 1);
+    for (int p = tid; p < P; p += 1024) atomicAdd(&cnt[in_lds ? sid[p] : ids[p]], 1);
     __syncthreads();
     if (tid == 0) {
         int run = 0;
@@ -131,7 +186,7 @@ __global__ __launch_bounds__(1024) void moe_route_permute_kernel(const uint16_t*
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int b0 = 0; b0 < P; b0 += 1024) {
         const int p = b0 + tid;
-        const int e = p < P ? ids[p] : -1;
+        const int e = p < P ? (in_lds ? sid[p] : ids[p]) : -1;
         int rank = 0;
         for (int x = 0; x < E; ++x) {
             const uint64_t m = __ballot(e == x);
@@ -238,18 +293,24 @@ __global__ __launch_bounds__(256, 2) void moe_expert_kernel(
     for (int r0 = 0; r0 < me; r0 += PASS) {
         const int R = me - r0 < PASS ? me - r0 : PASS;
         const int slot0 = off + r0;
-        // element offset of A row r of this pass (rows < 2^31 / H elements)
-        auto row_off = [&](int r) -> uint32_t {
-            if constexpr (MODE == 0) return (uint32_t)(wk.pairs[slot0 + r] / topK) * (uint32_t)H;
-            else return (uint32_t)(slot0 + r) * (uint32_t)I;
+        // A row r of this pass: its pair index (gate/up, gathered tokens) or
+        // its slot (down), and from that its element offset (rows < 2^31 / H
+        // elements)
+        auto row_key = [&](int r) -> uint32_t {
+            if constexpr (MODE == 0) return (uint32_t)wk.pairs[slot0 + r];
+            else return (uint32_t)(slot0 + r);
+        };
+        auto key_off = [&](uint32_t k) -> uint32_t {
+            if constexpr (MODE == 0) return (k / (uint32_t)topK) * (uint32_t)H;
+            else return k * (uint32_t)I;
         };
         switch ((R + 31) / 32) {
-            case 1: expert_pass<G, NB, 1, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
-            case 2: expert_pass<G, NB, 2, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
-            case 3: expert_pass<G, NB, 3, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
+            case 1: expert_pass<G, NB, 1, MODE, 4>(sA, abase, row_key, key_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
+            case 2: expert_pass<G, NB, 2, MODE, 4>(sA, abase, row_key, key_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
+            case 3: expert_pass<G, NB, 3, MODE, 4>(sA, abase, row_key, key_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act); break;
             default:
                 if constexpr (PASS == 128)
-                    expert_pass<G, NB, 4, MODE, 4>(sA, abase, row_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act);
+                    expert_pass<G, NB, 4, MODE, 4>(sA, abase, row_key, key_off, R, wf, S, N, N, kchunks, c0, c1, ncol0, slot0, out, act);
                 break;
         }
         __syncthreads();  // the next pass refills both LDS buffers

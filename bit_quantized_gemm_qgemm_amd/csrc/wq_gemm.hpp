@@ -1028,12 +1028,13 @@ __global__ __launch_bounds__(256, 2) void wq_mid_kernel(const uint16_t* __restri
     for (int r0 = 0; r0 < M; r0 += 128) {
         const int R = M - r0 < 128 ? M - r0 : 128;
         // element offset of A row r of this pass (M * K < 2^32 is checked at launch)
-        auto row_off = [&](int r) -> uint32_t { return (uint32_t)(r0 + r) * (uint32_t)K; };
+        auto row_key = [&](int r) -> uint32_t { return (uint32_t)(r0 + r); };
+        auto key_off = [&](uint32_t k) -> uint32_t { return k * (uint32_t)K; };
         switch ((R + 31) / 32) {
-            case 1: expert_pass<G, 1, 1, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
-            case 2: expert_pass<G, 1, 2, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
-            case 3: expert_pass<G, 1, 3, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
-            default: expert_pass<G, 1, 4, 1, WB>(sA, A, row_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            case 1: expert_pass<G, 1, 1, 1, WB>(sA, A, row_key, key_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            case 2: expert_pass<G, 1, 2, 1, WB>(sA, A, row_key, key_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            case 3: expert_pass<G, 1, 3, 1, WB>(sA, A, row_key, key_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
+            default: expert_pass<G, 1, 4, 1, WB>(sA, A, row_key, key_off, R, wfp, sp, N, ldS, kchunks, c0, c1, ncol0, r0, out); break;
         }
         __syncthreads();  // the next pass refills both LDS buffers
     }

@@ -21,9 +21,9 @@ constexpr int XP_SLAB = 128 * 128;  // halfs per LDS A buffer: 128 rows of 128 k
 // the gate activation (moe_act).
 // MODE 1: out[slot][n] = the fp32 partial sum over the pass's chunk range
 // (the K splits of the MoE down projection and of the mid-M GEMM).
-// slot0 + row indexes the output row; row_off(r) is the element offset of
-// A row r of the pass from abase.  N is the row stride of out, ldS that of
-// the scales (0: one scale per column).
+// slot0 + row indexes the output row; key_off(row_key(r)) is the element
+// offset of A row r of the pass from abase.  N is the row stride of out, ldS
+// that of the scales (0: one scale per column).
 // Gate activation of the gated expert FFN (QGEMM_MOE_ACT_*): SiLU, GELU
 // (erf form, tanh form) or ReLU, in fp32.
 __device__ __forceinline__ float moe_act(float g, int act) {
@@ -36,8 +36,12 @@ __device__ __forceinline__ float moe_act(float g, int act) {
     }
 }
 
-template <int G, int NB, int NRB, int MODE, int WB, typename RowOff>
-__device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowOff row_off, int R,
+// row_key(r) names A row r of the pass (it may load: a gathered row's pair
+// index), key_off(key) turns that name into the row's element offset from
+// abase.
+template <int G, int NB, int NRB, int MODE, int WB, typename RowKey, typename KeyOff>
+__device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase, RowKey row_key,
+                                            KeyOff key_off, int R,
                                             const uint8_t* const* wf, const uint16_t* const* S,
                                             int N, int ldS, int kchunks, int c0, int c1, int ncol0,
                                             int slot0, void* out, int act = 0) {
@@ -63,13 +67,19 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     // offset per lane, so a load takes no vector address arithmetic.  The
     // callers keep the A element offsets below 2^31 (byte offsets below
     // 2^32); the descriptors do not bound.
+    // The row keys come first (for gathered rows, a load of the pair index
+    // each), then the first chunk's B loads go out, and only then are the keys
+    // used: loads complete in issue order, so this waits for the keys alone
+    // and the weight stream starts one round trip earlier than behind that
+    // wait.
     const int rsub = lane >> 4, pos = lane & 15;
     uint32_t src[2 * NRB];  // byte offsets from the chunk's first k of abase
 #pragma unroll
     for (int j = 0; j < 2 * NRB; ++j) {
         const int r = 4 * (2 * NRB * wave + j) + rsub;
-        src[j] = (row_off(r < R ? r : R - 1) + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
+        src[j] = row_key(r < R ? r : R - 1);
     }
+    __builtin_amdgcn_sched_barrier(0);
     auto dma_a_one = [&](int c, int buf, int j) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(abase + (size_t)c * 128, 0xffffffffu);
         buffer_load_lds<16>(ra, sA + buf * XP_SLAB + (2 * NRB * wave + j) * 512, src[j], 0);
@@ -168,9 +178,14 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     // an odd chunk count leaves one chunk, already staged, for the tail.
     Chunk b0[NB], b1[NB];
     const int last = c1 - 1;
-    dma_a(c0, 0);
-    __builtin_amdgcn_sched_barrier(0);
     load_b(b0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2 * NRB; ++j) {
+        const int r = 4 * (2 * NRB * wave + j) + rsub;
+        src[j] = (key_off(src[j]) + (uint32_t)((pos ^ (r & 15)) * 8)) * 2u;
+    }
+    dma_a(c0, 0);
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
