@@ -455,15 +455,17 @@ def profile_one(name, launches, qg, qi, np, torch, to_dev):
     print(f"profiled {name} x{launches}", file=sys.stderr, flush=True)
 
 
-# sources of the decode kernel whose HBM counters profiles/decode_traffic.json holds
-DECODE_SOURCES = ("common.hpp", "wq_tile.hpp", "wq_pass.hpp", "wq_gemm.hpp", "w4a16.hip")
+# sources of the decode kernel whose HBM counters profiles/decode_traffic.json
+# holds, and the build script whose compiler flags shape its code
+DECODE_SOURCES = ("csrc/common.hpp", "csrc/wq_tile.hpp", "csrc/wq_pass.hpp", "csrc/wq_gemm.hpp",
+                  "csrc/w4a16.hip", "build.py")
 
 
 def decode_source_hash():
     import hashlib
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
-        with open(os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "bit_quantized_gemm_qgemm_amd", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
