@@ -324,13 +324,19 @@ def test_w8a8_cfg3_sampled(qg):
 
 # ------------------------------------------------------------------ MoE
 
-def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation=0):
+def moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, activation=0, logits_shift=0):
     E, H, I2 = Wg.shape
     I = I2 * 2
     pg = torch.cat([prepack(qg, Wg[e], H, I) for e in range(E)])
     pu = torch.cat([prepack(qg, Wu[e], H, I) for e in range(E)])
     pd = torch.cat([prepack(qg, Wd[e], I, H) for e in range(E)])
-    Y, ids, w, ws = qg.moe_w4a16(dev(X), dev(logits), pg, pu, pd, dev(Sg), dev(Su), dev(Sd), topK, G,
+    lg = dev(logits)
+    if logits_shift:  # the same logits at an address logits_shift elements past a 16-byte boundary
+        buf = torch.empty(lg.numel() + 8, dtype=lg.dtype, device=lg.device)
+        lg = buf[logits_shift:logits_shift + lg.numel()].view(lg.shape)
+        lg.copy_(dev(logits))
+        assert lg.data_ptr() % 16 == 2 * logits_shift
+    Y, ids, w, ws = qg.moe_w4a16(dev(X), lg, pg, pu, pd, dev(Sg), dev(Su), dev(Sd), topK, G,
                                  activation=activation)
     T = X.shape[0]
     P = T * topK
@@ -361,6 +367,24 @@ def test_moe_small(qg, T, H, I, E, topK, G):
     assert np.array_equal(off, offr) and np.array_equal(pairs, pairsr)
     assert np.allclose(w, wr, rtol=1e-6, atol=0)
     assert_fp16_close(Y, Yr, "moe small")
+
+
+# the routing kernel's paths: eight experts read with one 16-byte load per token (topK 1, 3
+# and 8; more tokens than the workgroup has threads; more pairs than its LDS holds, so the
+# permute reads the expert ids back from global memory) and, with the logits 2 bytes past a
+# 16-byte boundary, the path that reads each logit as it compares it
+@pytest.mark.parametrize("T,topK,shift", [(1100, 1, 0), (4500, 2, 0), (50, 8, 0), (64, 3, 0), (300, 2, 1)])
+def test_moe_routing_paths(qg, T, topK, shift):
+    H, I, E, G = 128, 128, 8, 128
+    X, logits, Wg, Wu, Wd, Sg, Su, Sd = qi.moe_problem(T, H, I, E, G, 900 + T + topK)
+    logits[3] = logits[3, 0]  # an all-tie row: lower expert index wins
+    Y, ids, w, off, pairs = moe_gpu(qg, X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G, logits_shift=shift)
+    Yr, idr, wr = oracle.moe(X, logits, Wg, Wu, Wd, Sg, Su, Sd, topK, G)
+    assert np.array_equal(ids, idr)
+    offr, pairsr = oracle.moe_permute(idr, E)
+    assert np.array_equal(off, offr) and np.array_equal(pairs, pairsr)
+    assert np.allclose(w, wr, rtol=1e-6, atol=0)
+    assert_fp16_close(Y, Yr, "moe routing paths")
 
 
 # each gate activation the MoE plugin page's activationType selects (SiLU, GELU in its erf
