@@ -73,7 +73,7 @@ __device__ __forceinline__ void expert_pass(uint16_t* sA, const uint16_t* abase,
     // and the weight stream starts one round trip earlier than behind that
     // wait.
     const int rsub = lane >> 4, pos = lane & 15;
-    uint32_t src[2 * NRB];  // byte offsets from the chunk's first k of abase
+    uint32_t src[2 * NRB];  // row keys, then byte offsets from the chunk's first k of abase
 #pragma unroll
     for (int j = 0; j < 2 * NRB; ++j) {
         const int r = 4 * (2 * NRB * wave + j) + rsub;
